@@ -1,0 +1,36 @@
+"""CPU oracle for the block-scaled FP8 GEMM with a global-amax epilogue.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path imports this package:
+only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+call it.  It shares no code, table or constant generator with the HIP library.
+
+What it computes ("GEMM + Amax (SM100)", section "Equations"):
+
+    A_hat[m,k,l] = dec(A[m,k,l]) * 2^(SFA(m, k // sf, l) - 127)
+    B_hat[n,k,l] = dec(B[n,k,l]) * 2^(SFB(n, k // sf, l) - 127)
+    C[m,n,l]     = sum_k A_hat[m,k,l] * B_hat[n,k,l]
+    Amax         = max_{m,n,l} |C[m,n,l]|
+
+in float64, where every decoded product is exact.  Modules:
+
+* ``codecs``    -- E4M3 / E5M2 / E8M0 decoders built from the bit definitions.
+* ``sf_atom``   -- expansion of the scale-factor atom layout (page section
+                   "Shapes" and the physical-shape paragraph of "Using JAX
+                   arrays") into one scale per (row, K-block).
+* ``gemm_amax`` -- dequantisation, the fp64 contraction, the |A|.|B| bound
+                   used by the tolerance, and the amax.
+
+Every function has a pin in ``tests/test_oracle_*.py``; see each module's
+header for which pin covers it.
+"""
+
+from .codecs import decode, decode_e4m3, decode_e5m2, decode_e8m0, FMT_E4M3, FMT_E5M2
+from .sf_atom import sf_physical_shape, sf_logical_shape, sf_logical_view, expand_scales
+from .gemm_amax import (dequantize, gemm_amax, gemm_amax_loops, gemm_rows, gemm_entries,
+                        amax_of)
+
+__all__ = [
+    "decode", "decode_e4m3", "decode_e5m2", "decode_e8m0", "FMT_E4M3", "FMT_E5M2",
+    "sf_physical_shape", "sf_logical_shape", "sf_logical_view", "expand_scales",
+    "dequantize", "gemm_amax", "gemm_amax_loops", "gemm_rows", "gemm_entries", "amax_of",
+]
