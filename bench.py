@@ -1,0 +1,162 @@
+"""Benchmark of the block-scaled FP8 GEMM + amax on one MI355X.
+
+One step = one full pass of the path over one batch of synthetic input:
+clear Amax, then the GEMM kernel (dequantise + contract + C store + amax),
+i.e. exactly what mxgemm_amax queues.  Inputs are generated on the host,
+copied to HBM before timing, and stay resident.
+
+Default workload: the projection-shaped GEMM+amax, M=8192 tokens,
+N=24576 (128 heads x 192), K=1536, L=1, sf_vec_size=32, E4M3 A/B from
+MX-quantised N(0,1) (B scaled by 1/sqrt(K)).  --workload selects another.
+
+Prints one JSON line: TFLOP/s of the whole step, the GEMM kernel's own
+duration (HIP events on the launch stream around each GEMM launch), its
+roofline against the MFMA peak of the datapath it uses, and the CPU oracle
+timed on a bounded sample on this host.
+
+    python bench.py [--steps K] [--warmup W] [--workload 1..5] [--fp8-mfma]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# Published MI355X dense matrix peaks (TFLOP/s)
+PEAK_BF16 = 2500.0
+PEAK_FP8 = 5000.0
+HBM_GBS = 8000.0
+
+
+def cpu_baseline(p, target_s=12.0):
+    """Time the CPU oracle on sampled rows of the workload; scale to TFLOP/s of the GEMM."""
+    import numpy as np
+
+    import oracle
+    rng = np.random.default_rng(0)
+    args = (p["A"], p["B"], p["SFA"], p["SFB"], p["M"], p["N"], p["K"], p["L"], p["sf"], p["a_fmt"], p["b_fmt"])
+    rows = 64
+    done_rows = 0
+    t_total = 0.0
+    while t_total < target_s:
+        idx = np.sort(rng.choice(p["M"], min(rows, p["M"]), replace=False))
+        t0 = time.perf_counter()
+        oracle.gemm_rows(*args, 0, idx)
+        t_total += time.perf_counter() - t0
+        done_rows += len(idx)
+        rows *= 2
+    flops = 2.0 * done_rows * p["N"] * p["K"]
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    return {
+        "value": flops / t_total / 1e12,
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"oracle.gemm_rows (fp64 decode + SF-atom expansion + C and sum|a||b| GEMMs via numpy BLAS) "
+                   f"on {done_rows} sampled rows of batch 0 ({done_rows}x{p['N']}x{p['K']}), {t_total:.1f} s; "
+                   f"value counts the 2*rows*N*K flops of C only"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=5)
+    ap.add_argument("--fp8-mfma", action="store_true", help="time the reduced-precision FP8 MFMA path")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this path runs on one GPU only; multi-GPU runs are not part of this build "
+              "(see DESIGN.md for how it would shard)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import block_scaled_precision_e4m3_amd as lib
+    import workloads as W
+
+    p = W.make_workload(args.workload)
+    M, N, K, L, sf = p["M"], p["N"], p["K"], p["L"], p["sf"]
+    dev = torch.device("cuda:0")
+    A = torch.from_numpy(p["A"]).to(dev)
+    B = torch.from_numpy(p["B"]).to(dev)
+    SFA = torch.from_numpy(p["SFA"]).to(dev)
+    SFB = torch.from_numpy(p["SFB"]).to(dev)
+    C = torch.empty(L * M * N, dtype=torch.float32, device=dev)
+    Amax = torch.zeros(4, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    mode_flag = lib.MXG_FLAG_FP8_MFMA if args.fp8_mfma else 0
+
+    def step():
+        lib.mxgemm_amax_ex(A, B, SFA, SFB, C, Amax, M, N, K, L, sf, p["a_fmt"], p["b_fmt"], mode_flag, sh)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        # one step == mxgemm_amax: the Amax-clearing kernel, then the GEMM kernel
+        lib.mxgemm_amax_reset(Amax, sh)
+        ev[i][0].record(stream)
+        lib.mxgemm_amax_ex(A, B, SFA, SFB, C, Amax, M, N, K, L, sf, p["a_fmt"], p["b_fmt"],
+                           mode_flag | lib.MXG_FLAG_AMAX_ACCUMULATE, sh)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+
+    flops = W.flops(M, N, K, L)
+    ms_per_step = wall * 1e3 / args.steps
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    peak = PEAK_FP8 if args.fp8_mfma else PEAK_BF16
+    tile_m, tile_n, grid = lib.mxgemm_launch_config(M, N, K, L, sf)
+    abytes = W.algorithmic_bytes(M, N, K, L, sf)
+
+    out = {
+        "metric": "block-scaled FP8 GEMM+amax TFLOP/s and % of MI355X MXFP8 MFMA peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8-e4m3 codes, exact bf16 dequant, fp32 accumulate" if not args.fp8_mfma
+                 else "fp8-e4m3 scaled MFMA (reduced-precision sums), fp32 accumulate",
+        "data": "synthetic (seeded, MX-quantised)",
+        "config": {"workload": W.WORKLOADS[args.workload]["name"], "M": M, "N": N, "K": K, "L": L,
+                   "sf_vec_size": sf, "a_fmt": "e4m3" if p["a_fmt"] == 0 else "e5m2",
+                   "b_fmt": "e4m3" if p["b_fmt"] == 0 else "e5m2", "tile": f"{tile_m}x{tile_n}", "grid": grid,
+                   "path": "fp8-mfma" if args.fp8_mfma else "bf16-mfma"},
+        "pct_of_mxfp8_peak": round(100.0 * achieved / PEAK_FP8, 2),
+        "kernel_ms": round(kernel_ms, 4),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "algorithmic_bytes": abytes,
+                     "algorithmic_GBps": round(abytes / (kernel_ms * 1e-3) / 1e9, 1)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(p)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

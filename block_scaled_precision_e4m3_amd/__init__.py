@@ -1,0 +1,225 @@
+"""Block-scaled FP8 GEMM with a fused global-amax epilogue on MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libmxgemm.so`` (declared in
+``include/mxgemm.h``).  Every step of the computation runs in the library's
+HIP kernels; this module only marshals arguments (PyTorch supplies device
+memory and streams).  It fails loudly when the library has not been built.
+
+Low-level functions carry the C names and arguments:
+``mxgemm_amax``, ``mxgemm_amax_ex``, ``mxgemm_amax_reset``,
+``mxgemm_check_support``, ``mxgemm_sf_bytes``, ``mxgemm_launch_config``,
+``mxgemm_strerror``.  Buffers may be torch tensors (their data pointer is
+passed) or integer device addresses.
+
+``gemm_amax`` mirrors the page's high-level wrapper ("GEMM + Amax (SM100)",
+section "High-level wrapper"): it takes A (M, K, L) / B (N, K, L) k-major
+tensors (or (L, M, K)-contiguous storage viewed that way), SF tensors in the
+logical atom view or the physical shape, allocates C (M, N, L) n-major and
+Amax (1, 1, 1) when not given, and returns (c, amax).
+"""
+
+import ctypes
+import os
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libmxgemm.so")
+
+MXG_FMT_E4M3 = 0
+MXG_FMT_E5M2 = 1
+MXG_FLAG_AMAX_ACCUMULATE = 1
+MXG_FLAG_FP8_MFMA = 2
+
+MXG_OK = 0
+MXG_ERR_NULL = -1
+MXG_ERR_SHAPE = -2
+MXG_ERR_ALIGN = -3
+MXG_ERR_SFVEC = -4
+MXG_ERR_FMT = -5
+MXG_ERR_DEVICE = -6
+MXG_ERR_LAUNCH = -7
+MXG_ERR_FLAGS = -8
+
+EXPORTED = ("mxgemm_amax", "mxgemm_amax_ex", "mxgemm_amax_reset", "mxgemm_check_support",
+            "mxgemm_sf_bytes", "mxgemm_launch_config", "mxgemm_strerror")
+
+
+class MxgemmError(Exception):
+    def __init__(self, status, msg):
+        super().__init__(f"mxgemm status {status}: {msg}")
+        self.status = status
+
+
+class MxgemmValueError(MxgemmError, ValueError):
+    pass
+
+
+class MxgemmRuntimeError(MxgemmError, RuntimeError):
+    pass
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it first with "
+            "`python -m block_scaled_precision_e4m3_amd._build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, ci, cu = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint
+    gemm_args = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, ci, ci, ci]
+    lib.mxgemm_amax.argtypes = gemm_args + [vp]
+    lib.mxgemm_amax.restype = ci
+    lib.mxgemm_amax_ex.argtypes = gemm_args + [cu, vp]
+    lib.mxgemm_amax_ex.restype = ci
+    lib.mxgemm_amax_reset.argtypes = [vp, vp]
+    lib.mxgemm_amax_reset.restype = ci
+    lib.mxgemm_check_support.argtypes = [i64, i64, i64, i64, ci, ci, ci]
+    lib.mxgemm_check_support.restype = ci
+    lib.mxgemm_sf_bytes.argtypes = [i64, i64, i64, ci]
+    lib.mxgemm_sf_bytes.restype = ctypes.c_size_t
+    lib.mxgemm_launch_config.argtypes = [i64, i64, i64, i64, ci, ctypes.POINTER(ci), ctypes.POINTER(ci),
+                                         ctypes.POINTER(i64)]
+    lib.mxgemm_launch_config.restype = ci
+    lib.mxgemm_strerror.argtypes = [ci]
+    lib.mxgemm_strerror.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load()
+
+
+def _raise(status):
+    msg = _lib.mxgemm_strerror(status).decode()
+    if status in (MXG_ERR_DEVICE, MXG_ERR_LAUNCH):
+        raise MxgemmRuntimeError(status, msg)
+    raise MxgemmValueError(status, msg)
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def mxgemm_strerror(status):
+    return _lib.mxgemm_strerror(int(status)).decode()
+
+
+def mxgemm_check_support(M, N, K, L, sf_vec_size, a_fmt, b_fmt):
+    """Status code (0 = supported) for these sizes and formats; host-only."""
+    return _lib.mxgemm_check_support(M, N, K, L, sf_vec_size, a_fmt, b_fmt)
+
+
+def mxgemm_sf_bytes(MN, K, L, sf_vec_size):
+    return _lib.mxgemm_sf_bytes(MN, K, L, sf_vec_size)
+
+
+def mxgemm_launch_config(M, N, K, L, sf_vec_size, with_grid=True):
+    """(tile_m, tile_n, grid) the library would use; grid is None unless with_grid (queries the device)."""
+    tm, tn, g = ctypes.c_int(), ctypes.c_int(), ctypes.c_int64()
+    st = _lib.mxgemm_launch_config(M, N, K, L, sf_vec_size, ctypes.byref(tm), ctypes.byref(tn),
+                                   ctypes.byref(g) if with_grid else None)
+    if st != MXG_OK:
+        _raise(st)
+    return tm.value, tn.value, (g.value if with_grid else None)
+
+
+def mxgemm_amax_ex(A, B, SFA, SFB, C, Amax, M, N, K, L, sf_vec_size, a_fmt, b_fmt, flags=0, stream=None):
+    """C-ABI mxgemm_amax_ex on torch tensors or raw device addresses; raises on a nonzero status."""
+    st = _lib.mxgemm_amax_ex(_ptr(A), _ptr(B), _ptr(SFA), _ptr(SFB), _ptr(C), _ptr(Amax),
+                             M, N, K, L, sf_vec_size, a_fmt, b_fmt, flags, _stream(stream))
+    if st != MXG_OK:
+        _raise(st)
+
+
+def mxgemm_amax(A, B, SFA, SFB, C, Amax, M, N, K, L, sf_vec_size, a_fmt, b_fmt, stream=None):
+    """C-ABI mxgemm_amax on torch tensors or raw device addresses; raises on a nonzero status."""
+    st = _lib.mxgemm_amax(_ptr(A), _ptr(B), _ptr(SFA), _ptr(SFB), _ptr(C), _ptr(Amax),
+                          M, N, K, L, sf_vec_size, a_fmt, b_fmt, _stream(stream))
+    if st != MXG_OK:
+        _raise(st)
+
+
+def mxgemm_amax_reset(Amax, stream=None):
+    st = _lib.mxgemm_amax_reset(_ptr(Amax), _stream(stream))
+    if st != MXG_OK:
+        _raise(st)
+
+
+# --- high-level wrapper ---------------------------------------------------------
+
+def _fmt_of(t):
+    import torch
+    if t.dtype == torch.float8_e4m3fn:
+        return MXG_FMT_E4M3
+    if t.dtype == torch.float8_e5m2:
+        return MXG_FMT_E5M2
+    raise MxgemmValueError(MXG_ERR_FMT, f"A/B dtype must be float8_e4m3fn or float8_e5m2, got {t.dtype}")
+
+
+def _as_lrk(t, name):
+    """Return (storage tensor contiguous as (L, rows, K), rows, K, L) from a k-major (rows, K, L) view or 2-D."""
+    if t.dim() == 2:
+        t = t.unsqueeze(2)
+    if t.dim() != 3:
+        raise MxgemmValueError(MXG_ERR_SHAPE, f"{name} must be (rows, K) or (rows, K, L)")
+    rows, k, l = t.shape
+    base = t.permute(2, 0, 1)
+    if not base.is_contiguous():
+        raise MxgemmValueError(MXG_ERR_ALIGN, f"{name} must be k-major with batch outermost: strides (K, 1, rows*K)")
+    return base, rows, k, l
+
+
+def _sf_phys(t, mn, k, l, sf):
+    """Accept the logical SF view (32, 4, MNb, 4, Kg, L) or the physical (L, MNb, Kg, 32, 4, 4) / flat bytes."""
+    import torch
+    mnb, kg = -(-mn // 128), -(-k // (4 * sf))
+    logical = (32, 4, mnb, 4, kg, l)
+    if tuple(t.shape) == logical and t.dim() == 6:
+        t = t.permute(5, 2, 4, 0, 1, 3)
+    if not t.is_contiguous():
+        raise MxgemmValueError(MXG_ERR_ALIGN, "SF tensor must be the physical buffer or its logical view")
+    if t.dtype != torch.uint8:
+        t = t.view(torch.uint8)
+    if t.numel() != 512 * l * mnb * kg:
+        raise MxgemmValueError(MXG_ERR_SHAPE, f"SF tensor has {t.numel()} bytes, expected {512 * l * mnb * kg}")
+    return t
+
+
+def gemm_amax(a, b, sfa, sfb, c=None, amax=None, sf_vec_size=32, stream=None, accumulate=False, fp8_mfma=False):
+    """(c, amax) = block-scaled GEMM + amax of torch FP8 tensors; see the module docstring."""
+    import torch
+    a_base, m, k, l = _as_lrk(a, "A")
+    b_base, n, kb, lb = _as_lrk(b, "B")
+    if kb != k or lb != l:
+        raise MxgemmValueError(MXG_ERR_SHAPE, "A and B disagree on K or L")
+    fa, fb = _fmt_of(a), _fmt_of(b)
+    sfa_p = _sf_phys(sfa, m, k, l, sf_vec_size)
+    sfb_p = _sf_phys(sfb, n, k, l, sf_vec_size)
+    if c is None:
+        c = torch.empty((l, m, n), dtype=torch.float32, device=a.device).permute(1, 2, 0)
+    c_base = c.permute(2, 0, 1) if c.dim() == 3 else c.unsqueeze(0)
+    if c.dtype != torch.float32 or not c_base.is_contiguous():
+        raise MxgemmValueError(MXG_ERR_ALIGN, "C must be float32, n-major (M, N, L) with strides (N, 1, M*N)")
+    if amax is None:
+        amax = torch.zeros((1, 1, 1), dtype=torch.float32, device=a.device)
+    flags = (MXG_FLAG_AMAX_ACCUMULATE if accumulate else 0) | (MXG_FLAG_FP8_MFMA if fp8_mfma else 0)
+    mxgemm_amax_ex(a_base, b_base, sfa_p, sfb_p, c_base, amax, m, n, k, l, sf_vec_size, fa, fb, flags, stream)
+    return c, amax
+
+
+__all__ = [
+    "mxgemm_amax", "mxgemm_amax_ex", "mxgemm_amax_reset", "mxgemm_check_support", "mxgemm_sf_bytes",
+    "mxgemm_launch_config", "mxgemm_strerror", "gemm_amax", "LIB_PATH", "EXPORTED",
+    "MXG_FMT_E4M3", "MXG_FMT_E5M2", "MXG_FLAG_AMAX_ACCUMULATE", "MXG_FLAG_FP8_MFMA", "MxgemmError", "MxgemmValueError",
+    "MxgemmRuntimeError",
+]

@@ -1,0 +1,253 @@
+// C-ABI entry points of the block-scaled FP8 GEMM + amax library (include/mxgemm.h).
+//
+// Host side: argument validation (reported before anything is queued, the
+// error convention of "Grouped GEMM (SM100 BF16)", section "Scheduling,
+// caching, and errors"), the per-shape tile choice, and the launches.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <string.h>
+
+#include "../../include/mxgemm.h"
+#include "mxgemm_kernel.hpp"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+struct DeviceInfo {
+  int checked = 0;   // 0 unknown, 1 gfx950, -1 other
+  int cus = 0;
+};
+
+DeviceInfo g_dev[kMaxDevices];
+std::mutex g_dev_mutex;
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool fits_i32(int64_t v) { return v >= 0 && v <= 0x7FFFFFFFLL; }
+
+// Pure size/format validation shared by every entry point.
+int check_sizes(int64_t M, int64_t N, int64_t K, int64_t L, int sf, int a_fmt, int b_fmt) {
+  if (M < 0 || N < 0 || K < 0 || L < 0) return MXG_ERR_SHAPE;
+  if (sf != 16 && sf != 32) return MXG_ERR_SFVEC;
+  if ((a_fmt != MXG_FMT_E4M3 && a_fmt != MXG_FMT_E5M2) || (b_fmt != MXG_FMT_E4M3 && b_fmt != MXG_FMT_E5M2))
+    return MXG_ERR_FMT;
+  // kernel indices are 32-bit per dimension, byte offsets 64-bit
+  if (!fits_i32(M) || !fits_i32(N) || !fits_i32(K) || !fits_i32(L)) return MXG_ERR_SHAPE;
+  const int64_t lim = INT64_MAX / 8;
+  if (M && K && L && (M > lim / K || M * K > lim / L)) return MXG_ERR_SHAPE;
+  if (N && K && L && (N > lim / K || N * K > lim / L)) return MXG_ERR_SHAPE;
+  if (M && N && L && (M > lim / N || M * N > lim / (4 * L))) return MXG_ERR_SHAPE;
+  // one tile's rows (up to 256) of A or B must be addressable with 32-bit offsets
+  if (K > (1LL << 23)) return MXG_ERR_SHAPE;
+  if (K % 16 != 0) return MXG_ERR_ALIGN;
+  if (N % 4 != 0) return MXG_ERR_ALIGN;
+  return MXG_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Current device must be gfx950; returns its CU count through *cus.
+int device_check(int* dev_out, int* cus) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MXG_ERR_DEVICE;
+  DeviceInfo& d = g_dev[dev];
+  if (d.checked == 0) {
+    std::lock_guard<std::mutex> lock(g_dev_mutex);
+    if (d.checked == 0) {
+      hipDeviceProp_t prop;
+      if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MXG_ERR_DEVICE;
+      d.cus = prop.multiProcessorCount;
+      d.checked = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    }
+  }
+  if (d.checked != 1) return MXG_ERR_DEVICE;
+  *dev_out = dev;
+  *cus = d.cus;
+  return MXG_OK;
+}
+
+// Device memory of `dev` (or managed memory) is accepted; host memory is not.
+bool on_device(const void* p, int dev) {
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged) return false;
+  return attr.device == dev;
+}
+
+struct TileChoice {
+  int bm, bn, occ;
+};
+
+// Per-shape tile choice.  256x256 tiles (4 waves of 128x128) halve LDS and
+// L2 traffic per flop against 128x128, but a shape with few tiles would
+// leave CUs idle: estimate the time of both and keep the faster.
+TileChoice choose_tiles(int64_t M, int64_t N, int64_t L, int cus) {
+  const int64_t t256 = L * cdiv(M, 256) * cdiv(N, 256);
+  const int64_t t128 = L * cdiv(M, 128) * cdiv(N, 128);
+  // relative per-tile cost: a 256x256 tile is 4x the work of a 128x128 one
+  // and runs at ~1.4x its flop rate; 128x128 runs two workgroups per CU.
+  const double w256 = (double)cdiv(t256, cus) * 4.0 / 1.4;
+  const double w128 = (double)cdiv(t128, 2LL * cus) * 2.0;
+  if (t256 >= cus && w256 <= w128) return {256, 256, 1};
+  return {128, 128, 2};
+}
+
+template <int BM, int BN, int MODE, int OCC>
+hipError_t launch_tiles(const mxg::Params& p, int sf, int fa, int fb, int64_t grid, hipStream_t s) {
+  const dim3 g((unsigned)grid), b(mxg::kThreads);
+#define MXG_LAUNCH(SF, FA, FB) \
+  hipLaunchKernelGGL((mxg::mxgemm_amax_kernel<BM, BN, SF, FA, FB, MODE, OCC>), g, b, 0, s, p)
+  if (sf == 32) {
+    if (fa == 0 && fb == 0) MXG_LAUNCH(32, 0, 0);
+    else if (fa == 0 && fb == 1) MXG_LAUNCH(32, 0, 1);
+    else if (fa == 1 && fb == 0) MXG_LAUNCH(32, 1, 0);
+    else MXG_LAUNCH(32, 1, 1);
+  } else {
+    if (fa == 0 && fb == 0) MXG_LAUNCH(16, 0, 0);
+    else if (fa == 0 && fb == 1) MXG_LAUNCH(16, 0, 1);
+    else if (fa == 1 && fb == 0) MXG_LAUNCH(16, 1, 0);
+    else MXG_LAUNCH(16, 1, 1);
+  }
+#undef MXG_LAUNCH
+  return hipGetLastError();
+}
+
+int64_t grid_for(int64_t tiles, int cus, int occ) {
+  int64_t g = (int64_t)cus * occ;
+  if (tiles < g) g = tiles;
+  return g;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mxgemm_check_support(int64_t M, int64_t N, int64_t K, int64_t L, int sf_vec_size, int a_fmt, int b_fmt) {
+  return check_sizes(M, N, K, L, sf_vec_size, a_fmt, b_fmt);
+}
+
+size_t mxgemm_sf_bytes(int64_t MN, int64_t K, int64_t L, int sf_vec_size) {
+  if (MN < 0 || K < 0 || L < 0 || (sf_vec_size != 16 && sf_vec_size != 32)) return 0;
+  return (size_t)(512 * L * cdiv(MN, 128) * cdiv(K, 4 * sf_vec_size));
+}
+
+int mxgemm_launch_config(int64_t M, int64_t N, int64_t K, int64_t L, int sf_vec_size, int* tile_m, int* tile_n,
+                         int64_t* grid) {
+  int st = check_sizes(M, N, K, L, sf_vec_size, MXG_FMT_E4M3, MXG_FMT_E4M3);
+  if (st != MXG_OK) return st;
+  int cus = 256;
+  if (grid) {
+    int dev = 0;
+    st = device_check(&dev, &cus);
+    if (st != MXG_OK) return st;
+  }
+  const TileChoice tc = choose_tiles(M, N, L, cus);
+  if (tile_m) *tile_m = tc.bm;
+  if (tile_n) *tile_n = tc.bn;
+  if (grid) {
+    const int64_t tiles = L * cdiv(M, tc.bm) * cdiv(N, tc.bn);
+    *grid = grid_for(tiles, cus, tc.occ);
+  }
+  return MXG_OK;
+}
+
+int mxgemm_amax_reset(float* Amax, void* stream) {
+  if (!Amax) return MXG_ERR_NULL;
+  if (!aligned16(Amax)) return MXG_ERR_ALIGN;
+  int dev = 0, cus = 0;
+  int st = device_check(&dev, &cus);
+  if (st != MXG_OK) return st;
+  if (!on_device(Amax, dev)) return MXG_ERR_DEVICE;
+  hipLaunchKernelGGL(mxg::amax_reset_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream,
+                     reinterpret_cast<unsigned*>(Amax));
+  return hipGetLastError() == hipSuccess ? MXG_OK : MXG_ERR_LAUNCH;
+}
+
+int mxgemm_amax_ex(const void* A, const void* B, const uint8_t* SFA, const uint8_t* SFB, float* C, float* Amax,
+                   int64_t M, int64_t N, int64_t K, int64_t L, int sf_vec_size, int a_fmt, int b_fmt,
+                   unsigned flags, void* stream) {
+  int st = check_sizes(M, N, K, L, sf_vec_size, a_fmt, b_fmt);
+  if (st != MXG_OK) return st;
+  if (flags & ~(unsigned)(MXG_FLAG_AMAX_ACCUMULATE | MXG_FLAG_FP8_MFMA)) return MXG_ERR_FLAGS;
+  // A, B and the scales are read only when there is a non-empty C and a non-empty K
+  const bool need_c = M > 0 && N > 0 && L > 0;
+  const bool need_a = need_c && K > 0, need_b = need_a;
+  if (!Amax || (need_a && (!A || !SFA)) || (need_b && (!B || !SFB)) || (need_c && !C)) return MXG_ERR_NULL;
+  if (!aligned16(Amax) || (need_a && (!aligned16(A) || !aligned16(SFA))) ||
+      (need_b && (!aligned16(B) || !aligned16(SFB))) || (need_c && !aligned16(C)))
+    return MXG_ERR_ALIGN;
+
+  int dev = 0, cus = 0;
+  st = device_check(&dev, &cus);
+  if (st != MXG_OK) return st;
+  if (!on_device(Amax, dev) || (need_a && (!on_device(A, dev) || !on_device(SFA, dev))) ||
+      (need_b && (!on_device(B, dev) || !on_device(SFB, dev))) || (need_c && !on_device(C, dev)))
+    return MXG_ERR_DEVICE;
+
+  hipStream_t s = (hipStream_t)stream;
+  if (!(flags & MXG_FLAG_AMAX_ACCUMULATE)) {
+    hipLaunchKernelGGL(mxg::amax_reset_kernel, dim3(1), dim3(64), 0, s, reinterpret_cast<unsigned*>(Amax));
+    if (hipGetLastError() != hipSuccess) return MXG_ERR_LAUNCH;
+  }
+  if (!need_c) return MXG_OK;
+
+  const TileChoice tc = choose_tiles(M, N, L, cus);
+  mxg::Params p;
+  p.A = static_cast<const uint8_t*>(A);
+  p.B = static_cast<const uint8_t*>(B);
+  p.SFA = SFA;
+  p.SFB = SFB;
+  p.C = C;
+  p.amax_bits = reinterpret_cast<unsigned*>(Amax);
+  p.M = (int)M;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.L = (int)L;
+  p.Kb = (int)cdiv(K, sf_vec_size);
+  p.Kg = (int)cdiv(K, 4 * sf_vec_size);
+  p.MNbA = (int)cdiv(M, 128);
+  p.MNbB = (int)cdiv(N, 128);
+  p.tilesM = (int)cdiv(M, tc.bm);
+  p.tilesN = (int)cdiv(N, tc.bn);
+  p.ksteps = (int)cdiv(K, mxg::kBK);
+  p.num_tiles = L * (int64_t)p.tilesM * p.tilesN;
+  const int64_t grid = grid_for(p.num_tiles, cus, tc.occ);
+  p.xcd_remap = (grid % 8 == 0) ? 1 : 0;
+
+  hipError_t e;
+  const bool fp8 = (flags & MXG_FLAG_FP8_MFMA) != 0;
+  if (tc.bm == 256)
+    e = fp8 ? launch_tiles<256, 256, mxg::kModeFp8, 1>(p, sf_vec_size, a_fmt, b_fmt, grid, s)
+            : launch_tiles<256, 256, mxg::kModeBf16, 1>(p, sf_vec_size, a_fmt, b_fmt, grid, s);
+  else
+    e = fp8 ? launch_tiles<128, 128, mxg::kModeFp8, 2>(p, sf_vec_size, a_fmt, b_fmt, grid, s)
+            : launch_tiles<128, 128, mxg::kModeBf16, 2>(p, sf_vec_size, a_fmt, b_fmt, grid, s);
+  return e == hipSuccess ? MXG_OK : MXG_ERR_LAUNCH;
+}
+
+int mxgemm_amax(const void* A, const void* B, const uint8_t* SFA, const uint8_t* SFB, float* C, float* Amax,
+                int64_t M, int64_t N, int64_t K, int64_t L, int sf_vec_size, int a_fmt, int b_fmt, void* stream) {
+  return mxgemm_amax_ex(A, B, SFA, SFB, C, Amax, M, N, K, L, sf_vec_size, a_fmt, b_fmt, 0u, stream);
+}
+
+const char* mxgemm_strerror(int status) {
+  switch (status) {
+    case MXG_OK: return "success";
+    case MXG_ERR_NULL: return "a required pointer is NULL";
+    case MXG_ERR_SHAPE: return "invalid size (negative, or offsets overflow)";
+    case MXG_ERR_ALIGN: return "misaligned buffer (16 bytes), K not a multiple of 16, or N not a multiple of 4";
+    case MXG_ERR_SFVEC: return "sf_vec_size must be 16 or 32";
+    case MXG_ERR_FMT: return "element format must be MXG_FMT_E4M3 or MXG_FMT_E5M2";
+    case MXG_ERR_DEVICE: return "current device is not gfx950, or a buffer is not memory of the current device";
+    case MXG_ERR_LAUNCH: return "HIP kernel launch failed";
+    case MXG_ERR_FLAGS: return "unknown flag bit";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

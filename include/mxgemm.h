@@ -1,0 +1,175 @@
+/*
+ * mxgemm.h -- C ABI of the block-scaled FP8 GEMM with a fused global-amax
+ * epilogue, for AMD Instinct MI355X (gfx950).
+ *
+ * Operation ("GEMM + Amax (SM100)", section "Equations"):
+ *
+ *   A_hat[m,k,l] = dec(A[m,k,l]) * 2^(SFA(m, k/sf, l) - 127)
+ *   B_hat[n,k,l] = dec(B[n,k,l]) * 2^(SFB(n, k/sf, l) - 127)
+ *   C[m,n,l]     = sum_k A_hat[m,k,l] * B_hat[n,k,l]      (FP32 accumulation)
+ *   Amax         = max_{m,n,l} |C[m,n,l]|
+ *
+ * with sf = sf_vec_size in {16, 32} consecutive K elements per E8M0 scale.
+ *
+ * Memory layout (section "Parameters", input/output tensors; all buffers are
+ * device memory owned by the caller, contiguous, byte offsets 64-bit):
+ *   A    : (L, M, K) element codes, one byte each ("k-major" A, strides
+ *          (K, 1, M*K) in the page's (M, K, L) notation).
+ *   B    : (L, N, K) element codes ("k-major" B).
+ *   SFA  : E8M0 scale bytes in the physical atom layout
+ *          (L, ceil(M/128), ceil(K/(4*sf)), 32, 4, 4) -- the C-contiguous
+ *          allocation whose permutation (3,4,1,5,2,0) is the logical
+ *          (32, 4, ceil(M/128), 4, ceil(K/(4*sf)), L) of section "Shapes"
+ *          (section "Using JAX arrays").  Row mn = i0 + 32*i1 + 128*i2 and
+ *          K-block kb = i3 + 4*i4 of logical index (i0,i1,i2,i3,i4,l), i.e.
+ *          byte 16*(mn%32) + 4*((mn/32)%4) + kb%4 of 512-byte atom
+ *          (l*ceil(M/128) + mn/128)*ceil(K/(4*sf)) + kb/4.
+ *          Padding bytes (rows >= M, K-blocks >= ceil(K/sf)) are never used
+ *          and may hold anything.
+ *   SFB  : the same for B with N in place of M.
+ *   C    : (L, M, N) float32 ("n-major" C, the page's default c_major="n").
+ *   Amax : one float32 (the page's (1,1,1) tensor).
+ *
+ * Element formats: MXG_FMT_E4M3 (float8_e4m3fn) and MXG_FMT_E5M2
+ * (float8_e5m2).  A and B may use different formats and FP8 may be used
+ * with sf = 16; both go beyond the page's support list (section "Support
+ * surface and constraints", Dtypes) and follow the format-agnostic equations.
+ *
+ * Errors: every entry point returns MXG_OK (0) or a negative status, and an
+ * invalid argument is reported before any work is queued on the stream
+ * (the error convention of "Grouped GEMM (SM100 BF16)", section
+ * "Scheduling, caching, and errors").  MXG_ERR_LAUNCH reports a HIP error
+ * from the launch itself.
+ *
+ * Streams: `stream` is a hipStream_t passed as void*; NULL is the null
+ * stream (the page's eager default, section "Using JAX arrays").  Calls are
+ * asynchronous; inputs must stay alive and unmodified, and outputs unread,
+ * until the stream has reached the call.
+ *
+ * The library allocates no device memory (inputs, outputs and the stream
+ * are the caller's) and keeps no pointer after a call returns.
+ */
+#ifndef MXGEMM_H
+#define MXGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element formats of A and B */
+enum {
+  MXG_FMT_E4M3 = 0, /* float8_e4m3fn: bias 7, no inf, NaN = 0x7F/0xFF, max 448 */
+  MXG_FMT_E5M2 = 1  /* float8_e5m2:   bias 15, inf = 0x7C/0xFC, max 57344      */
+};
+
+/* status codes */
+enum {
+  MXG_OK = 0,
+  MXG_ERR_NULL = -1,   /* a required pointer is NULL                          */
+  MXG_ERR_SHAPE = -2,  /* a negative size, or a size whose offsets overflow   */
+  MXG_ERR_ALIGN = -3,  /* A/B/C/Amax not 16-byte aligned, K % 16, N % 4       */
+  MXG_ERR_SFVEC = -4,  /* sf_vec_size not 16 or 32                            */
+  MXG_ERR_FMT = -5,    /* element format not MXG_FMT_E4M3 / MXG_FMT_E5M2      */
+  MXG_ERR_DEVICE = -6, /* current device is not gfx950, or a pointer is not
+                          device memory of the current device                 */
+  MXG_ERR_LAUNCH = -7, /* HIP reported an error when launching                */
+  MXG_ERR_FLAGS = -8   /* unknown bit in `flags`                              */
+};
+
+/* flags of mxgemm_amax_ex */
+enum {
+  /* Do not clear Amax first: Amax := max(Amax, max|C|).  The caller keeps
+     Amax a non-negative float (or NaN); lets several GEMMs share one Amax. */
+  MXG_FLAG_AMAX_ACCUMULATE = 1u,
+  /* Feed the FP8 codes straight to gfx950's scaled FP8 MFMA (twice the
+     matrix rate of the default path).  That instruction keeps only the top
+     ~13 bits, relative to the largest product, of each 8-element partial
+     dot product, so small products next to large ones are truncated and
+     the result can miss a 1e-5 * sum|A_hat*B_hat| error bound on
+     heavy-tailed data.  The default path dequantises each element exactly
+     to bf16 (scale folded in) and accumulates in fp32 on the bf16 MFMA. */
+  MXG_FLAG_FP8_MFMA = 2u
+};
+
+/*
+ * mxgemm_amax -- C = A_hat . B_hat^T per batch and Amax = max |C|.
+ *
+ *   A, B       device pointers to the element codes (layouts above).
+ *   SFA, SFB   device pointers to the physical SF atom buffers,
+ *              mxgemm_sf_bytes(M or N, K, L, sf_vec_size) bytes each.
+ *   C          device pointer, L*M*N float32, fully overwritten.
+ *   Amax       device pointer to one float32; set to max|C| (0 when
+ *              M*N*L == 0; NaN if any C is NaN).
+ *   M, N, K, L sizes, each >= 0.  K == 0 gives C == 0.
+ *   sf_vec_size 16 or 32.
+ *   a_fmt, b_fmt MXG_FMT_E4M3 or MXG_FMT_E5M2.
+ *   stream     hipStream_t (NULL = null stream).
+ *
+ * Requirements: A, B, C, Amax, SFA, SFB 16-byte aligned; K % 16 == 0 (16-byte
+ * rows of A/B) and K <= 2^23; N % 4 == 0 (16-byte rows of C) -- the page's "16-byte aligned along
+ * the contiguous dimension" (section "Support surface and constraints",
+ * Layouts and strides).  Current device must be gfx950 and own every pointer.
+ *
+ * Queues a one-wave kernel that clears Amax, then the GEMM kernel.
+ */
+int mxgemm_amax(const void* A, const void* B, const uint8_t* SFA, const uint8_t* SFB,
+                float* C, float* Amax, int64_t M, int64_t N, int64_t K, int64_t L,
+                int sf_vec_size, int a_fmt, int b_fmt, void* stream);
+
+/*
+ * mxgemm_amax_ex -- mxgemm_amax with flags.  flags == 0 is exactly
+ * mxgemm_amax; MXG_FLAG_AMAX_ACCUMULATE skips the clearing kernel and
+ * max-reduces into the existing Amax (queues the GEMM kernel only);
+ * MXG_FLAG_FP8_MFMA selects the reduced-precision FP8 matrix path.
+ *
+ * Exactness of the default path: every dequantised element is exact when
+ * its scale byte lies in 3..246 (E4M3) or 10..239 (E5M2), i.e. when the
+ * value fits bf16; products are exact and sums round as fp32 additions.
+ */
+int mxgemm_amax_ex(const void* A, const void* B, const uint8_t* SFA, const uint8_t* SFB,
+                   float* C, float* Amax, int64_t M, int64_t N, int64_t K, int64_t L,
+                   int sf_vec_size, int a_fmt, int b_fmt, unsigned flags, void* stream);
+
+/*
+ * mxgemm_amax_reset -- queue the one-wave kernel that sets *Amax = 0.0f.
+ * mxgemm_amax == mxgemm_amax_reset + mxgemm_amax_ex(MXG_FLAG_AMAX_ACCUMULATE).
+ */
+int mxgemm_amax_reset(float* Amax, void* stream);
+
+/*
+ * mxgemm_check_support -- host-only check of a problem description, the
+ * counterpart of the page's check_support() (section "API Usage", class
+ * API).  Returns MXG_OK or the status mxgemm_amax would return for these
+ * sizes/formats (pointers and device are not checked).  No HIP call.
+ */
+int mxgemm_check_support(int64_t M, int64_t N, int64_t K, int64_t L, int sf_vec_size,
+                         int a_fmt, int b_fmt);
+
+/*
+ * mxgemm_sf_bytes -- size of one physical SF buffer:
+ * 512 * L * ceil(MN/128) * ceil(K/(4*sf_vec_size)); 0 for invalid input.
+ * No HIP call.
+ */
+size_t mxgemm_sf_bytes(int64_t MN, int64_t K, int64_t L, int sf_vec_size);
+
+/*
+ * mxgemm_launch_config -- the tile shape and grid the GEMM kernel would use
+ * for this problem (for reporting and tests).  Writes tile_m, tile_n and
+ * the number of workgroups; any output pointer may be NULL.  Returns a
+ * status like mxgemm_check_support.  Queries the current device's compute
+ * unit count (HIP call) only when `grid` is requested.
+ */
+int mxgemm_launch_config(int64_t M, int64_t N, int64_t K, int64_t L, int sf_vec_size,
+                         int* tile_m, int* tile_n, int64_t* grid);
+
+/* mxgemm_strerror -- static text for a status code. No HIP call. */
+const char* mxgemm_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXGEMM_H */

@@ -1,0 +1,104 @@
+"""CPU checks of the C ABI: the library loads, exports every function the
+header declares, and its host-side validation returns the documented status
+codes before touching a device (no kernel is launched here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxgemm.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from block_scaled_precision_e4m3_amd import _build
+    if not os.path.exists(_build.LIB):
+        _build.build()
+    import block_scaled_precision_e4m3_amd as lib
+    return lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mxgemm_\w+)\s*\(", text)))
+
+
+def test_header_declares_expected_set(lib):
+    assert declared_functions() == sorted(lib.EXPORTED)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    cdll = ctypes.CDLL(lib.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(cdll, name), name
+
+
+def test_status_codes_match_header(lib):
+    text = open(HEADER).read()
+    for name, val in re.findall(r"\b(MXG_\w+)\s*=\s*(-?\d+)", text):
+        assert getattr(lib, name) == int(val), name
+
+
+def test_check_support(lib):
+    ok = lib.mxgemm_check_support
+    assert ok(256, 256, 256, 1, 32, 0, 0) == lib.MXG_OK
+    assert ok(4000, 7168, 2048, 1, 16, 1, 0) == lib.MXG_OK
+    assert ok(0, 0, 0, 0, 32, 0, 0) == lib.MXG_OK
+    assert ok(-1, 256, 256, 1, 32, 0, 0) == lib.MXG_ERR_SHAPE
+    assert ok(256, 256, 256, 1, 8, 0, 0) == lib.MXG_ERR_SFVEC
+    assert ok(256, 256, 256, 1, 32, 2, 0) == lib.MXG_ERR_FMT
+    assert ok(256, 256, 256, 1, 32, 0, 4) == lib.MXG_ERR_FMT
+    assert ok(256, 256, 200, 1, 32, 0, 0) == lib.MXG_ERR_ALIGN       # K % 16
+    assert ok(256, 258, 256, 1, 32, 0, 0) == lib.MXG_ERR_ALIGN       # N % 4
+    assert ok(1 << 31, 256, 256, 1, 32, 0, 0) == lib.MXG_ERR_SHAPE   # > int32 rows
+    assert ok(1 << 30, 1 << 30, 1 << 30, 1 << 20, 32, 0, 0) == lib.MXG_ERR_SHAPE
+
+
+def test_sf_bytes(lib):
+    assert lib.mxgemm_sf_bytes(256, 256, 1, 32) == 2048
+    assert lib.mxgemm_sf_bytes(4000, 2048, 1, 16) == 512 * 32 * 32
+    assert lib.mxgemm_sf_bytes(7168, 2048, 1, 16) == 917504
+    assert lib.mxgemm_sf_bytes(8192, 1536, 1, 32) == 393216
+    assert lib.mxgemm_sf_bytes(256, 256, 1, 7) == 0
+
+
+def test_launch_config_host_only(lib):
+    tm, tn, g = lib.mxgemm_launch_config(8192, 24576, 1536, 1, 32, with_grid=False)
+    assert (tm, tn, g) == (256, 256, None)
+    tm, tn, _ = lib.mxgemm_launch_config(2048, 2048, 2048, 1, 32, with_grid=False)
+    assert (tm, tn) == (128, 128)
+
+
+def test_errors_before_device_work(lib):
+    c = ctypes.CDLL(lib.LIB_PATH)
+    f = c.mxgemm_amax_ex
+    vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    f.argtypes = [vp] * 6 + [i64] * 4 + [ci] * 3 + [ctypes.c_uint, vp]
+    f.restype = ci
+    good = 0x7F0000000000
+    args = [good] * 6
+    dims = [256, 256, 256, 1]
+    assert f(*([None] + args[1:]), *dims, 32, 0, 0, 0, None) == lib.MXG_ERR_NULL
+    assert f(*(args[:5] + [None]), *dims, 32, 0, 0, 0, None) == lib.MXG_ERR_NULL
+    assert f(*([good + 8] + args[1:]), *dims, 32, 0, 0, 0, None) == lib.MXG_ERR_ALIGN
+    assert f(*(args[:4] + [good + 4] + args[5:]), *dims, 32, 0, 0, 0, None) == lib.MXG_ERR_ALIGN
+    assert f(*args, *dims, 32, 0, 0, 4, None) == lib.MXG_ERR_FLAGS
+    assert f(*args, 256, 256, 256, 1, 64, 0, 0, 0, None) == lib.MXG_ERR_SFVEC
+    assert f(*args, 256, 256, 256, 1, 32, 0, 9, 0, None) == lib.MXG_ERR_FMT
+    assert f(*args, 256, 256, 100, 1, 32, 0, 0, 0, None) == lib.MXG_ERR_ALIGN
+    assert f(*args, 256, -5, 256, 1, 32, 0, 0, 0, None) == lib.MXG_ERR_SHAPE
+    r = c.mxgemm_amax_reset
+    r.argtypes = [vp, vp]
+    r.restype = ci
+    assert r(None, None) == lib.MXG_ERR_NULL
+
+
+def test_python_errors_map_to_exceptions(lib):
+    with pytest.raises(ValueError):
+        lib.mxgemm_amax(None, None, None, None, None, None, 16, 16, 16, 1, 32, 0, 0, stream=0)
+    assert "sf_vec_size" in lib.mxgemm_strerror(lib.MXG_ERR_SFVEC)
+    assert lib.mxgemm_strerror(-99) == "unknown status"

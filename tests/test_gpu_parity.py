@@ -1,0 +1,245 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Small shapes (several tiles, ragged M/N, K tails, both sf_vec_size values,
+all format pairs, both tile configurations) are compared element by element
+with the full fp64 oracle.  The five workloads run at their full sizes in the
+launch configuration the benchmark times: workloads 1-2 against the full
+oracle, 3-5 on sampled rows and entries, plus properties that hold at any
+size (Amax equals max |C_gpu| bitwise; every output written).
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from parity_util import (amax_bits_of, check_amax, check_c, fetch, float_bits, run, to_device)
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+E4, E5 = W.FMT_E4M3, W.FMT_E5M2
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import block_scaled_precision_e4m3_amd as lib
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return lib
+
+
+def _oracle_full(p):
+    return oracle.gemm_amax(p["A"], p["B"], p["SFA"], p["SFB"], p["M"], p["N"], p["K"], p["L"], p["sf"],
+                            p["a_fmt"], p["b_fmt"])
+
+
+SMALL = [
+    # M, N, K, L, sf, fa, fb
+    (300, 520, 592, 2, 32, E4, E4),     # ragged M/N, K % 128 = 80, partial last sf block
+    (257, 260, 336, 1, 16, E5, E4),     # sf=16, K % 64 = 16
+    (128, 128, 128, 1, 32, E5, E5),
+    (1000, 772, 1040, 1, 16, E4, E5),
+    (64, 36, 48, 3, 32, E4, E4),        # one partial tile per batch, K < 2 blocks
+    (33, 4, 16, 1, 16, E5, E5),         # minimal K and N
+    (4096, 4096, 272, 1, 32, E4, E4),   # large enough for the 256x256 tile path
+    (4000, 4100, 208, 1, 16, E5, E4),   # 256x256 path, ragged, sf=16
+]
+
+
+@pytest.mark.parametrize("dist", ["normal", "student_t3"])
+@pytest.mark.parametrize("M,N,K,L,sf,fa,fb", SMALL)
+def test_small_shapes_full_oracle(lib, M, N, K, L, sf, fa, fb, dist):
+    print(f"case M={M} N={N} K={K} L={L} sf={sf} fmt={fa}{fb} {dist} "
+          f"tiles={lib.mxgemm_launch_config(M, N, K, L, sf)}", flush=True)
+    p = W.make_problem(M, N, K, L, sf, fa, fb, seed=M + N + K, dist=dist)
+    d = to_device(p)
+    run(lib, p, d)
+    c, amax = fetch(p, d)
+    c_ref, s_ref, amax_ref = _oracle_full(p)
+    ratio = check_c(c, c_ref, s_ref, f"{M}x{N}x{K}x{L}")
+    check_amax(amax, amax_ref)
+    assert float_bits(amax) == amax_bits_of(c)
+    print(f"  max |diff|/bound = {ratio:.3g}", flush=True)
+
+
+# The opt-in FP8 matrix path keeps, per 8-element K group, only the bits of
+# each product down to 2^-13 of the group's largest product P, so at most 7
+# products lose less than 2^-13 * P <= 2^-13 * sum|p| each: |error| stays
+# below 2^-10 * sum_k |A_hat||B_hat| (plus fp32 rounding).
+FP8_MFMA_REL = 2.0 ** -10
+
+
+@pytest.mark.parametrize("dist", ["normal", "student_t3"])
+@pytest.mark.parametrize("M,N,K,L,sf,fa,fb", SMALL[:6])
+def test_fp8_mfma_mode_within_model_bound(lib, M, N, K, L, sf, fa, fb, dist):
+    print(f"fp8-mfma case M={M} N={N} K={K} L={L} sf={sf} fmt={fa}{fb} {dist}", flush=True)
+    p = W.make_problem(M, N, K, L, sf, fa, fb, seed=M + N + K, dist=dist)
+    d = to_device(p)
+    run(lib, p, d, flags=lib.MXG_FLAG_FP8_MFMA)
+    c, amax = fetch(p, d)
+    c_ref, s_ref, amax_ref = _oracle_full(p)
+    err = np.abs(c.astype(np.float64) - c_ref)
+    bound = FP8_MFMA_REL * s_ref + 1e-30
+    assert np.all(err <= bound), f"max err/bound {np.max(err / bound):.3g}"
+    assert float_bits(amax) == amax_bits_of(c)
+    print(f"  max |diff|/(1e-5 S) = {np.max(err / (1e-5 * s_ref + 1e-30)):.3g}", flush=True)
+
+
+@pytest.mark.parametrize("wid", [1, 2])
+def test_workload_full_oracle(lib, wid):
+    print(f"workload {wid}", flush=True)
+    p = W.make_workload(wid)
+    d = to_device(p)
+    run(lib, p, d)
+    c, amax = fetch(p, d)
+    c_ref, s_ref, amax_ref = _oracle_full(p)
+    ratio = check_c(c, c_ref, s_ref, f"workload {wid}")
+    check_amax(amax, amax_ref)
+    assert float_bits(amax) == amax_bits_of(c)
+    print(f"  max |diff|/bound = {ratio:.3g}", flush=True)
+
+
+def _sample_rows(p, rng, count):
+    M = p["M"]
+    rows = set(rng.integers(0, M, count).tolist())
+    rows.update([0, M - 1, min(M - 1, 127), min(M - 1, 128), min(M - 1, 255), min(M - 1, 256)])
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("wid", [3, 4, 5])
+def test_workload_sampled(lib, wid):
+    print(f"workload {wid}", flush=True)
+    p = W.make_workload(wid)
+    d = to_device(p)
+    run(lib, p, d)
+    c, amax = fetch(p, d)
+    assert not np.isnan(c).any(), "unwritten or NaN outputs"
+    assert float_bits(amax) == amax_bits_of(c)
+    rng = np.random.default_rng(100 + wid)
+    args = (p["A"], p["B"], p["SFA"], p["SFB"], p["M"], p["N"], p["K"], p["L"], p["sf"], p["a_fmt"], p["b_fmt"])
+    worst = 0.0
+    for batch in sorted(set([0, p["L"] - 1] + ([p["outlier"][0]] if p["outlier"] else []))):
+        rows = _sample_rows(p, rng, 24)
+        if p["outlier"] and p["outlier"][0] == batch:
+            rows = np.union1d(rows, [p["outlier"][1]])
+        cr, sr = oracle.gemm_rows(*args, batch, rows)
+        worst = max(worst, check_c(c[batch, rows], cr, sr, f"workload {wid} batch {batch}"))
+        if p["outlier"] and p["outlier"][0] == batch:
+            # the planted outlier's row holds a large |C|: Amax is at least its oracle maximum
+            assert amax >= np.max(np.abs(cr)) * (1 - 1e-5)
+    il = rng.integers(0, p["L"], 4000)
+    im = rng.integers(0, p["M"], 4000)
+    jn = rng.integers(0, p["N"], 4000)
+    ce, se = oracle.gemm_entries(*args, il, im, jn)
+    worst = max(worst, check_c(c[il, im, jn], ce, se, f"workload {wid} entries"))
+    print(f"  max |diff|/bound = {worst:.3g}", flush=True)
+
+
+def test_scale_plus_one_doubles_bitwise(lib):
+    p = W.make_problem(520, 264, 384, 2, 32, E4, E5, seed=11)
+    d = to_device(p)
+    run(lib, p, d)
+    c0, a0 = fetch(p, d)
+    d["SFA"] += 1          # every scale byte +1: 2x every product (bytes stay < 255 here)
+    run(lib, p, d)
+    c1, a1 = fetch(p, d)
+    assert np.array_equal(c1, 2 * c0)
+    assert a1 == 2 * a0
+
+
+def test_sign_flip_negates(lib):
+    # Flipping every A sign bit negates C.  The bf16 MFMA truncates its
+    # 16-product partial sums toward zero before the round-to-nearest add into
+    # the accumulator, so the negation is checked to the tolerance rather than
+    # bitwise; the count of bitwise differences is reported.
+    p = W.make_problem(300, 200, 256, 1, 16, E5, E4, seed=12)
+    d = to_device(p)
+    run(lib, p, d)
+    c0, a0 = fetch(p, d)
+    d["A"] ^= 0x80
+    run(lib, p, d)
+    c1, a1 = fetch(p, d)
+    _, s_ref, _ = _oracle_full(p)
+    assert np.all(np.abs(c1.astype(np.float64) + c0) <= 2e-5 * s_ref)
+    assert abs(a1 - a0) <= 1e-5 * a0
+    print(f"  bitwise-different entries: {int(np.sum(c1 != -c0))} of {c0.size}", flush=True)
+
+
+def test_deterministic_and_padding_poison(lib):
+    # padding SF bytes set to 0xFF (NaN scale) must never reach the result
+    p = W.make_problem(200, 196, 592, 2, 32, E4, E4, seed=13, pad_byte=0xFF)
+    d = to_device(p)
+    run(lib, p, d)
+    c0, a0 = fetch(p, d)
+    run(lib, p, d)
+    c1, a1 = fetch(p, d)
+    assert np.array_equal(c0.view(np.uint32), c1.view(np.uint32)) and a0 == a1
+    c_ref, s_ref, amax_ref = _oracle_full(p)
+    check_c(c0, c_ref, s_ref, "poisoned padding")
+    check_amax(a0, amax_ref)
+
+
+def test_guard_band_untouched(lib):
+    p = W.make_problem(130, 68, 160, 2, 16, E4, E4, seed=14)
+    pad = 1024
+    d = to_device(p, pad_c=pad, c_fill=12345.0)
+    run(lib, p, d)
+    torch.cuda.synchronize()
+    full = d["C_full"].cpu().numpy()
+    assert np.all(full[:pad] == 12345.0) and np.all(full[-pad:] == 12345.0)
+    assert not np.any(full[pad:-pad] == 12345.0)
+
+
+def test_accumulate_flag(lib):
+    p = W.make_problem(128, 128, 128, 1, 32, E4, E4, seed=15)
+    d = to_device(p)
+    run(lib, p, d)
+    c, amax = fetch(p, d)
+    d["Amax"].fill_(1e30)
+    run(lib, p, d, flags=lib.MXG_FLAG_AMAX_ACCUMULATE)
+    assert fetch(p, d)[1] == np.float32(1e30)
+    d["Amax"].fill_(0.0)
+    run(lib, p, d, flags=lib.MXG_FLAG_AMAX_ACCUMULATE)
+    assert fetch(p, d)[1] == amax
+    lib.mxgemm_amax_reset(d["Amax"])
+    assert fetch(p, d)[1] == 0.0
+
+
+def test_empty_and_k_zero(lib):
+    dev = torch.device("cuda:0")
+    amax = torch.full((4,), 7.0, device=dev)
+    c = torch.full((64 * 32,), 5.0, device=dev)
+    # K = 0: an empty sum, C = 0 and Amax = 0
+    lib.mxgemm_amax(None, None, None, None, c, amax, 64, 32, 0, 1, 32, E4, E4)
+    torch.cuda.synchronize()
+    assert torch.all(c == 0).item() and amax[0].item() == 0.0
+    # M = 0: nothing to compute, Amax = 0
+    amax.fill_(7.0)
+    lib.mxgemm_amax(None, None, None, None, None, amax, 0, 32, 64, 1, 32, E4, E4)
+    torch.cuda.synchronize()
+    assert amax[0].item() == 0.0
+
+
+def test_host_pointer_rejected(lib):
+    p = W.make_problem(128, 128, 128, 1, 32, E4, E4, seed=16)
+    d = to_device(p)
+    host_c = torch.empty(128 * 128, dtype=torch.float32, pin_memory=False)
+    with pytest.raises(lib.MxgemmRuntimeError):
+        lib.mxgemm_amax(d["A"], d["B"], d["SFA"], d["SFB"], host_c, d["Amax"], 128, 128, 128, 1, 32, E4, E4)
+
+
+def test_high_level_wrapper_logical_sf(lib):
+    M, N, K, L, sf = 256, 192, 256, 2, 32
+    p = W.make_problem(M, N, K, L, sf, E4, E4, seed=17)
+    dev = torch.device("cuda:0")
+    a = torch.from_numpy(p["A"]).to(dev).view(torch.float8_e4m3fn).permute(1, 2, 0)   # (M, K, L) k-major
+    b = torch.from_numpy(p["B"]).to(dev).view(torch.float8_e4m3fn).permute(1, 2, 0)
+    mnb_a, mnb_b, kg = M // 128, -(-N // 128), K // (4 * sf)
+    sfa = torch.from_numpy(p["SFA"]).to(dev).view(L, mnb_a, kg, 32, 4, 4).permute(3, 4, 1, 5, 2, 0)
+    sfb = torch.from_numpy(p["SFB"]).to(dev).view(torch.float8_e8m0fnu).view(L, mnb_b, kg, 32, 4, 4)
+    c, amax = lib.gemm_amax(a, b, sfa, sfb, sf_vec_size=sf)
+    torch.cuda.synchronize()
+    assert tuple(c.shape) == (M, N, L) and c.stride() == (N, 1, M * N)
+    c_ref, s_ref, amax_ref = _oracle_full(p)
+    check_c(c.permute(2, 0, 1).cpu().numpy(), c_ref, s_ref, "wrapper")
+    check_amax(amax.item(), amax_ref)
