@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <mutex>
+#include <stdlib.h>
 #include <string.h>
 
 #include "../../include/mxgemm.h"
@@ -39,8 +40,9 @@ int check_sizes(int64_t M, int64_t N, int64_t K, int64_t L, int sf, int a_fmt, i
   if (M && K && L && (M > lim / K || M * K > lim / L)) return MXG_ERR_SHAPE;
   if (N && K && L && (N > lim / K || N * K > lim / L)) return MXG_ERR_SHAPE;
   if (M && N && L && (M > lim / N || M * N > lim / (4 * L))) return MXG_ERR_SHAPE;
-  // one tile's rows (up to 256) of A or B must be addressable with 32-bit offsets
-  if (K > (1LL << 23)) return MXG_ERR_SHAPE;
+  // one tile's rows (up to 256) of A, B or C must be addressable with 32-bit
+  // buffer offsets
+  if (K > (1LL << 23) || N > (1LL << 22) - 4) return MXG_ERR_SHAPE;
   if (K % 16 != 0) return MXG_ERR_ALIGN;
   if (N % 4 != 0) return MXG_ERR_ALIGN;
   return MXG_OK;
@@ -79,29 +81,14 @@ bool on_device(const void* p, int dev) {
   return attr.device == dev;
 }
 
-struct TileChoice {
-  int bm, bn, occ;
-};
+// One tile shape: 128x128 per workgroup, two workgroups per CU (so one's
+// barrier waits overlap the other's math), 4 waves of 64x64.
+constexpr int kTileM = mxg::kBM, kTileN = mxg::kBN, kWgPerCu = 2;
 
-// Per-shape tile choice.  256x256 tiles (4 waves of 128x128) halve LDS and
-// L2 traffic per flop against 128x128, but a shape with few tiles would
-// leave CUs idle: estimate the time of both and keep the faster.
-TileChoice choose_tiles(int64_t M, int64_t N, int64_t L, int cus) {
-  const int64_t t256 = L * cdiv(M, 256) * cdiv(N, 256);
-  const int64_t t128 = L * cdiv(M, 128) * cdiv(N, 128);
-  // relative per-tile cost: a 256x256 tile is 4x the work of a 128x128 one
-  // and runs at ~1.4x its flop rate; 128x128 runs two workgroups per CU.
-  const double w256 = (double)cdiv(t256, cus) * 4.0 / 1.4;
-  const double w128 = (double)cdiv(t128, 2LL * cus) * 2.0;
-  if (t256 >= cus && w256 <= w128) return {256, 256, 1};
-  return {128, 128, 2};
-}
-
-template <int BM, int BN, int MODE, int OCC>
-hipError_t launch_tiles(const mxg::Params& p, int sf, int fa, int fb, int64_t grid, hipStream_t s) {
+template <int MODE>
+hipError_t launch_mode(const mxg::Params& p, int sf, int fa, int fb, int64_t grid, hipStream_t s) {
   const dim3 g((unsigned)grid), b(mxg::kThreads);
-#define MXG_LAUNCH(SF, FA, FB) \
-  hipLaunchKernelGGL((mxg::mxgemm_amax_kernel<BM, BN, SF, FA, FB, MODE, OCC>), g, b, 0, s, p)
+#define MXG_LAUNCH(SF, FA, FB) hipLaunchKernelGGL((mxg::mxgemm_amax_kernel<SF, FA, FB, MODE>), g, b, 0, s, p)
   if (sf == 32) {
     if (fa == 0 && fb == 0) MXG_LAUNCH(32, 0, 0);
     else if (fa == 0 && fb == 1) MXG_LAUNCH(32, 0, 1);
@@ -146,12 +133,11 @@ int mxgemm_launch_config(int64_t M, int64_t N, int64_t K, int64_t L, int sf_vec_
     st = device_check(&dev, &cus);
     if (st != MXG_OK) return st;
   }
-  const TileChoice tc = choose_tiles(M, N, L, cus);
-  if (tile_m) *tile_m = tc.bm;
-  if (tile_n) *tile_n = tc.bn;
+  if (tile_m) *tile_m = kTileM;
+  if (tile_n) *tile_n = kTileN;
   if (grid) {
-    const int64_t tiles = L * cdiv(M, tc.bm) * cdiv(N, tc.bn);
-    *grid = grid_for(tiles, cus, tc.occ);
+    const int64_t tiles = L * cdiv(M, kTileM) * cdiv(N, kTileN);
+    *grid = grid_for(tiles, cus, kWgPerCu);
   }
   return MXG_OK;
 }
@@ -196,7 +182,6 @@ int mxgemm_amax_ex(const void* A, const void* B, const uint8_t* SFA, const uint8
   }
   if (!need_c) return MXG_OK;
 
-  const TileChoice tc = choose_tiles(M, N, L, cus);
   mxg::Params p;
   p.A = static_cast<const uint8_t*>(A);
   p.B = static_cast<const uint8_t*>(B);
@@ -212,21 +197,16 @@ int mxgemm_amax_ex(const void* A, const void* B, const uint8_t* SFA, const uint8
   p.Kg = (int)cdiv(K, 4 * sf_vec_size);
   p.MNbA = (int)cdiv(M, 128);
   p.MNbB = (int)cdiv(N, 128);
-  p.tilesM = (int)cdiv(M, tc.bm);
-  p.tilesN = (int)cdiv(N, tc.bn);
+  p.tilesM = (int)cdiv(M, kTileM);
+  p.tilesN = (int)cdiv(N, kTileN);
   p.ksteps = (int)cdiv(K, mxg::kBK);
   p.num_tiles = L * (int64_t)p.tilesM * p.tilesN;
-  const int64_t grid = grid_for(p.num_tiles, cus, tc.occ);
+  const int64_t grid = grid_for(p.num_tiles, cus, kWgPerCu);
   p.xcd_remap = (grid % 8 == 0) ? 1 : 0;
 
-  hipError_t e;
-  const bool fp8 = (flags & MXG_FLAG_FP8_MFMA) != 0;
-  if (tc.bm == 256)
-    e = fp8 ? launch_tiles<256, 256, mxg::kModeFp8, 1>(p, sf_vec_size, a_fmt, b_fmt, grid, s)
-            : launch_tiles<256, 256, mxg::kModeBf16, 1>(p, sf_vec_size, a_fmt, b_fmt, grid, s);
-  else
-    e = fp8 ? launch_tiles<128, 128, mxg::kModeFp8, 2>(p, sf_vec_size, a_fmt, b_fmt, grid, s)
-            : launch_tiles<128, 128, mxg::kModeBf16, 2>(p, sf_vec_size, a_fmt, b_fmt, grid, s);
+  const hipError_t e = (flags & MXG_FLAG_FP8_MFMA)
+                          ? launch_mode<mxg::kModeFp8>(p, sf_vec_size, a_fmt, b_fmt, grid, s)
+                          : launch_mode<mxg::kModeBf16>(p, sf_vec_size, a_fmt, b_fmt, grid, s);
   return e == hipSuccess ? MXG_OK : MXG_ERR_LAUNCH;
 }
 

@@ -109,7 +109,7 @@ enum {
  *   stream     hipStream_t (NULL = null stream).
  *
  * Requirements: A, B, C, Amax, SFA, SFB 16-byte aligned; K % 16 == 0 (16-byte
- * rows of A/B) and K <= 2^23; N % 4 == 0 (16-byte rows of C) -- the page's "16-byte aligned along
+ * rows of A/B) and K <= 2^23; N % 4 == 0 (16-byte rows of C) and N < 2^22 -- the page's "16-byte aligned along
  * the contiguous dimension" (section "Support surface and constraints",
  * Layouts and strides).  Current device must be gfx950 and own every pointer.
  *

@@ -68,7 +68,7 @@ def test_sf_bytes(lib):
 
 def test_launch_config_host_only(lib):
     tm, tn, g = lib.mxgemm_launch_config(8192, 24576, 1536, 1, 32, with_grid=False)
-    assert (tm, tn, g) == (256, 256, None)
+    assert (tm, tn, g) == (128, 128, None)
     tm, tn, _ = lib.mxgemm_launch_config(2048, 2048, 2048, 1, 32, with_grid=False)
     assert (tm, tn) == (128, 128)
 
