@@ -18,8 +18,12 @@ timed on a bounded sample on this host.
 """
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -31,6 +35,122 @@ if ROOT not in sys.path:
 PEAK_BF16 = 2500.0
 PEAK_FP8 = 5000.0
 HBM_GBS = 8000.0
+
+CSRC = os.path.join(ROOT, "block_scaled_precision_e4m3_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+COPY_PROBE_BYTES = 1 << 30   # float32 bytes read (and written) by each calibration copy
+
+
+def kernel_source_hash():
+    """Short digest of the HIP sources; a traffic figure is only valid for the source it was taken on."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".hpp", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def profile_name(workload_name, fp8_mfma):
+    return f"mxgemm_amax_kernel_{'fp8' if fp8_mfma else 'bf16'}__{workload_name}.txt"
+
+
+def read_traffic(workload_name, fp8_mfma):
+    """HBM bytes per launch from the committed counter summary, or None if absent or taken on other sources."""
+    path = os.path.join(PROFILES, profile_name(workload_name, fp8_mfma))
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            m = re.match(r"^([a-z_0-9]+):\s*(\S+)\s*$", line)
+            if m:
+                kv[m.group(1)] = m.group(2)
+    if kv.get("kernel_source_sha256") != kernel_source_hash() or "traffic_bytes_per_launch" not in kv:
+        return None
+    return int(kv["traffic_bytes_per_launch"])
+
+
+def copy_probe():
+    """Three launches of a plain elementwise copy (y = -x, float32) of COPY_PROBE_BYTES: the
+    calibration kernel for the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = COPY_PROBE_BYTES // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+
+
+def _csv_rows(pattern):
+    rows = []
+    for f in sorted(glob.glob(pattern, recursive=True)):
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def _per_dispatch(rows, kernel_substr, counter):
+    per = {}
+    for r in rows:
+        if kernel_substr in r["Kernel_Name"] and r["Counter_Name"] == counter:
+            per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    return list(per.values())
+
+
+def rocprof_summary(d, workload, fp8_mfma, commands):
+    """Text summary of a rocprofv3 kernel trace (d/kt) and two counter passes (d/fetch, d/write)."""
+    import workloads as W
+    cfg = W.WORKLOADS[workload]
+    M, N, K, L, sf = cfg["M"], cfg["N"], cfg["K"], cfg["L"], cfg["sf"]
+    out = [f"# rocprofv3 summary: mxgemm_amax_kernel ({'fp8 MFMA' if fp8_mfma else 'bf16 MFMA'} path), "
+           f"workload {cfg['name']} (M={M} N={N} K={K} L={L} sf={sf})", ""]
+    out.append("commands (from the repository root; rocprofv3 runs from /tmp with TMPDIR=/tmp):")
+    out.extend("  " + c for c in commands)
+    out.append("")
+    stats = _csv_rows(os.path.join(d, "kt", "**", "*kernel_stats.csv"))
+    out.append("kernel trace (--kernel-trace --stats):")
+    avg_us = None
+    for r in stats:
+        name = r["Name"]
+        out.append(f"  {name[:100]:100s} calls {int(r['Calls']):5d}  avg {float(r['AverageNs']) / 1e3:10.2f} us  "
+                   f"min {float(r['MinNs']) / 1e3:10.2f}  max {float(r['MaxNs']) / 1e3:10.2f}  "
+                   f"{float(r['Percentage']):5.1f}%")
+        if "mxgemm_amax_kernel" in name:
+            avg_us = float(r["AverageNs"]) / 1e3
+    out.append("")
+    fl = W.flops(M, N, K, L)
+    if avg_us:
+        out.append(f"gemm_avg_duration_us: {avg_us:.2f}")
+        out.append(f"gemm_tflops_at_avg_duration: {fl / (avg_us * 1e-6) / 1e12:.1f}")
+    fetch = _csv_rows(os.path.join(d, "fetch", "**", "*counter_collection.csv"))
+    write = _csv_rows(os.path.join(d, "write", "**", "*counter_collection.csv"))
+    if fetch and write:
+        gf = _per_dispatch(fetch, "mxgemm_amax_kernel", "FETCH_SIZE")
+        gw = _per_dispatch(write, "mxgemm_amax_kernel", "WRITE_SIZE")
+        cf = _per_dispatch(fetch, "neg", "FETCH_SIZE")
+        cw = _per_dispatch(write, "neg", "WRITE_SIZE")
+        f_fac = COPY_PROBE_BYTES / (1024.0 * sum(cf) / len(cf))
+        w_fac = COPY_PROBE_BYTES / (1024.0 * sum(cw) / len(cw))
+        fb = sum(gf) / len(gf) * 1024.0 * f_fac
+        wb = sum(gw) / len(gw) * 1024.0 * w_fac
+        ab = W.algorithmic_bytes(M, N, K, L, sf)
+        out += ["",
+                "HBM traffic (--pmc FETCH_SIZE, then --pmc WRITE_SIZE; KiB per dispatch):",
+                f"  gemm FETCH_SIZE per dispatch (KiB, mean of {len(gf)}): {sum(gf) / len(gf):.0f}",
+                f"  gemm WRITE_SIZE per dispatch (KiB, mean of {len(gw)}): {sum(gw) / len(gw):.0f}",
+                f"  copy probe (y = -x, {COPY_PROBE_BYTES} B read + {COPY_PROBE_BYTES} B written): "
+                f"FETCH_SIZE {sum(cf) / len(cf):.0f} KiB, WRITE_SIZE {sum(cw) / len(cw):.0f} KiB",
+                f"  calibration factors (true bytes / counter bytes): fetch {f_fac:.4f}, write {w_fac:.4f}",
+                f"fetch_bytes_per_launch: {fb:.0f}",
+                f"write_bytes_per_launch: {wb:.0f}",
+                f"traffic_bytes_per_launch: {fb + wb:.0f}",
+                f"algorithmic_bytes_per_launch: {ab}",
+                f"traffic_over_algorithmic: {(fb + wb) / ab:.3f}"]
+    out += ["", f"kernel_source_sha256: {kernel_source_hash()}"]
+    return "\n".join(out) + "\n"
 
 
 def cpu_baseline(p, target_s=12.0):
@@ -74,7 +194,17 @@ def main():
     ap.add_argument("--workload", type=int, default=5)
     ap.add_argument("--fp8-mfma", action="store_true", help="time the reduced-precision FP8 MFMA path")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after the timed steps, run the copy kernel that calibrates the HBM byte counters")
+    ap.add_argument("--rocprof-summary", metavar="DIR",
+                    help="no GPU work: summarise rocprofv3 output under DIR (kt/, fetch/, write/) and print it")
+    ap.add_argument("--command", action="append", default=[],
+                    help="with --rocprof-summary: a command line to record in the summary (repeatable)")
     args = ap.parse_args()
+
+    if args.rocprof_summary:
+        print(rocprof_summary(args.rocprof_summary, args.workload, args.fp8_mfma, args.command), end="")
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this path runs on one GPU only; multi-GPU runs are not part of this build "
@@ -149,10 +279,13 @@ def main():
         "pct_of_mxfp8_peak": round(100.0 * achieved / PEAK_FP8, 2),
         "kernel_ms": round(kernel_ms, 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "frac": round(achieved / peak, 4),
+                     "traffic": read_traffic(W.WORKLOADS[args.workload]["name"], args.fp8_mfma),
                      "algorithmic_bytes": abytes,
                      "algorithmic_GBps": round(abytes / (kernel_ms * 1e-3) / 1e9, 1)},
     }
+    if args.copy_probe:
+        copy_probe()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p)
     print(json.dumps(out), flush=True)
