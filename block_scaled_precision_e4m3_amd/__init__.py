@@ -28,6 +28,8 @@ MXG_FMT_E4M3 = 0
 MXG_FMT_E5M2 = 1
 MXG_FLAG_AMAX_ACCUMULATE = 1
 MXG_FLAG_FP8_MFMA = 2
+MXG_FLAG_TILE_128 = 4
+MXG_FLAG_TILE_256 = 8
 
 MXG_OK = 0
 MXG_ERR_NULL = -1
@@ -220,6 +222,7 @@ def gemm_amax(a, b, sfa, sfb, c=None, amax=None, sf_vec_size=32, stream=None, ac
 __all__ = [
     "mxgemm_amax", "mxgemm_amax_ex", "mxgemm_amax_reset", "mxgemm_check_support", "mxgemm_sf_bytes",
     "mxgemm_launch_config", "mxgemm_strerror", "gemm_amax", "LIB_PATH", "EXPORTED",
-    "MXG_FMT_E4M3", "MXG_FMT_E5M2", "MXG_FLAG_AMAX_ACCUMULATE", "MXG_FLAG_FP8_MFMA", "MxgemmError", "MxgemmValueError",
+    "MXG_FMT_E4M3", "MXG_FMT_E5M2", "MXG_FLAG_AMAX_ACCUMULATE", "MXG_FLAG_FP8_MFMA", "MXG_FLAG_TILE_128",
+    "MXG_FLAG_TILE_256", "MxgemmError", "MxgemmValueError",
     "MxgemmRuntimeError",
 ]

@@ -10,6 +10,7 @@
 #include <string.h>
 
 #include "../../include/mxgemm.h"
+#include "mxgemm_big.hpp"
 #include "mxgemm_kernel.hpp"
 
 namespace {
@@ -43,6 +44,8 @@ int check_sizes(int64_t M, int64_t N, int64_t K, int64_t L, int sf, int a_fmt, i
   // one tile's rows (up to 256) of A, B or C must be addressable with 32-bit
   // buffer offsets
   if (K > (1LL << 23) || N > (1LL << 22) - 4) return MXG_ERR_SHAPE;
+  // tile and tile-step counts are 32-bit in the kernels
+  if (L * cdiv(M, 128) * cdiv(N, 128) * (cdiv(K, 128) + 1) > 0x7FFFFFFFLL) return MXG_ERR_SHAPE;
   if (K % 16 != 0) return MXG_ERR_ALIGN;
   if (N % 4 != 0) return MXG_ERR_ALIGN;
   return MXG_OK;
@@ -81,14 +84,38 @@ bool on_device(const void* p, int dev) {
   return attr.device == dev;
 }
 
-// One tile shape: 128x128 per workgroup, two workgroups per CU (so one's
-// barrier waits overlap the other's math), 4 waves of 64x64.
-constexpr int kTileM = mxg::kBM, kTileN = mxg::kBN, kWgPerCu = 2;
+// Two tile shapes.  Small: 128x128 per workgroup, two workgroups per CU,
+// 4 waves of 64x64.  Big: 256x256 per workgroup, one per CU, 4 waves of
+// 128x128; half the L2->LDS bytes per flop, used when its tiles fill the
+// chip at least as evenly as the small ones do.
+struct Config {
+  bool big;
+  int tile_m, tile_n, per_cu;
+};
 
-template <int MODE>
+double fill(int64_t tiles, int64_t slots) {
+  if (tiles <= 0) return 0.0;
+  const int64_t waves = cdiv(tiles, slots);
+  return (double)tiles / (double)(waves * slots);
+}
+
+Config choose(int64_t M, int64_t N, int64_t K, int64_t L, int cus) {
+  const int64_t small = L * cdiv(M, 128) * cdiv(N, 128);
+  const int64_t big = L * cdiv(M, 256) * cdiv(N, 256);
+  if (K > 0 && big >= cus && fill(big, cus) >= fill(small, 2 * (int64_t)cus) - 1e-9) return {true, 256, 256, 1};
+  return {false, 128, 128, 2};
+}
+
+template <int MODE, bool BIG>
 hipError_t launch_mode(const mxg::Params& p, int sf, int fa, int fb, int64_t grid, hipStream_t s) {
-  const dim3 g((unsigned)grid), b(mxg::kThreads);
-#define MXG_LAUNCH(SF, FA, FB) hipLaunchKernelGGL((mxg::mxgemm_amax_kernel<SF, FA, FB, MODE>), g, b, 0, s, p)
+  const dim3 g((unsigned)grid), b(BIG ? mxg::big::kThreads : mxg::kThreads);
+#define MXG_LAUNCH(SF, FA, FB)                                                                         \
+  do {                                                                                                 \
+    if constexpr (BIG)                                                                                 \
+      hipLaunchKernelGGL((mxg::big::mxgemm_amax_big_kernel<SF, FA, FB, MODE>), g, b, 0, s, p);         \
+    else                                                                                               \
+      hipLaunchKernelGGL((mxg::mxgemm_amax_kernel<SF, FA, FB, MODE>), g, b, 0, s, p);                  \
+  } while (0)
   if (sf == 32) {
     if (fa == 0 && fb == 0) MXG_LAUNCH(32, 0, 0);
     else if (fa == 0 && fb == 1) MXG_LAUNCH(32, 0, 1);
@@ -133,11 +160,12 @@ int mxgemm_launch_config(int64_t M, int64_t N, int64_t K, int64_t L, int sf_vec_
     st = device_check(&dev, &cus);
     if (st != MXG_OK) return st;
   }
-  if (tile_m) *tile_m = kTileM;
-  if (tile_n) *tile_n = kTileN;
+  const Config cfg = choose(M, N, K, L, cus);
+  if (tile_m) *tile_m = cfg.tile_m;
+  if (tile_n) *tile_n = cfg.tile_n;
   if (grid) {
-    const int64_t tiles = L * cdiv(M, kTileM) * cdiv(N, kTileN);
-    *grid = grid_for(tiles, cus, kWgPerCu);
+    const int64_t tiles = L * cdiv(M, cfg.tile_m) * cdiv(N, cfg.tile_n);
+    *grid = grid_for(tiles, cus, cfg.per_cu);
   }
   return MXG_OK;
 }
@@ -159,7 +187,9 @@ int mxgemm_amax_ex(const void* A, const void* B, const uint8_t* SFA, const uint8
                    unsigned flags, void* stream) {
   int st = check_sizes(M, N, K, L, sf_vec_size, a_fmt, b_fmt);
   if (st != MXG_OK) return st;
-  if (flags & ~(unsigned)(MXG_FLAG_AMAX_ACCUMULATE | MXG_FLAG_FP8_MFMA)) return MXG_ERR_FLAGS;
+  if (flags & ~(unsigned)(MXG_FLAG_AMAX_ACCUMULATE | MXG_FLAG_FP8_MFMA | MXG_FLAG_TILE_128 | MXG_FLAG_TILE_256))
+    return MXG_ERR_FLAGS;
+  if ((flags & MXG_FLAG_TILE_128) && (flags & MXG_FLAG_TILE_256)) return MXG_ERR_FLAGS;
   // A, B and the scales are read only when there is a non-empty C and a non-empty K
   const bool need_c = M > 0 && N > 0 && L > 0;
   const bool need_a = need_c && K > 0, need_b = need_a;
@@ -197,16 +227,24 @@ int mxgemm_amax_ex(const void* A, const void* B, const uint8_t* SFA, const uint8
   p.Kg = (int)cdiv(K, 4 * sf_vec_size);
   p.MNbA = (int)cdiv(M, 128);
   p.MNbB = (int)cdiv(N, 128);
-  p.tilesM = (int)cdiv(M, kTileM);
-  p.tilesN = (int)cdiv(N, kTileN);
-  p.ksteps = (int)cdiv(K, mxg::kBK);
-  p.num_tiles = L * (int64_t)p.tilesM * p.tilesN;
-  const int64_t grid = grid_for(p.num_tiles, cus, kWgPerCu);
+  Config cfg = choose(M, N, K, L, cus);
+  if (flags & MXG_FLAG_TILE_128) cfg = {false, 128, 128, 2};
+  if ((flags & MXG_FLAG_TILE_256) && K > 0) cfg = {true, 256, 256, 1};
+  p.tilesM = (int)cdiv(M, cfg.tile_m);
+  p.tilesN = (int)cdiv(N, cfg.tile_n);
+  p.ksteps = (int)cdiv(K, 128);
+  p.num_tiles = (int)(L * p.tilesM * p.tilesN);
+  const int64_t grid = grid_for(p.num_tiles, cus, cfg.per_cu);
   p.xcd_remap = (grid % 8 == 0) ? 1 : 0;
 
-  const hipError_t e = (flags & MXG_FLAG_FP8_MFMA)
-                          ? launch_mode<mxg::kModeFp8>(p, sf_vec_size, a_fmt, b_fmt, grid, s)
-                          : launch_mode<mxg::kModeBf16>(p, sf_vec_size, a_fmt, b_fmt, grid, s);
+  const bool fp8 = (flags & MXG_FLAG_FP8_MFMA) != 0;
+  hipError_t e;
+  if (cfg.big)
+    e = fp8 ? launch_mode<mxg::kModeFp8, true>(p, sf_vec_size, a_fmt, b_fmt, grid, s)
+            : launch_mode<mxg::kModeBf16, true>(p, sf_vec_size, a_fmt, b_fmt, grid, s);
+  else
+    e = fp8 ? launch_mode<mxg::kModeFp8, false>(p, sf_vec_size, a_fmt, b_fmt, grid, s)
+            : launch_mode<mxg::kModeBf16, false>(p, sf_vec_size, a_fmt, b_fmt, grid, s);
   return e == hipSuccess ? MXG_OK : MXG_ERR_LAUNCH;
 }
 

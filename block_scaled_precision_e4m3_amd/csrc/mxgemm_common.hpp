@@ -1,0 +1,187 @@
+// Pieces shared by the block-scaled FP8 GEMM + amax kernels for gfx950:
+// kernel parameters, tile scheduling, buffer resources and the global->LDS
+// DMA, waits and barriers, E8M0 decoding, the scaled conversions and the
+// scaled FP8 MFMA wrapper.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace mxg {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+constexpr int kGroupM = 8;           // tile rows per raster group
+constexpr int kRsrcFlags = 0x00020000;
+
+constexpr int kModeBf16 = 0;
+constexpr int kModeFp8 = 1;
+
+struct Params {
+  const uint8_t* A;
+  const uint8_t* B;
+  const uint8_t* SFA;
+  const uint8_t* SFB;
+  float* C;
+  unsigned* amax_bits;
+  int M, N, K, L;
+  int Kb;      // ceil(K / sf): K-blocks
+  int Kg;      // ceil(K / (4 sf)): atoms along K
+  int MNbA;    // ceil(M / 128)
+  int MNbB;    // ceil(N / 128)
+  int tilesM, tilesN;
+  int ksteps;  // ceil(K / 128)
+  int num_tiles;   // L * tilesM * tilesN (the host keeps it below 2^31)
+  int xcd_remap;  // 1 when gridDim.x is a multiple of 8
+};
+
+// --- tile scheduling ---------------------------------------------------------
+
+// Tile t -> (batch, tile row, tile column): batch-major, then groups of
+// kGroupM tile rows walked column-major inside a batch.
+__device__ __forceinline__ void tile_coords(const Params& p, int t, int& l, int& tm, int& tn) {
+  const int per_batch = p.tilesM * p.tilesN;
+  l = t / per_batch;
+  const int r = t - l * per_batch;
+  const int group_size = kGroupM * p.tilesN;
+  const int g = r / group_size;
+  const int first_m = g * kGroupM;
+  const int gm = min(p.tilesM - first_m, kGroupM);
+  const int rg = r - g * group_size;
+  tm = first_m + rg % gm;
+  tn = rg / gm;
+}
+
+struct Tile {
+  int l, m0, n0, mvalid, nvalid;
+};
+
+template <int BM, int BN>
+__device__ __forceinline__ Tile make_tile(const Params& p, int t) {
+  int l, tm, tn;
+  tile_coords(p, t, l, tm, tn);
+  Tile T;
+  T.l = __builtin_amdgcn_readfirstlane(l);
+  T.m0 = __builtin_amdgcn_readfirstlane(tm * BM);
+  T.n0 = __builtin_amdgcn_readfirstlane(tn * BN);
+  T.mvalid = min(p.M - T.m0, BM);
+  T.nvalid = min(p.N - T.n0, BN);
+  return T;
+}
+
+// First tile of workgroup b in a grid of G: when G is a multiple of 8 the
+// index is remapped so that the workgroups of one XCD (dispatched
+// round-robin over the 8 XCDs) take a contiguous run of tiles.
+__device__ __forceinline__ int first_tile(const Params& p) {
+  const int G = (int)gridDim.x;
+  const int b = (int)blockIdx.x;
+  return p.xcd_remap ? (b & 7) * (G >> 3) + (b >> 3) : b;
+}
+
+// --- memory helpers ------------------------------------------------------------
+
+// Buffer resource over [base, base + bytes) built from values forced into
+// scalar registers (the DMA asm needs its resource in SGPRs; a value the
+// compiler could not prove wave-uniform would otherwise land in VGPRs).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)a);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
+  void* ptr = (void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ptr, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), kRsrcFlags);
+}
+
+// One 16-byte-per-lane buffer load into LDS at (m0 + 16 * lane).  Issued as
+// inline assembly on purpose: the compiler cannot prove that a DMA into one
+// ring stage does not alias the ds_reads of another, and for the builtin it
+// inserts "s_waitcnt vmcnt(0)" before those reads, which drains the whole
+// prefetch ring every step.  Ordering is kept by explicit per-wave vmcnt
+// waits instead.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, unsigned voff, const uint8_t* lds_dst) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(
+      (unsigned)(size_t)(__attribute__((address_space(3))) const uint8_t*)lds_dst);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs),
+               "s"(m0)
+               : "memory", "m0");
+}
+
+// The same with the LDS destination given as a 32-bit LDS address (m0 value).
+__device__ __forceinline__ void dma16_at(__amdgpu_buffer_rsrc_t rs, unsigned voff, unsigned lds_addr) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_addr);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs),
+               "s"(m0)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// 32-bit LDS address of a __shared__ object.
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(size_t)(__attribute__((address_space(3))) const uint8_t*)p;
+}
+
+// s_waitcnt with vmcnt = N (N <= 63), other counters untouched.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N <= 63, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier without a memory fence.  __syncthreads() also waits for
+// every outstanding vector-memory operation, which would drain the DMA ring
+// and the C stores; here each wave has already waited for the DMA it needs,
+// and every LDS read of a stage is consumed by an MFMA before the wave
+// reaches the next barrier.
+__device__ __forceinline__ void barrier() { __builtin_amdgcn_s_barrier(); }
+
+// E8M0 byte b (low 8 bits) -> the f32 scale operand of the scaled
+// conversions v_cvt_scalef32_pk_bf16_{fp8,bf8}.  Those instructions read only
+// the exponent field of their scale and give it E8M0 meaning: exponent e
+// scales by 2^(e-127), exponent 0 by 2^-127 and exponent 255 makes every
+// result NaN (measured on MI355X for all 256 bytes, mantissa bits ignored).
+// So the byte moved into the exponent field is the operand: one shift.
+__device__ __forceinline__ float e8m0_to_f32(unsigned b) { return __uint_as_float(b << 23); }
+
+template <int OPSEL, int FA, int FB>
+__device__ __forceinline__ v16f mfma_f8(const v8i& b, const v8i& a, const v16f& c, unsigned sb, unsigned sa) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, FB, FA, OPSEL, (int)sb, OPSEL, (int)sa);
+}
+
+// Two FP8 codes (bytes 0,1 or 2,3 of `w`) -> two bf16 times `scale`, as one
+// dword (the pair is bit-cast whole; element-wise extraction of the v2bf16
+// result was seen to duplicate the low half).
+template <int FMT, bool HI>
+__device__ __forceinline__ unsigned cvt2(unsigned w, float scale) {
+  v2bf r;
+  if constexpr (FMT == 0)
+    r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, scale, HI);
+  else
+    r = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, scale, HI);
+  return __builtin_bit_cast(unsigned, r);
+}
+
+// 8 codes (two dwords) -> one bf16 MFMA operand.
+template <int FMT>
+__device__ __forceinline__ v8bf cvt8(unsigned w0, unsigned w1, float scale) {
+  v4u u;
+  u[0] = cvt2<FMT, false>(w0, scale);
+  u[1] = cvt2<FMT, true>(w0, scale);
+  u[2] = cvt2<FMT, false>(w1, scale);
+  u[3] = cvt2<FMT, true>(w1, scale);
+  return __builtin_bit_cast(v8bf, u);
+}
+
+// Clears the Amax bits (queued before a GEMM that does not accumulate).
+__global__ void amax_reset_kernel(unsigned* amax_bits) {
+  if (threadIdx.x == 0) *amax_bits = 0u;
+}
+
+}  // namespace mxg

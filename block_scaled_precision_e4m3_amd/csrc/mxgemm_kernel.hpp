@@ -72,25 +72,13 @@
 // reduced across the wave with xor-shuffles, then one atomic max per wave.
 #pragma once
 
-#include <hip/hip_runtime.h>
-#include <stdint.h>
-
-#include <type_traits>
+#include "mxgemm_common.hpp"
 
 namespace mxg {
-
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef unsigned v4u __attribute__((ext_vector_type(4)));
-typedef float v4f __attribute__((ext_vector_type(4)));
-typedef float v16f __attribute__((ext_vector_type(16)));
-typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
-typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr int kThreads = 256;
 constexpr int kBM = 128, kBN = 128;  // workgroup tile
 constexpr int kBK = 128;             // K bytes per pipeline step
-constexpr int kGroupM = 8;           // tile rows per raster group
-constexpr int kRsrcFlags = 0x00020000;
 
 // LDS stage: A tile, B tile, then the SF atoms of A and of B (up to two
 // atoms each: sf=16 needs two per 128-K step)
@@ -107,102 +95,6 @@ constexpr int kTM = 2, kTN = 2;  // MFMA blocks per wave
 constexpr int kNStores = kTM * kTN * 4;
 constexpr int kStoresPerStep = 2;
 constexpr int kStoreSteps = kNStores / kStoresPerStep;
-
-constexpr int kModeBf16 = 0;
-constexpr int kModeFp8 = 1;
-
-struct Params {
-  const uint8_t* A;
-  const uint8_t* B;
-  const uint8_t* SFA;
-  const uint8_t* SFB;
-  float* C;
-  unsigned* amax_bits;
-  int M, N, K, L;
-  int Kb;      // ceil(K / sf): K-blocks
-  int Kg;      // ceil(K / (4 sf)): atoms along K
-  int MNbA;    // ceil(M / 128)
-  int MNbB;    // ceil(N / 128)
-  int tilesM, tilesN;
-  int ksteps;  // ceil(K / 128)
-  int64_t num_tiles;
-  int xcd_remap;  // 1 when gridDim.x is a multiple of 8
-};
-
-// --- tile scheduling ---------------------------------------------------------
-
-__device__ __forceinline__ void tile_coords(const Params& p, int64_t t, int& l, int& tm, int& tn) {
-  const int per_batch = p.tilesM * p.tilesN;
-  l = (int)(t / per_batch);
-  const int r = (int)(t - (int64_t)l * per_batch);
-  const int group_size = kGroupM * p.tilesN;
-  const int g = r / group_size;
-  const int first_m = g * kGroupM;
-  const int gm = min(p.tilesM - first_m, kGroupM);
-  const int rg = r - g * group_size;
-  tm = first_m + rg % gm;
-  tn = rg / gm;
-}
-
-struct Tile {
-  int l, m0, n0, mvalid, nvalid;
-};
-
-__device__ __forceinline__ Tile make_tile(const Params& p, int64_t t) {
-  int l, tm, tn;
-  tile_coords(p, t, l, tm, tn);
-  Tile T;
-  T.l = __builtin_amdgcn_readfirstlane(l);
-  T.m0 = __builtin_amdgcn_readfirstlane(tm * kBM);
-  T.n0 = __builtin_amdgcn_readfirstlane(tn * kBN);
-  T.mvalid = min(p.M - T.m0, kBM);
-  T.nvalid = min(p.N - T.n0, kBN);
-  return T;
-}
-
-// --- memory helpers ------------------------------------------------------------
-
-// Buffer resource over [base, base + bytes) built from values forced into
-// scalar registers (the DMA asm needs its resource in SGPRs; a value the
-// compiler could not prove wave-uniform would otherwise land in VGPRs).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
-  const uint64_t a = (uint64_t)(uintptr_t)base;
-  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)a);
-  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
-  void* ptr = (void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
-  return __builtin_amdgcn_make_buffer_rsrc(ptr, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), kRsrcFlags);
-}
-
-// One 16-byte-per-lane buffer load into LDS at (m0 + 16 * lane).  Issued as
-// inline assembly on purpose: the compiler cannot prove that a DMA into one
-// ring stage does not alias the ds_reads of another, and for the builtin it
-// inserts "s_waitcnt vmcnt(0)" before those reads, which drains the whole
-// prefetch ring every step.  Ordering is kept by explicit per-wave vmcnt
-// waits instead.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, unsigned voff, const uint8_t* lds_dst) {
-  const unsigned m0 = __builtin_amdgcn_readfirstlane(
-      (unsigned)(size_t)(__attribute__((address_space(3))) const uint8_t*)lds_dst);
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs),
-               "s"(m0)
-               : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-// s_waitcnt with vmcnt = N (N <= 63), other counters untouched.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N <= 63, "vmcnt is 6 bits");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-// Workgroup barrier without a memory fence.  __syncthreads() also waits for
-// every outstanding vector-memory operation, which would drain the DMA ring
-// and the C stores; here each wave has already waited for the DMA it needs,
-// and every LDS read of a stage is consumed by an MFMA before the wave
-// reaches the next barrier.
-__device__ __forceinline__ void barrier() { __builtin_amdgcn_s_barrier(); }
 
 // --- fragments -----------------------------------------------------------------
 
@@ -229,42 +121,6 @@ __device__ __forceinline__ unsigned fix_tail(unsigned d, int g, int Kb) {
   if (valid >= 4) return d;
   const unsigned keep = valid <= 0 ? 0u : (1u << (8 * valid)) - 1u;
   return (d & keep) | (0x7F7F7F7Fu & ~keep);
-}
-
-// E8M0 byte -> the fp32 2^(b-127) used by the scaled conversions (byte 0 is
-// the fp32 denormal 2^-127, byte 255 is NaN).
-__device__ __forceinline__ float e8m0_to_f32(unsigned b) {
-  const unsigned bits = b == 0u ? 0x00400000u : (b == 255u ? 0x7FC00000u : (b << 23));
-  return __uint_as_float(bits);
-}
-
-template <int OPSEL, int FA, int FB>
-__device__ __forceinline__ v16f mfma_f8(const v8i& b, const v8i& a, const v16f& c, unsigned sb, unsigned sa) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, FB, FA, OPSEL, (int)sb, OPSEL, (int)sa);
-}
-
-// Two FP8 codes (bytes 0,1 or 2,3 of `w`) -> two bf16 times `scale`, as one
-// dword (the pair is bit-cast whole; element-wise extraction of the v2bf16
-// result was seen to duplicate the low half).
-template <int FMT, bool HI>
-__device__ __forceinline__ unsigned cvt2(unsigned w, float scale) {
-  v2bf r;
-  if constexpr (FMT == 0)
-    r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, scale, HI);
-  else
-    r = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, scale, HI);
-  return __builtin_bit_cast(unsigned, r);
-}
-
-// 8 codes (two dwords) -> one bf16 MFMA operand.
-template <int FMT>
-__device__ __forceinline__ v8bf cvt8(unsigned w0, unsigned w1, float scale) {
-  v4u u;
-  u[0] = cvt2<FMT, false>(w0, scale);
-  u[1] = cvt2<FMT, true>(w0, scale);
-  u[2] = cvt2<FMT, false>(w1, scale);
-  u[3] = cvt2<FMT, true>(w1, scale);
-  return __builtin_bit_cast(v8bf, u);
 }
 
 // One 64-K slice S (0 or 1) of a 128-K step for one wave.  `sfa`/`sfb` hold
@@ -384,11 +240,10 @@ __global__ __launch_bounds__(kThreads, 2) void mxgemm_amax_kernel(Params p) {
 
   unsigned lmax = 0u;
 
-  const int64_t G = gridDim.x;
-  int64_t t0 = blockIdx.x;
-  if (p.xcd_remap) t0 = (int64_t)(blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
-  const int64_t my_tiles = t0 < p.num_tiles ? (p.num_tiles - 1 - t0) / G + 1 : 0;
-  const int64_t total = my_tiles * p.ksteps;
+  const int G = (int)gridDim.x;
+  const int t0 = first_tile(p);
+  const int my_tiles = t0 < p.num_tiles ? (p.num_tiles - 1 - t0) / G + 1 : 0;
+  const int total = my_tiles * p.ksteps;
 
   // queue the DMA of step kt of tile T into stage `st` (exactly kOps
   // instructions per wave)
@@ -489,21 +344,21 @@ __global__ __launch_bounds__(kThreads, 2) void mxgemm_amax_kernel(Params p) {
   };
 
   Tile cur = {0, 0, 0, 0, 0}, nxt = {0, 0, 0, 0, 0}, prv = {0, 0, 0, 0, 0};
-  int64_t tcur = t0;
+  int tcur = t0;
   int kt = 0;
   bool have_prev = false;      // `prev` holds a tile whose stores are not all issued
   int stores_done = 0;         // store batches of `prev` issued so far
   int after_dma = 0;           // store instructions issued after the last DMA
 
   if (total > 0) {
-    cur = make_tile(p, tcur);
+    cur = make_tile<kBM, kBN>(p, tcur);
     issue_step(cur, 0, lds);
   } else if (p.ksteps == 0) {
     // K == 0: every C of this workgroup is an empty sum
-    for (int64_t i = 0; i < my_tiles; ++i) store_rest(make_tile(p, t0 + i * G), 0);
+    for (int i = 0; i < my_tiles; ++i) store_rest(make_tile<kBM, kBN>(p, t0 + i * G), 0);
   }
 
-  for (int64_t s = 0; s < total; ++s) {
+  for (int s = 0; s < total; ++s) {
     // step s's DMA has landed for this wave (only store instructions may
     // have been issued after it); the barrier makes that true for all waves
     // and frees the other stage, read during step s-1
@@ -519,7 +374,7 @@ __global__ __launch_bounds__(kThreads, 2) void mxgemm_amax_kernel(Params p) {
       if (kt + 1 < p.ksteps) {
         issue_step(cur, kt + 1, lds + (int)((s + 1) & 1) * kStage);
       } else {
-        nxt = make_tile(p, tcur + G);
+        nxt = make_tile<kBM, kBN>(p, tcur + G);
         issue_step(nxt, 0, lds + (int)((s + 1) & 1) * kStage);
       }
     }
@@ -585,10 +440,6 @@ __global__ __launch_bounds__(kThreads, 2) void mxgemm_amax_kernel(Params p) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) lmax = max(lmax, (unsigned)__shfl_xor((int)lmax, off));
   if (lane == 0 && lmax != 0u) atomicMax(p.amax_bits, lmax);
-}
-
-__global__ void amax_reset_kernel(unsigned* amax_bits) {
-  if (threadIdx.x == 0) *amax_bits = 0u;
 }
 
 }  // namespace mxg

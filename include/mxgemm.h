@@ -91,7 +91,13 @@ enum {
      the result can miss a 1e-5 * sum|A_hat*B_hat| error bound on
      heavy-tailed data.  The default path dequantises each element exactly
      to bf16 (scale folded in) and accumulates in fp32 on the bf16 MFMA. */
-  MXG_FLAG_FP8_MFMA = 2u
+  MXG_FLAG_FP8_MFMA = 2u,
+  /* Force the tile configuration instead of the automatic choice (for tests
+     and tuning; results agree within the tolerance either way).  TILE_128:
+     128x128 tiles, two workgroups per CU.  TILE_256: 256x256 tiles, one
+     workgroup per CU (ignored when K == 0).  Setting both is an error. */
+  MXG_FLAG_TILE_128 = 4u,
+  MXG_FLAG_TILE_256 = 8u
 };
 
 /*
@@ -123,7 +129,9 @@ int mxgemm_amax(const void* A, const void* B, const uint8_t* SFA, const uint8_t*
  * mxgemm_amax_ex -- mxgemm_amax with flags.  flags == 0 is exactly
  * mxgemm_amax; MXG_FLAG_AMAX_ACCUMULATE skips the clearing kernel and
  * max-reduces into the existing Amax (queues the GEMM kernel only);
- * MXG_FLAG_FP8_MFMA selects the reduced-precision FP8 matrix path.
+ * MXG_FLAG_FP8_MFMA selects the reduced-precision FP8 matrix path;
+ * MXG_FLAG_TILE_128 / MXG_FLAG_TILE_256 force a tile configuration.
+ * Returns MXG_ERR_FLAGS for unknown bits or both tile flags.
  *
  * Exactness of the default path: every dequantised element is exact when
  * its scale byte lies in 3..246 (E4M3) or 10..239 (E5M2), i.e. when the

@@ -20,11 +20,15 @@ pytestmark = pytest.mark.gpu
 
 E4, E5 = W.FMT_E4M3, W.FMT_E5M2
 
+# tile configuration flags of mxgemm_amax_ex (0 = the library's own choice)
+TILES = {"auto": 0, "t128": 4, "t256": 8}
+
 
 @pytest.fixture(scope="module")
 def lib():
     import block_scaled_precision_e4m3_amd as lib
     assert torch.cuda.is_available(), "GPU tests need a GPU"
+    assert (lib.MXG_FLAG_TILE_128, lib.MXG_FLAG_TILE_256) == (TILES["t128"], TILES["t256"])
     return lib
 
 
@@ -46,14 +50,15 @@ SMALL = [
 ]
 
 
+@pytest.mark.parametrize("tile", list(TILES))
 @pytest.mark.parametrize("dist", ["normal", "student_t3"])
 @pytest.mark.parametrize("M,N,K,L,sf,fa,fb", SMALL)
-def test_small_shapes_full_oracle(lib, M, N, K, L, sf, fa, fb, dist):
-    print(f"case M={M} N={N} K={K} L={L} sf={sf} fmt={fa}{fb} {dist} "
-          f"tiles={lib.mxgemm_launch_config(M, N, K, L, sf)}", flush=True)
+def test_small_shapes_full_oracle(lib, M, N, K, L, sf, fa, fb, dist, tile):
+    print(f"case M={M} N={N} K={K} L={L} sf={sf} fmt={fa}{fb} {dist} tile={tile} "
+          f"auto={lib.mxgemm_launch_config(M, N, K, L, sf)}", flush=True)
     p = W.make_problem(M, N, K, L, sf, fa, fb, seed=M + N + K, dist=dist)
     d = to_device(p)
-    run(lib, p, d)
+    run(lib, p, d, flags=TILES[tile])
     c, amax = fetch(p, d)
     c_ref, s_ref, amax_ref = _oracle_full(p)
     ratio = check_c(c, c_ref, s_ref, f"{M}x{N}x{K}x{L}")
@@ -69,13 +74,14 @@ def test_small_shapes_full_oracle(lib, M, N, K, L, sf, fa, fb, dist):
 FP8_MFMA_REL = 2.0 ** -10
 
 
+@pytest.mark.parametrize("tile", ["t128", "t256"])
 @pytest.mark.parametrize("dist", ["normal", "student_t3"])
 @pytest.mark.parametrize("M,N,K,L,sf,fa,fb", SMALL[:6])
-def test_fp8_mfma_mode_within_model_bound(lib, M, N, K, L, sf, fa, fb, dist):
-    print(f"fp8-mfma case M={M} N={N} K={K} L={L} sf={sf} fmt={fa}{fb} {dist}", flush=True)
+def test_fp8_mfma_mode_within_model_bound(lib, M, N, K, L, sf, fa, fb, dist, tile):
+    print(f"fp8-mfma case M={M} N={N} K={K} L={L} sf={sf} fmt={fa}{fb} {dist} tile={tile}", flush=True)
     p = W.make_problem(M, N, K, L, sf, fa, fb, seed=M + N + K, dist=dist)
     d = to_device(p)
-    run(lib, p, d, flags=lib.MXG_FLAG_FP8_MFMA)
+    run(lib, p, d, flags=lib.MXG_FLAG_FP8_MFMA | TILES[tile])
     c, amax = fetch(p, d)
     c_ref, s_ref, amax_ref = _oracle_full(p)
     err = np.abs(c.astype(np.float64) - c_ref)
@@ -135,29 +141,31 @@ def test_workload_sampled(lib, wid):
     print(f"  max |diff|/bound = {worst:.3g}", flush=True)
 
 
-def test_scale_plus_one_doubles_bitwise(lib):
+@pytest.mark.parametrize("tile", ["t128", "t256"])
+def test_scale_plus_one_doubles_bitwise(lib, tile):
     p = W.make_problem(520, 264, 384, 2, 32, E4, E5, seed=11)
     d = to_device(p)
-    run(lib, p, d)
+    run(lib, p, d, flags=TILES[tile])
     c0, a0 = fetch(p, d)
     d["SFA"] += 1          # every scale byte +1: 2x every product (bytes stay < 255 here)
-    run(lib, p, d)
+    run(lib, p, d, flags=TILES[tile])
     c1, a1 = fetch(p, d)
     assert np.array_equal(c1, 2 * c0)
     assert a1 == 2 * a0
 
 
-def test_sign_flip_negates(lib):
+@pytest.mark.parametrize("tile", ["t128", "t256"])
+def test_sign_flip_negates(lib, tile):
     # Flipping every A sign bit negates C.  The bf16 MFMA truncates its
     # 16-product partial sums toward zero before the round-to-nearest add into
     # the accumulator, so the negation is checked to the tolerance rather than
     # bitwise; the count of bitwise differences is reported.
     p = W.make_problem(300, 200, 256, 1, 16, E5, E4, seed=12)
     d = to_device(p)
-    run(lib, p, d)
+    run(lib, p, d, flags=TILES[tile])
     c0, a0 = fetch(p, d)
     d["A"] ^= 0x80
-    run(lib, p, d)
+    run(lib, p, d, flags=TILES[tile])
     c1, a1 = fetch(p, d)
     _, s_ref, _ = _oracle_full(p)
     assert np.all(np.abs(c1.astype(np.float64) + c0) <= 2e-5 * s_ref)
@@ -165,13 +173,14 @@ def test_sign_flip_negates(lib):
     print(f"  bitwise-different entries: {int(np.sum(c1 != -c0))} of {c0.size}", flush=True)
 
 
-def test_deterministic_and_padding_poison(lib):
+@pytest.mark.parametrize("tile", ["t128", "t256"])
+def test_deterministic_and_padding_poison(lib, tile):
     # padding SF bytes set to 0xFF (NaN scale) must never reach the result
     p = W.make_problem(200, 196, 592, 2, 32, E4, E4, seed=13, pad_byte=0xFF)
     d = to_device(p)
-    run(lib, p, d)
+    run(lib, p, d, flags=TILES[tile])
     c0, a0 = fetch(p, d)
-    run(lib, p, d)
+    run(lib, p, d, flags=TILES[tile])
     c1, a1 = fetch(p, d)
     assert np.array_equal(c0.view(np.uint32), c1.view(np.uint32)) and a0 == a1
     c_ref, s_ref, amax_ref = _oracle_full(p)
@@ -179,11 +188,12 @@ def test_deterministic_and_padding_poison(lib):
     check_amax(a0, amax_ref)
 
 
-def test_guard_band_untouched(lib):
+@pytest.mark.parametrize("tile", ["t128", "t256"])
+def test_guard_band_untouched(lib, tile):
     p = W.make_problem(130, 68, 160, 2, 16, E4, E4, seed=14)
     pad = 1024
     d = to_device(p, pad_c=pad, c_fill=12345.0)
-    run(lib, p, d)
+    run(lib, p, d, flags=TILES[tile])
     torch.cuda.synchronize()
     full = d["C_full"].cpu().numpy()
     assert np.all(full[:pad] == 12345.0) and np.all(full[-pad:] == 12345.0)
@@ -243,3 +253,29 @@ def test_high_level_wrapper_logical_sf(lib):
     c_ref, s_ref, amax_ref = _oracle_full(p)
     check_c(c.permute(2, 0, 1).cpu().numpy(), c_ref, s_ref, "wrapper")
     check_amax(amax.item(), amax_ref)
+
+
+@pytest.mark.parametrize("tile", ["t128", "t256"])
+@pytest.mark.parametrize("sf", [32, 16])
+def test_special_scale_bytes(lib, sf, tile):
+    # E8M0 0xFF is NaN: every element of its block dequantises to NaN, so the
+    # row's C is NaN and so is Amax.  E8M0 0x00 is 2^-127: its block's products
+    # vanish below the absolute tolerance.  The bytes are set through the
+    # oracle's logical view of the atoms.
+    from oracle.sf_atom import sf_logical_view
+    M, N, K, L = 300, 264, 384, 1
+    p = W.make_problem(M, N, K, L, sf, E4, E4, seed=18)
+    lva = sf_logical_view(p["SFA"], M, K, L, sf)
+    nan_row, zero_row = 133, 7
+    for m, kb, byte in ((nan_row, 5, 255), (zero_row, 2, 0), (zero_row, 3, 0)):
+        lva[m % 32, (m // 32) % 4, m // 128, kb % 4, kb // 4, 0] = byte
+    d = to_device(p)
+    run(lib, p, d, flags=TILES[tile])
+    c, amax = fetch(p, d)
+    c_ref, s_ref, amax_ref = _oracle_full(p)
+    assert np.isnan(c_ref[0, nan_row]).all() and np.isnan(amax_ref)
+    nan_gpu = np.isnan(c)
+    assert np.array_equal(nan_gpu, np.isnan(c_ref)), f"NaN rows differ: {np.argwhere(nan_gpu != np.isnan(c_ref))[:5]}"
+    assert np.isnan(amax)
+    keep = ~np.isnan(c_ref)
+    check_c(c[keep], c_ref[keep], s_ref[keep], "special scale bytes")
