@@ -84,14 +84,18 @@ bool on_device(const void* p, int dev) {
   return attr.device == dev;
 }
 
-// Two tile shapes.  Small: 128x128 per workgroup, two workgroups per CU,
-// 4 waves of 64x64.  Big: 256x256 per workgroup, one per CU, 4 waves of
-// 128x128; half the L2->LDS bytes per flop, used when its tiles fill the
-// chip at least as evenly as the small ones do.
+// Three tile shapes.  128x128: two workgroups per CU, 4 waves of 64x64.
+// 256x256: one workgroup per CU, 4 waves of 128x128; half the L2->LDS bytes
+// per flop of 128x128, but a tile's C is stored in one burst at its end.
+// 256x128: one workgroup per CU, 4 waves of 128x64; its C stores are spread
+// over the next tile.  The automatic choice takes 256x128 when its tiles fill
+// the CUs at least as evenly as 128x128 tiles fill two workgroups per CU (and
+// K > 0), otherwise 128x128.
 struct Config {
-  bool big;
+  int kind;  // 0: 128x128, 1: 256x256, 2: 256x128
   int tile_m, tile_n, per_cu;
 };
+constexpr Config kSmall = {0, 128, 128, 2}, kBig = {1, 256, 256, 1}, kMid = {2, 256, 128, 1};
 
 double fill(int64_t tiles, int64_t slots) {
   if (tiles <= 0) return 0.0;
@@ -101,18 +105,20 @@ double fill(int64_t tiles, int64_t slots) {
 
 Config choose(int64_t M, int64_t N, int64_t K, int64_t L, int cus) {
   const int64_t small = L * cdiv(M, 128) * cdiv(N, 128);
-  const int64_t big = L * cdiv(M, 256) * cdiv(N, 256);
-  if (K > 0 && big >= cus && fill(big, cus) >= fill(small, 2 * (int64_t)cus) - 1e-9) return {true, 256, 256, 1};
-  return {false, 128, 128, 2};
+  const int64_t mid = L * cdiv(M, 256) * cdiv(N, 128);
+  if (K > 0 && mid >= cus && fill(mid, cus) >= fill(small, 2 * (int64_t)cus) - 1e-9) return kMid;
+  return kSmall;
 }
 
-template <int MODE, bool BIG>
+template <int MODE, int KIND>
 hipError_t launch_mode(const mxg::Params& p, int sf, int fa, int fb, int64_t grid, hipStream_t s) {
-  const dim3 g((unsigned)grid), b(BIG ? mxg::big::kThreads : mxg::kThreads);
+  const dim3 g((unsigned)grid), b(KIND ? mxg::big::kThreads : mxg::kThreads);
 #define MXG_LAUNCH(SF, FA, FB)                                                                         \
   do {                                                                                                 \
-    if constexpr (BIG)                                                                                 \
-      hipLaunchKernelGGL((mxg::big::mxgemm_amax_big_kernel<SF, FA, FB, MODE>), g, b, 0, s, p);         \
+    if constexpr (KIND == 1)                                                                           \
+      hipLaunchKernelGGL((mxg::big::mxgemm_amax_big_kernel<SF, FA, FB, MODE, 256>), g, b, 0, s, p);    \
+    else if constexpr (KIND == 2)                                                                      \
+      hipLaunchKernelGGL((mxg::big::mxgemm_amax_big_kernel<SF, FA, FB, MODE, 128>), g, b, 0, s, p);    \
     else                                                                                               \
       hipLaunchKernelGGL((mxg::mxgemm_amax_kernel<SF, FA, FB, MODE>), g, b, 0, s, p);                  \
   } while (0)
@@ -187,9 +193,11 @@ int mxgemm_amax_ex(const void* A, const void* B, const uint8_t* SFA, const uint8
                    unsigned flags, void* stream) {
   int st = check_sizes(M, N, K, L, sf_vec_size, a_fmt, b_fmt);
   if (st != MXG_OK) return st;
-  if (flags & ~(unsigned)(MXG_FLAG_AMAX_ACCUMULATE | MXG_FLAG_FP8_MFMA | MXG_FLAG_TILE_128 | MXG_FLAG_TILE_256))
+  const unsigned tile_flags = flags & (MXG_FLAG_TILE_128 | MXG_FLAG_TILE_256 | MXG_FLAG_TILE_256X128);
+  if (flags & ~(unsigned)(MXG_FLAG_AMAX_ACCUMULATE | MXG_FLAG_FP8_MFMA | MXG_FLAG_TILE_128 | MXG_FLAG_TILE_256 |
+                          MXG_FLAG_TILE_256X128))
     return MXG_ERR_FLAGS;
-  if ((flags & MXG_FLAG_TILE_128) && (flags & MXG_FLAG_TILE_256)) return MXG_ERR_FLAGS;
+  if (tile_flags & (tile_flags - 1)) return MXG_ERR_FLAGS;  // more than one tile flag
   // A, B and the scales are read only when there is a non-empty C and a non-empty K
   const bool need_c = M > 0 && N > 0 && L > 0;
   const bool need_a = need_c && K > 0, need_b = need_a;
@@ -228,8 +236,9 @@ int mxgemm_amax_ex(const void* A, const void* B, const uint8_t* SFA, const uint8
   p.MNbA = (int)cdiv(M, 128);
   p.MNbB = (int)cdiv(N, 128);
   Config cfg = choose(M, N, K, L, cus);
-  if (flags & MXG_FLAG_TILE_128) cfg = {false, 128, 128, 2};
-  if ((flags & MXG_FLAG_TILE_256) && K > 0) cfg = {true, 256, 256, 1};
+  if (flags & MXG_FLAG_TILE_128) cfg = kSmall;
+  if ((flags & MXG_FLAG_TILE_256) && K > 0) cfg = kBig;
+  if ((flags & MXG_FLAG_TILE_256X128) && K > 0) cfg = kMid;
   p.tilesM = (int)cdiv(M, cfg.tile_m);
   p.tilesN = (int)cdiv(N, cfg.tile_n);
   p.ksteps = (int)cdiv(K, 128);
@@ -239,12 +248,15 @@ int mxgemm_amax_ex(const void* A, const void* B, const uint8_t* SFA, const uint8
 
   const bool fp8 = (flags & MXG_FLAG_FP8_MFMA) != 0;
   hipError_t e;
-  if (cfg.big)
-    e = fp8 ? launch_mode<mxg::kModeFp8, true>(p, sf_vec_size, a_fmt, b_fmt, grid, s)
-            : launch_mode<mxg::kModeBf16, true>(p, sf_vec_size, a_fmt, b_fmt, grid, s);
+  if (cfg.kind == 1)
+    e = fp8 ? launch_mode<mxg::kModeFp8, 1>(p, sf_vec_size, a_fmt, b_fmt, grid, s)
+            : launch_mode<mxg::kModeBf16, 1>(p, sf_vec_size, a_fmt, b_fmt, grid, s);
+  else if (cfg.kind == 2)
+    e = fp8 ? launch_mode<mxg::kModeFp8, 2>(p, sf_vec_size, a_fmt, b_fmt, grid, s)
+            : launch_mode<mxg::kModeBf16, 2>(p, sf_vec_size, a_fmt, b_fmt, grid, s);
   else
-    e = fp8 ? launch_mode<mxg::kModeFp8, false>(p, sf_vec_size, a_fmt, b_fmt, grid, s)
-            : launch_mode<mxg::kModeBf16, false>(p, sf_vec_size, a_fmt, b_fmt, grid, s);
+    e = fp8 ? launch_mode<mxg::kModeFp8, 0>(p, sf_vec_size, a_fmt, b_fmt, grid, s)
+            : launch_mode<mxg::kModeBf16, 0>(p, sf_vec_size, a_fmt, b_fmt, grid, s);
   return e == hipSuccess ? MXG_OK : MXG_ERR_LAUNCH;
 }
 

@@ -1,25 +1,30 @@
-// Large-tile variant of the block-scaled FP8 GEMM + amax kernel for gfx950.
+// One-workgroup-per-CU variants of the block-scaled FP8 GEMM + amax kernel
+// for gfx950: 256x256 and 256x128 C tiles.
 //
 // Same operation, operand layouts, scale handling and amax as the 128x128
 // kernel in mxgemm_kernel.hpp ("GEMM + Amax (SM100)", sections "Equations"
 // and "Shapes"); what changes is the shape of the work:
 //
-// * One workgroup per CU (the LDS ring takes 132-136 KB of the 160 KB) owns a
-//   256x256 C tile; its 4 waves, one per SIMD, each hold a 128x128 block in
-//   4x4 MFMA accumulators (256 registers).  Per 128-K step a CU then moves
-//   66-68 KB from L2 for 8.4 M multiply-adds, half the bytes per flop of two
-//   128x128 workgroups, and each converted fragment feeds 4 MFMAs instead of 2.
-// * The K loop is one straight block per step: the step's 16-17 DMA
-//   instructions for the next stage are spread between its MFMAs (4 after each
-//   32-K chunk's fragment reads), so the memory pipe sees a steady stream
-//   instead of a burst, and the single wave per SIMD keeps the matrix core fed
-//   by issuing conversions, LDS reads and DMA in the shadow of its MFMAs.
-// * A tile's C is stored at its end straight from the accumulators (64
-//   16-byte stores per lane), then the next tile starts; the stores drain
-//   under the next tile's first step.
+// * One workgroup per CU (the LDS ring takes up to 136 KB of the 160 KB) owns
+//   a 256 x BN tile; its 4 waves, one per SIMD, each hold a 128 x BN/2 block in
+//   4 x BN/64 MFMA accumulators.  Per 128-K step a CU moves 32 KB of A,
+//   BN*128 bytes of B and the scale atoms from L2.
+// * The K loop is one straight block per step: the next stage's DMA
+//   instructions go out a few at a time between the 32-K chunks' MFMAs, the
+//   next chunk's fragment reads are queued ahead, and each slice's conversions
+//   run under the previous slice's MFMAs (scheduling-group barriers pin the
+//   interleave), so one wave per SIMD keeps the matrix core fed.
+// * C stores.  BN = 256: the 256 accumulators of a wave take all the matrix-
+//   core registers, so a tile's C is stored at its end.  Every CU ends its
+//   tiles at the same time, so these stores arrive as bursts that are bound
+//   by HBM write bandwidth.  BN = 128: the 128 accumulators are copied to a
+//   second set at tile end and their 32 stores per lane go out 4 per step
+//   during the next tile, after the step's DMA, spreading the C traffic over
+//   the whole run (the vector-memory counter retires in issue order, so a
+//   wave waiting for its next DMA never waits for stores queued after it).
 //
 // bf16 datapath, per 32-K chunk c of a step: lane (r, h) reads the 16 bytes
-// K [32c + 16h, +16) of its row for each of its 4 A and 4 B fragments; bytes
+// K [32c + 16h, +16) of its row for each of its A and B fragments; bytes
 // 0..7 feed MFMA slice 0 and bytes 8..15 slice 1 (any K assignment is valid
 // when A and B share it, since the scale is folded into every element).  The
 // chunk lies in one K-block for sf=32 (block c) and for sf=16 (block 2c + h).
@@ -33,18 +38,20 @@ namespace mxg {
 namespace big {
 
 constexpr int kThreads = 256;
-constexpr int kBM = 256, kBN = 256, kBK = 128;
-constexpr int kTM = 4, kTN = 4;  // 32x32 MFMA blocks per wave: a 128x128 wave tile
-constexpr int kNStores = kTM * kTN * 4;
+constexpr int kBM = 256, kBK = 128;
+constexpr int kTM = 4;  // 32-row MFMA blocks per wave (128 rows)
 
-template <int SF>
+template <int SF, int BN>
 struct Layout {
-  static constexpr int NSF = SF == 32 ? 1 : 2;      // atoms per 128-row group per step
-  static constexpr int kSF = 2 * NSF * 512;         // atom bytes per operand per stage
-  static constexpr int kOffB = kBM * kBK;           // A tile: 256 rows x 128 bytes
-  static constexpr int kOffSFA = kOffB + kBN * kBK;  // B tile
+  static constexpr int NSF = SF == 32 ? 1 : 2;       // atoms per 128-row group per step
+  static constexpr int kSF = 2 * NSF * 512;          // atom bytes per operand per stage
+  static constexpr int kOffB = kBM * kBK;            // A tile: 256 rows x 128 bytes
+  static constexpr int kOffSFA = kOffB + BN * kBK;   // B tile: BN rows x 128 bytes
   static constexpr int kOffSFB = kOffSFA + kSF;
-  static constexpr int kStage = kOffSFB + kSF;       // 66 KB (sf=32) or 68 KB (sf=16)
+  static constexpr int kStage = kOffSFB + kSF;
+  static constexpr int kTN = BN / 64;                // 32-column MFMA blocks per wave
+  static constexpr int kDma = (kBM + BN) / 32;       // A/B DMA instructions per wave per step
+  static constexpr bool kTrickle = BN == 128;        // C stores spread over the next tile
 };
 
 __device__ __forceinline__ uint4 lds16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
@@ -58,10 +65,12 @@ __device__ __forceinline__ unsigned sf_tail(unsigned d, int g, int Kb) {
   return (d & keep) | (0x7F7F7F7Fu & ~keep);
 }
 
-template <int SF, int FA, int FB, int MODE>
+template <int SF, int FA, int FB, int MODE, int BN>
 __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) {
-  using Y = Layout<SF>;
+  using Y = Layout<SF, BN>;
   constexpr int NSF = Y::NSF;
+  constexpr int kTN = Y::kTN;
+  constexpr int kWN = BN / 2;  // wave tile columns
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * Y::kStage];
 
   const int lane = threadIdx.x & 63;
@@ -71,7 +80,6 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   const int G = (int)gridDim.x;
   const int t0 = first_tile(p);
   const int my_tiles = t0 < p.num_tiles ? (p.num_tiles - 1 - t0) / G + 1 : 0;
-  const int total = my_tiles * p.ksteps;
   const unsigned lds0 = lds_addr(lds);
 
   // Per-lane geometry.  It is recomputed every step from an opaque copy of the
@@ -93,7 +101,7 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
     g.h = ln >> 5;
     g.xr = ln & 7;
     g.a_off = (128 * wm + g.r) * kBK;
-    g.b_off = Y::kOffB + (128 * wn + g.r) * kBK;
+    g.b_off = Y::kOffB + (kWN * wn + g.r) * kBK;
     const int dma_row = ln >> 3;
     g.row_k = (unsigned)(wave * 8 + dma_row) * (unsigned)p.K;
     g.kchunk = (unsigned)(((ln & 7) ^ dma_row) << 4);
@@ -109,14 +117,15 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   };
 
   // --- DMA of one stage ------------------------------------------------------
-  // A/B: wave w fills the 8-row groups w, w+4, ..., w+28 of each tile, one
-  // instruction (1 KB) per group.  A lane's offset is row*K + k; rows past the
-  // tile's valid rows fall past the resource (num_records = valid rows * K)
-  // and K chunks past K get an offset of 2^31 or more: both read as zero.
-  // A and B rows use the same offsets, only the resources differ.
-  // SF: sf=32 -> waves 0 and 1 load the A and B atoms of both 128-row groups
-  // (lanes 0-31 group 0, 32-63 group 1); sf=16 -> waves 0,1 (A,B) load row
-  // group 0's two atoms, waves 2,3 row group 1's.
+  // A/B: wave w fills the 8-row groups w, w+4, ... of each tile, one
+  // instruction (1 KB) per group: 8 for A, BN/32 for B.  A lane's offset is
+  // row*K + k; rows past the tile's valid rows fall past the resource
+  // (num_records = valid rows * K) and K chunks past K get an offset of 2^31
+  // or more: both read as zero.  A and B rows use the same offsets, only the
+  // resources differ.  SF: sf=32 -> waves 0 and 1 load the A and B atoms of
+  // both 128-row groups (lanes 0-31 group 0, 32-63 group 1); sf=16 -> waves
+  // 0,1 (A,B) load row group 0's two atoms, waves 2,3 row group 1's.  Groups
+  // past the tile (B with BN = 128) or past the matrix read as zero.
   constexpr unsigned kOob = 0x80000000u;
   const bool sf_wave = NSF == 2 || wave < 2;
   const bool sf_is_b = (wave & 1) != 0;
@@ -135,18 +144,21 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
     const int mn0 = sf_is_b ? T.n0 : T.m0;
     const int mnb = sf_is_b ? p.MNbB : p.MNbA;
     const int g0 = mn0 >> 7;
-    const unsigned nrec = live ? (unsigned)min(2, mnb - g0) * (unsigned)p.Kg * 512u : 0u;
+    const int tile_groups = sf_is_b ? BN / 128 : 2;
+    const unsigned nrec = live ? (unsigned)min(tile_groups, mnb - g0) * (unsigned)p.Kg * 512u : 0u;
     d.rs = make_rsrc((sf_is_b ? p.SFB : p.SFA) + ((int64_t)T.l * mnb + g0) * p.Kg * 512, nrec);
     const int kg = NSF * kt + g.sf_j;
     d.sf_voff = kg < p.Kg ? (unsigned)(g.sf_rg * p.Kg + kg) * 512u + g.sf_lane : kOob;
     d.dst = stage;
     return d;
   };
-  // A/B DMA instruction q (0..15) of this wave: q < 8 -> A group wave + 4q
+  // A/B DMA instruction q of this wave: q < 8 -> A group wave + 4q, else B
+  // group wave + 4(q - 8)
   const unsigned grp_stride = 32u * (unsigned)p.K;
   auto dma_ab = [&](const Dma& d, int q) {
-    const unsigned voff = d.voff + (unsigned)(q & 7) * grp_stride;
-    const unsigned dst = d.dst + (q >= 8 ? (unsigned)Y::kOffB : 0u) + (unsigned)(wave + 4 * (q & 7)) * 1024u;
+    const int qq = q < 8 ? q : q - 8;
+    const unsigned voff = d.voff + (unsigned)qq * grp_stride;
+    const unsigned dst = d.dst + (q >= 8 ? (unsigned)Y::kOffB : 0u) + (unsigned)(wave + 4 * qq) * 1024u;
     dma16_at(q >= 8 ? d.rb : d.ra, voff, dst);
   };
   auto dma_sf = [&](const Dma& d) {
@@ -156,19 +168,99 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
                    (NSF == 1 ? 0u : (unsigned)(wave >> 1) * 1024u));
   };
 
-  v16f acc[kTM][kTN];  // written by each tile's first step before any read
+  v16f acc[kTM][kTN];   // written by each tile's first step before any read
+  v16f prev[kTM][kTN];  // BN = 128: the previous tile, stored during this one
   const v16f zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   unsigned lmax = 0u;
 
+  // --- C stores -----------------------------------------------------------------
+  // Lane (r, h) of block (i, j) holds C row 128*wm + 32i + r and, for q =
+  // 0..3, the 4 columns kWN*wn + 32j + 8q + 4h + (0..3).  Rows past the tile's
+  // valid rows land past the resource (num_records = valid rows * N * 4);
+  // columns past N get an offset past it as well.  Every store folds its
+  // values into the lane's amax.
+  struct StoreCtx {
+    __amdgpu_buffer_rsrc_t rc;
+    unsigned c_bytes, vbase;
+    int mrow, ncol, mvalid, nvalid;
+  };
+  auto store_ctx = [&](const Tile& T) {
+    StoreCtx x;
+    const int ln = lane_opaque();
+    x.c_bytes = (unsigned)T.mvalid * (unsigned)p.N * 4u;
+    x.rc = make_rsrc(p.C + ((int64_t)T.l * p.M + T.m0) * p.N, x.c_bytes);
+    x.mrow = 128 * wm + (ln & 31);
+    x.ncol = kWN * wn + 4 * (ln >> 5);
+    x.vbase = ((unsigned)x.mrow * (unsigned)p.N + (unsigned)(T.n0 + x.ncol)) * 4u;
+    x.mvalid = T.mvalid;
+    x.nvalid = T.nvalid;
+    return x;
+  };
+  auto store4 = [&](const StoreCtx& x, const v16f& blk, int i, int j, int q) {
+    const bool ok = (x.mrow + 32 * i < x.mvalid) & (x.ncol + 32 * j + 8 * q < x.nvalid);
+    v4f v;
+    v[0] = blk[4 * q];
+    v[1] = blk[4 * q + 1];
+    v[2] = blk[4 * q + 2];
+    v[3] = blk[4 * q + 3];
+    const unsigned off = x.vbase + (unsigned)(32 * i) * (unsigned)p.N * 4u + (unsigned)((32 * j + 8 * q) * 4);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), x.rc, ok ? (int)off : (int)x.c_bytes, 0, 0);
+    const unsigned m4 = max(max(__float_as_uint(v[0]) & 0x7FFFFFFFu, __float_as_uint(v[1]) & 0x7FFFFFFFu),
+                            max(__float_as_uint(v[2]) & 0x7FFFFFFFu, __float_as_uint(v[3]) & 0x7FFFFFFFu));
+    lmax = max(lmax, m4 & (0u - (unsigned)ok));  // arithmetic mask: no branch
+  };
+  // BN = 256: every block of `acc` at tile end, one block at a time (each block
+  // is pinned in the accumulation registers until its turn, so its copies out
+  // are made block by block rather than all at once)
+  auto store_all = [&](const StoreCtx& x) {
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+      for (int j = 0; j < kTN; ++j) {
+        asm volatile("" : "+a"(acc[i][j])::"memory");
+#pragma unroll
+        for (int q = 0; q < 4; ++q) store4(x, acc[i][j], i, j, q);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  };
+  // BN = 128: batch b (4 stores) of `prev`; b is a compile-time constant so
+  // the registers are named statically
+  constexpr int kBatch = 4;
+  constexpr int kBatches = kTM * kTN * 4 / kBatch;
+  auto store_batch = [&](const StoreCtx& x, auto bc) {
+    constexpr int b = decltype(bc)::value;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int idx = b * kBatch + u;
+      const int i = idx / (kTN * 4), j = (idx / 4) % kTN, q = idx % 4;
+      store4(x, prev[i][j], i, j, q);
+    }
+  };
+  auto store_one = [&](const StoreCtx& x, int b) {
+    static_assert(!Y::kTrickle || kBatches == 8, "batch dispatch below is written for 8 batches");
+    switch (b) {
+      case 0: store_batch(x, std::integral_constant<int, 0>{}); break;
+      case 1: store_batch(x, std::integral_constant<int, 1>{}); break;
+      case 2: store_batch(x, std::integral_constant<int, 2>{}); break;
+      case 3: store_batch(x, std::integral_constant<int, 3>{}); break;
+      case 4: store_batch(x, std::integral_constant<int, 4>{}); break;
+      case 5: store_batch(x, std::integral_constant<int, 5>{}); break;
+      case 6: store_batch(x, std::integral_constant<int, 6>{}); break;
+      default: store_batch(x, std::integral_constant<int, 7>{}); break;
+    }
+  };
+
   Tile cur = {0, 0, 0, 0, 0};
-  bool stores_pending = false;
-  int s = 0;  // global step index: selects the ring stage
-  if (total > 0) {
-    cur = make_tile<kBM, kBN>(p, t0);
+  Tile ptile = {0, 0, 0, 0, 0};  // BN = 128: the tile held in `prev`
+  int pend = 0;                  // BN = 128: batches of `prev` not yet stored
+  int after_dma = 0;             // store instructions queued after the last DMA
+  int s = 0;                     // global step index: selects the ring stage
+  if (my_tiles > 0) {
+    cur = make_tile<kBM, BN>(p, t0);
     const Dma d0 = dma_setup(geo(lane), cur, 0, true, lds0);
     dma_sf(d0);
 #pragma unroll
-    for (int q = 0; q < 16; ++q) dma_ab(d0, q);
+    for (int q = 0; q < Y::kDma; ++q) dma_ab(d0, q);
   }
 
   // One K step of tile `cur`; queues the DMA of the next step (this tile's
@@ -178,11 +270,14 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   // matrix-core registers from tile to tile.
   auto step = [&](auto first, int kt, const Tile& nt, bool has_next) {
     constexpr bool kFirst = decltype(first)::value;
-    // this wave's DMA for step s is complete (stores queued after it may not
-    // be); the barrier extends that to every wave and frees the other stage
-    if (stores_pending) wait_vm<63>();
+    // this wave's DMA for step s is complete (only stores may have been
+    // queued after it); the barrier extends that to every wave and frees the
+    // other stage
+    if (after_dma == 0) wait_vm<0>();
+    else if (after_dma == kBatch) wait_vm<kBatch>();
+    else if (after_dma <= 63) wait_vm<63>();
     else wait_vm<0>();
-    stores_pending = false;
+    after_dma = 0;
     barrier();
     const Geo g = geo(lane_opaque());
     const uint8_t* st = lds + (s & 1) * Y::kStage;
@@ -193,8 +288,11 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
     const bool last_k = kt + 1 == p.ksteps;
     const Dma d = dma_setup(g, nt, last_k ? 0 : kt + 1, has_next, lds0 + (unsigned)(((s & 1) ^ 1) * Y::kStage));
     dma_sf(d);
-    // SF dwords of this step: NSF atoms x 4 fragment rows per operand
+    // SF dwords of this step: NSF atoms x (4 or kTN) fragment rows per operand.
+    // A rows 128*wm + 32i + r: atom group wm, dword i; B rows kWN*wn + 32i + r:
+    // atom group (kWN*wn)/128, dword ((kWN*wn)/32)%4 + i.
     unsigned sa[NSF][kTM], sb[NSF][kTN];
+    const int brg = (kWN * wn) >> 7, bdw = ((kWN * wn) >> 5) & 3;
 #pragma unroll
     for (int j = 0; j < NSF; ++j) {
       const int ga = NSF * kt + j;
@@ -203,59 +301,75 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
         sa[j][i] = sf_tail(lds4(st + Y::kOffSFA + (wm * NSF + j) * 512 + 16 * g.r + 4 * i), ga, p.Kb);
 #pragma unroll
       for (int i = 0; i < kTN; ++i)
-        sb[j][i] = sf_tail(lds4(st + Y::kOffSFB + (wn * NSF + j) * 512 + 16 * g.r + 4 * i), ga, p.Kb);
+        sb[j][i] = sf_tail(lds4(st + Y::kOffSFB + (brg * NSF + j) * 512 + 16 * g.r + 4 * (bdw + i)), ga, p.Kb);
     }
 
     if constexpr (MODE == kModeBf16) {
-      // software pipeline over the 4 chunks: chunk c+1's fragment reads are
-      // queued before chunk c's conversions and MFMAs; scheduling barriers
-      // keep the compiler from hoisting further ahead (register pressure)
-      uint4 ar[kTM], br[kTN];
+      // Software pipeline over the step's 8 MFMA slices (4 chunks of 32 K x
+      // 2 halves): while the MFMAs of slice n run, the wave converts slice n+1
+      // (2 or 3 conversions per MFMA) and, on even n, queues the fragment reads
+      // of chunk c+1 and a quarter of the next stage's DMA instructions.
+      // Scheduling-group barriers pin that interleave (1 MFMA, then VALU and
+      // LDS work) so the matrix core never waits for a conversion burst.
+      uint4 ra[2][kTM], rb[2][kTN];  // raw 16-byte fragments, by chunk parity
+      v8bf ab[2][kTM], bb[2][kTN];   // converted operands, by slice parity
+      float fa[kTM], fb[kTN];        // scale operands of the chunk being converted
+      auto load_raw = [&](int c) {
 #pragma unroll
-      for (int i = 0; i < kTM; ++i) ar[i] = a_frag(i, g.h);
+        for (int i = 0; i < kTM; ++i) ra[c & 1][i] = a_frag(i, 2 * c + g.h);
 #pragma unroll
-      for (int i = 0; i < kTN; ++i) br[i] = b_frag(i, g.h);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        uint4 an[kTM], bn[kTN];
-        if (c < 3) {
-#pragma unroll
-          for (int i = 0; i < kTM; ++i) an[i] = a_frag(i, 2 * (c + 1) + g.h);
-#pragma unroll
-          for (int i = 0; i < kTN; ++i) bn[i] = b_frag(i, 2 * (c + 1) + g.h);
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) dma_ab(d, 4 * c + q);
-        // the chunk's scale: sf=32 -> block c (byte c); sf=16 -> block 2c+h,
-        // byte 2(c&1)+h of atom c>>1
-        float fa[kTM], fb[kTN];
+        for (int i = 0; i < kTN; ++i) rb[c & 1][i] = b_frag(i, 2 * c + g.h);
+      };
+      // chunk c's scale: sf=32 -> block c (byte c); sf=16 -> block 2c+h, byte
+      // 2(c&1)+h of atom c>>1
+      auto scales = [&](int c) {
         const int j = SF == 32 ? 0 : (c >> 1);
         const int sh = SF == 32 ? 8 * c : 8 * (2 * (c & 1) + g.h);
 #pragma unroll
         for (int i = 0; i < kTM; ++i) fa[i] = e8m0_to_f32((sa[j][i] >> sh) & 0xFFu);
 #pragma unroll
         for (int i = 0; i < kTN; ++i) fb[i] = e8m0_to_f32((sb[j][i] >> sh) & 0xFFu);
+      };
+      // slice n = chunk n/2, bytes 0..7 (even n) or 8..15 (odd n) of each fragment
+      auto convert = [&](int n) {
+        const int c = n >> 1, t = n & 1;
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          v8bf ab[kTM], bb[kTN];
+        for (int i = 0; i < kTM; ++i)
+          ab[n & 1][i] = cvt8<FA>(t ? ra[c & 1][i].z : ra[c & 1][i].x, t ? ra[c & 1][i].w : ra[c & 1][i].y, fa[i]);
 #pragma unroll
-          for (int i = 0; i < kTM; ++i) ab[i] = cvt8<FA>(t ? ar[i].z : ar[i].x, t ? ar[i].w : ar[i].y, fa[i]);
+        for (int i = 0; i < kTN; ++i)
+          bb[n & 1][i] = cvt8<FB>(t ? rb[c & 1][i].z : rb[c & 1][i].x, t ? rb[c & 1][i].w : rb[c & 1][i].y, fb[i]);
+      };
+      load_raw(0);
+      scales(0);
+      convert(0);
 #pragma unroll
-          for (int i = 0; i < kTN; ++i) bb[i] = cvt8<FB>(t ? br[i].z : br[i].x, t ? br[i].w : br[i].y, fb[i]);
+      for (int n = 0; n < 8; ++n) {
+        const int c = n >> 1;
+        if ((n & 1) == 0 && c < 3) load_raw(c + 1);
+        if ((n & 1) == 0) {
 #pragma unroll
-          for (int i = 0; i < kTM; ++i)
+          for (int q = 0; q < Y::kDma / 4; ++q) dma_ab(d, (Y::kDma / 4) * c + q);
+        }
+        if (n < 7) {
+          if (((n + 1) & 1) == 0) scales((n + 1) >> 1);
+          convert(n + 1);
+        }
 #pragma unroll
-            for (int jj = 0; jj < kTN; ++jj)
-              acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                  bb[jj], ab[i], (kFirst && c == 0 && t == 0) ? zero16 : acc[i][jj], 0, 0, 0);
+        for (int i = 0; i < kTM; ++i)
+#pragma unroll
+          for (int jj = 0; jj < kTN; ++jj)
+            acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bb[n & 1][jj], ab[n & 1][i],
+                                                                 (kFirst && n == 0) ? zero16 : acc[i][jj], 0, 0, 0);
+        // interleave: each MFMA followed by up to 3 VALU ops; the chunk's
+        // fragment reads go out one after each of the first MFMAs
+#pragma unroll
+        for (int k = 0; k < kTM * kTN; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+          if (k < kTM + kTN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
         }
         __builtin_amdgcn_sched_barrier(0);
-        if (c < 3) {
-#pragma unroll
-          for (int i = 0; i < kTM; ++i) ar[i] = an[i];
-#pragma unroll
-          for (int i = 0; i < kTN; ++i) br[i] = bn[i];
-        }
       }
     } else {
 #pragma unroll
@@ -274,7 +388,7 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
           bf[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         }
 #pragma unroll
-        for (int q = 0; q < 8; ++q) dma_ab(d, 8 * S + q);
+        for (int q = 0; q < Y::kDma / 2; ++q) dma_ab(d, (Y::kDma / 2) * S + q);
         if constexpr (SF == 32) {
           // lane r supplies block 2S (K [0,32) of the slice), lane r+32 block 2S+1
           const int sh = 8 * (2 * S + g.h);
@@ -304,55 +418,46 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
         }
       }
     }
+
+    // BN = 128: one batch of the previous tile's stores, after all of this
+    // step's DMA
+    if constexpr (Y::kTrickle) {
+      if (pend > 0) {
+        const StoreCtx x = store_ctx(ptile);
+        store_one(x, kBatches - pend);
+        --pend;
+        after_dma += kBatch;
+      }
+    }
     ++s;
   };
 
-  // C stores and amax of tile `cur` from the accumulators
-  auto epilogue = [&]() {
-    // tile done: C stores (lane owns row m, 4-element runs of n) and amax,
-    // one 32x32 block at a time (its 16 accumulators are stored and folded
-    // into the amax before the next block is touched).  Rows past the
-    // tile's valid rows land past the resource (num_records = valid rows *
-    // N * 4); columns past N get an offset past it as well.
-    const Geo ge = geo(lane_opaque());
-    const unsigned c_bytes = (unsigned)cur.mvalid * (unsigned)p.N * 4u;
-    const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.C + ((int64_t)cur.l * p.M + cur.m0) * p.N, c_bytes);
-    const int mrow = 128 * wm + ge.r;
-    const int ncol = 128 * wn + 4 * ge.h;
-    const unsigned vbase = ((unsigned)mrow * (unsigned)p.N + (unsigned)(cur.n0 + ncol)) * 4u;
-#pragma unroll
-    for (int i = 0; i < kTM; ++i) {
-      const unsigned vrow = vbase + (unsigned)(32 * i) * (unsigned)p.N * 4u;
-      const bool rok = mrow + 32 * i < cur.mvalid;
-#pragma unroll
-      for (int jj = 0; jj < kTN; ++jj) {
-        // pin the block in the accumulator registers until here, so its
-        // copies out are made block by block rather than all at once
-        asm volatile("" : "+a"(acc[i][jj])::"memory");
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const bool ok = rok & (ncol + 32 * jj + 8 * q < cur.nvalid);
-          v4f v;
-          v[0] = acc[i][jj][4 * q];
-          v[1] = acc[i][jj][4 * q + 1];
-          v[2] = acc[i][jj][4 * q + 2];
-          v[3] = acc[i][jj][4 * q + 3];
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), rc,
-                                                 ok ? (int)(vrow + (32 * jj + 8 * q) * 4) : (int)c_bytes, 0, 0);
-          const unsigned m4 = max(max(__float_as_uint(v[0]) & 0x7FFFFFFFu, __float_as_uint(v[1]) & 0x7FFFFFFFu),
-                                  max(__float_as_uint(v[2]) & 0x7FFFFFFFu, __float_as_uint(v[3]) & 0x7FFFFFFFu));
-          lmax = max(lmax, m4 & (0u - (unsigned)ok));  // arithmetic mask: no branch
-        }
-        __builtin_amdgcn_sched_barrier(0);
+  // tile end: BN = 256 stores `acc` now; BN = 128 finishes the previous
+  // tile's stores if K was too short to spread them, then moves `acc` to
+  // `prev` for the next tile to store
+  auto tile_end = [&]() {
+    if constexpr (Y::kTrickle) {
+      if (pend > 0) {
+        const StoreCtx x = store_ctx(ptile);
+        for (; pend > 0; --pend) store_one(x, kBatches - pend);
+        after_dma = 64;  // an unusual count: the next wait drains everything
       }
+#pragma unroll
+      for (int i = 0; i < kTM; ++i)
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) prev[i][j] = acc[i][j];
+      ptile = cur;
+      pend = kBatches;
+    } else {
+      store_all(store_ctx(cur));
+      after_dma = 63;  // 64 stores: waiting for 63 covers every earlier DMA
     }
-    stores_pending = true;
   };
 
   for (int i = 0; i < my_tiles; ++i) {
     const int tn = t0 + (i + 1) * G;
     const bool more = i + 1 < my_tiles;
-    const Tile nxt = more ? make_tile<kBM, kBN>(p, tn) : cur;
+    const Tile nxt = more ? make_tile<kBM, BN>(p, tn) : cur;
     if (p.ksteps == 1) {
       step(std::true_type{}, 0, nxt, more);
     } else {
@@ -360,8 +465,15 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
       for (int kt = 1; kt + 1 < p.ksteps; ++kt) step(std::false_type{}, kt, cur, true);
       step(std::false_type{}, p.ksteps - 1, nxt, more);
     }
-    epilogue();
+    tile_end();
     cur = nxt;
+  }
+  if constexpr (Y::kTrickle) {
+    // the last tile's stores
+    if (pend > 0) {
+      const StoreCtx x = store_ctx(ptile);
+      for (; pend > 0; --pend) store_one(x, kBatches - pend);
+    }
   }
   // no DMA may still be writing this workgroup's LDS when it exits
   wait_vm<0>();

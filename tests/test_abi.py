@@ -67,10 +67,10 @@ def test_sf_bytes(lib):
 
 
 def test_launch_config_host_only(lib):
-    # without a device the choice assumes 256 CUs: 3072 tiles of 256x256 fill them evenly
+    # without a device the choice assumes 256 CUs: 6144 tiles of 256x128 fill them evenly
     tm, tn, g = lib.mxgemm_launch_config(8192, 24576, 1536, 1, 32, with_grid=False)
-    assert (tm, tn, g) == (256, 256, None)
-    # 64 tiles of 256x256 would leave most CUs idle: 128x128
+    assert (tm, tn, g) == (256, 128, None)
+    # 128 tiles of 256x128 would leave most CUs idle: 128x128
     tm, tn, _ = lib.mxgemm_launch_config(2048, 2048, 2048, 1, 32, with_grid=False)
     assert (tm, tn) == (128, 128)
     tm, tn, _ = lib.mxgemm_launch_config(4096, 4096, 0, 1, 32, with_grid=False)
@@ -90,7 +90,8 @@ def test_errors_before_device_work(lib):
     assert f(*(args[:5] + [None]), *dims, 32, 0, 0, 0, None) == lib.MXG_ERR_NULL
     assert f(*([good + 8] + args[1:]), *dims, 32, 0, 0, 0, None) == lib.MXG_ERR_ALIGN
     assert f(*(args[:4] + [good + 4] + args[5:]), *dims, 32, 0, 0, 0, None) == lib.MXG_ERR_ALIGN
-    assert f(*args, *dims, 32, 0, 0, 16, None) == lib.MXG_ERR_FLAGS
+    assert f(*args, *dims, 32, 0, 0, 32, None) == lib.MXG_ERR_FLAGS
+    assert f(*args, *dims, 32, 0, 0, 24, None) == lib.MXG_ERR_FLAGS   # two tile flags
     assert f(*args, *dims, 32, 0, 0, 12, None) == lib.MXG_ERR_FLAGS   # both tile flags
     assert f(*args, 256, 256, 256, 1, 64, 0, 0, 0, None) == lib.MXG_ERR_SFVEC
     assert f(*args, 256, 256, 256, 1, 32, 0, 9, 0, None) == lib.MXG_ERR_FMT
