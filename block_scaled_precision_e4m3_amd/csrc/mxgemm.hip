@@ -88,9 +88,10 @@ bool on_device(const void* p, int dev) {
 // 256x256: one workgroup per CU, 4 waves of 128x128; half the L2->LDS bytes
 // per flop of 128x128, but a tile's C is stored in one burst at its end.
 // 256x128: one workgroup per CU, 4 waves of 128x64; its C stores are spread
-// over the next tile.  The automatic choice takes 256x128 when its tiles fill
-// the CUs at least as evenly as 128x128 tiles fill two workgroups per CU (and
-// K > 0), otherwise 128x128.
+// over the next tile (measured slower than 256x256 on the large workloads; kept
+// for tests and tuning).  The automatic choice takes 256x256 when its tiles
+// fill the CUs at least as evenly as 128x128 tiles fill two workgroups per CU
+// (and K > 0), otherwise 128x128.
 struct Config {
   int kind;  // 0: 128x128, 1: 256x256, 2: 256x128
   int tile_m, tile_n, per_cu;
@@ -105,8 +106,8 @@ double fill(int64_t tiles, int64_t slots) {
 
 Config choose(int64_t M, int64_t N, int64_t K, int64_t L, int cus) {
   const int64_t small = L * cdiv(M, 128) * cdiv(N, 128);
-  const int64_t mid = L * cdiv(M, 256) * cdiv(N, 128);
-  if (K > 0 && mid >= cus && fill(mid, cus) >= fill(small, 2 * (int64_t)cus) - 1e-9) return kMid;
+  const int64_t big = L * cdiv(M, 256) * cdiv(N, 256);
+  if (K > 0 && big >= cus && fill(big, cus) >= fill(small, 2 * (int64_t)cus) - 1e-9) return kBig;
   return kSmall;
 }
 

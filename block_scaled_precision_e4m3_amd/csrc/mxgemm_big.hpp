@@ -196,7 +196,7 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
     x.nvalid = T.nvalid;
     return x;
   };
-  auto store4 = [&](const StoreCtx& x, const v16f& blk, int i, int j, int q) {
+  auto store4 = [&](const StoreCtx& x, const v16f& blk, int i, int j, int q) __attribute__((always_inline)) {
     const bool ok = (x.mrow + 32 * i < x.mvalid) & (x.ncol + 32 * j + 8 * q < x.nvalid);
     v4f v;
     v[0] = blk[4 * q];
@@ -212,7 +212,7 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   // BN = 256: every block of `acc` at tile end, one block at a time (each block
   // is pinned in the accumulation registers until its turn, so its copies out
   // are made block by block rather than all at once)
-  auto store_all = [&](const StoreCtx& x) {
+  auto store_all = [&](const StoreCtx& x) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < kTM; ++i)
 #pragma unroll
@@ -227,7 +227,7 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   // the registers are named statically
   constexpr int kBatch = 4;
   constexpr int kBatches = kTM * kTN * 4 / kBatch;
-  auto store_batch = [&](const StoreCtx& x, auto bc) {
+  auto store_batch = [&](const StoreCtx& x, auto bc) __attribute__((always_inline)) {
     constexpr int b = decltype(bc)::value;
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
@@ -236,7 +236,7 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
       store4(x, prev[i][j], i, j, q);
     }
   };
-  auto store_one = [&](const StoreCtx& x, int b) {
+  auto store_one = [&](const StoreCtx& x, int b) __attribute__((always_inline)) {
     static_assert(!Y::kTrickle || kBatches == 8, "batch dispatch below is written for 8 batches");
     switch (b) {
       case 0: store_batch(x, std::integral_constant<int, 0>{}); break;
@@ -268,7 +268,7 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   // (FIRST) the first MFMA of every accumulator takes a zero C operand instead
   // of the register, so the accumulators never need clearing and stay in the
   // matrix-core registers from tile to tile.
-  auto step = [&](auto first, int kt, const Tile& nt, bool has_next) {
+  auto step = [&](auto first, int kt, const Tile& nt, bool has_next) __attribute__((always_inline)) {
     constexpr bool kFirst = decltype(first)::value;
     // this wave's DMA for step s is complete (only stores may have been
     // queued after it); the barrier extends that to every wave and frees the
@@ -435,7 +435,7 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   // tile end: BN = 256 stores `acc` now; BN = 128 finishes the previous
   // tile's stores if K was too short to spread them, then moves `acc` to
   // `prev` for the next tile to store
-  auto tile_end = [&]() {
+  auto tile_end = [&]() __attribute__((always_inline)) {
     if constexpr (Y::kTrickle) {
       if (pend > 0) {
         const StoreCtx x = store_ctx(ptile);

@@ -67,10 +67,10 @@ def test_sf_bytes(lib):
 
 
 def test_launch_config_host_only(lib):
-    # without a device the choice assumes 256 CUs: 6144 tiles of 256x128 fill them evenly
+    # without a device the choice assumes 256 CUs: 3072 tiles of 256x256 fill them evenly
     tm, tn, g = lib.mxgemm_launch_config(8192, 24576, 1536, 1, 32, with_grid=False)
-    assert (tm, tn, g) == (256, 128, None)
-    # 128 tiles of 256x128 would leave most CUs idle: 128x128
+    assert (tm, tn, g) == (256, 256, None)
+    # 64 tiles of 256x256 would leave most CUs idle: 128x128
     tm, tn, _ = lib.mxgemm_launch_config(2048, 2048, 2048, 1, 32, with_grid=False)
     assert (tm, tn) == (128, 128)
     tm, tn, _ = lib.mxgemm_launch_config(4096, 4096, 0, 1, 32, with_grid=False)
