@@ -52,6 +52,10 @@ struct Layout {
   static constexpr int kTN = BN / 64;                // 32-column MFMA blocks per wave
   static constexpr int kDma = (kBM + BN) / 32;       // A/B DMA instructions per wave per step
   static constexpr bool kTrickle = BN == 128;        // C stores spread over the next tile
+  // BN = 256: per-wave LDS area where the epilogue transposes one 32x32 fp32
+  // block (rows padded to 36 floats) so its stores write whole 128-byte lines
+  static constexpr int kEpiRow = 36;
+  static constexpr int kEpiBytes = kTrickle ? 0 : 4 * 32 * kEpiRow * 4;
 };
 
 __device__ __forceinline__ uint4 lds16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
@@ -71,7 +75,7 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   constexpr int NSF = Y::NSF;
   constexpr int kTN = Y::kTN;
   constexpr int kWN = BN / 2;  // wave tile columns
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * Y::kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * Y::kStage + Y::kEpiBytes];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -182,7 +186,7 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   struct StoreCtx {
     __amdgpu_buffer_rsrc_t rc;
     unsigned c_bytes, vbase;
-    int mrow, ncol, mvalid, nvalid;
+    int mrow, ncol, mvalid, nvalid, n0;
   };
   auto store_ctx = [&](const Tile& T) {
     StoreCtx x;
@@ -194,6 +198,7 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
     x.vbase = ((unsigned)x.mrow * (unsigned)p.N + (unsigned)(T.n0 + x.ncol)) * 4u;
     x.mvalid = T.mvalid;
     x.nvalid = T.nvalid;
+    x.n0 = T.n0;
     return x;
   };
   auto store4 = [&](const StoreCtx& x, const v16f& blk, int i, int j, int q) __attribute__((always_inline)) {
@@ -212,14 +217,48 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   // BN = 256: every block of `acc` at tile end, one block at a time (each block
   // is pinned in the accumulation registers until its turn, so its copies out
   // are made block by block rather than all at once)
+  // BN = 256: every block of `acc` at tile end, one block at a time (each block
+  // is pinned in the accumulation registers until its turn, so its copies out
+  // are made block by block rather than all at once).  A block goes through
+  // the wave's LDS area: lane (r, h) writes its row r, columns 8q + 4h; lane L
+  // then reads row 8k + L/8, columns 4(L%8) .. +4, so each of the 4 stores
+  // covers 8 rows x 128 contiguous bytes (whole cache lines) instead of
+  // 32 rows x 2 x 16 bytes.  Rows of 36 floats keep both passes free of bank
+  // conflicts.  The wave's own LDS operations run in order, so no barrier.
   auto store_all = [&](const StoreCtx& x) __attribute__((always_inline)) {
+    const int ln = lane_opaque();
+    uint8_t* epi = lds + 2 * Y::kStage + wave * (32 * Y::kEpiRow * 4);
+    const int wr_off = ((ln & 31) * Y::kEpiRow + 4 * (ln >> 5)) * 4;        // + 32 q bytes
+    const int rd_row = ln >> 3, rd_col = 4 * (ln & 7);
+    const int rd_off = (rd_row * Y::kEpiRow + rd_col) * 4;                  // + 8 k rows
+    const int col_base = kWN * wn + rd_col;                                  // tile column of the lane's run
+    const unsigned vrow0 = ((unsigned)(128 * wm + rd_row) * (unsigned)p.N + (unsigned)(x.n0 + col_base)) * 4u;
 #pragma unroll
     for (int i = 0; i < kTM; ++i)
 #pragma unroll
       for (int j = 0; j < kTN; ++j) {
         asm volatile("" : "+a"(acc[i][j])::"memory");
 #pragma unroll
-        for (int q = 0; q < 4; ++q) store4(x, acc[i][j], i, j, q);
+        for (int q = 0; q < 4; ++q) {
+          v4f v;
+          v[0] = acc[i][j][4 * q];
+          v[1] = acc[i][j][4 * q + 1];
+          v[2] = acc[i][j][4 * q + 2];
+          v[3] = acc[i][j][4 * q + 3];
+          *reinterpret_cast<v4f*>(epi + wr_off + 32 * q) = v;
+        }
+        const bool cok = col_base + 32 * j < x.nvalid;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const v4f v = *reinterpret_cast<const v4f*>(epi + rd_off + k * 8 * Y::kEpiRow * 4);
+          const int row = 128 * wm + 32 * i + 8 * k + rd_row;
+          const bool ok = cok & (row < x.mvalid);
+          const unsigned off = vrow0 + (unsigned)(32 * i + 8 * k) * (unsigned)p.N * 4u + (unsigned)(32 * j * 4);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), x.rc, ok ? (int)off : (int)x.c_bytes, 0, 0);
+          const unsigned m4 = max(max(__float_as_uint(v[0]) & 0x7FFFFFFFu, __float_as_uint(v[1]) & 0x7FFFFFFFu),
+                                  max(__float_as_uint(v[2]) & 0x7FFFFFFFu, __float_as_uint(v[3]) & 0x7FFFFFFFu));
+          lmax = max(lmax, m4 & (0u - (unsigned)ok));
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
   };
