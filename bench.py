@@ -92,10 +92,16 @@ def _csv_rows(pattern):
     return rows
 
 
+def _is_gemm(name):
+    return "mxgemm_amax" in name and "reset" not in name
+
+
 def _per_dispatch(rows, kernel_substr, counter):
     per = {}
     for r in rows:
-        if kernel_substr in r["Kernel_Name"] and r["Counter_Name"] == counter:
+        name = r["Kernel_Name"]
+        hit = _is_gemm(name) if kernel_substr == "gemm" else kernel_substr in name
+        if hit and r["Counter_Name"] == counter:
             per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
     return list(per.values())
 
@@ -105,7 +111,7 @@ def rocprof_summary(d, workload, fp8_mfma, commands):
     import workloads as W
     cfg = W.WORKLOADS[workload]
     M, N, K, L, sf = cfg["M"], cfg["N"], cfg["K"], cfg["L"], cfg["sf"]
-    out = [f"# rocprofv3 summary: mxgemm_amax_kernel ({'fp8 MFMA' if fp8_mfma else 'bf16 MFMA'} path), "
+    out = [f"# rocprofv3 summary: the GEMM + amax kernel ({'fp8 MFMA' if fp8_mfma else 'bf16 MFMA'} path), "
            f"workload {cfg['name']} (M={M} N={N} K={K} L={L} sf={sf})", ""]
     out.append("commands (from the repository root; rocprofv3 runs from /tmp with TMPDIR=/tmp):")
     out.extend("  " + c for c in commands)
@@ -118,7 +124,7 @@ def rocprof_summary(d, workload, fp8_mfma, commands):
         out.append(f"  {name[:100]:100s} calls {int(r['Calls']):5d}  avg {float(r['AverageNs']) / 1e3:10.2f} us  "
                    f"min {float(r['MinNs']) / 1e3:10.2f}  max {float(r['MaxNs']) / 1e3:10.2f}  "
                    f"{float(r['Percentage']):5.1f}%")
-        if "mxgemm_amax_kernel" in name:
+        if _is_gemm(name):
             avg_us = float(r["AverageNs"]) / 1e3
     out.append("")
     fl = W.flops(M, N, K, L)
@@ -128,8 +134,8 @@ def rocprof_summary(d, workload, fp8_mfma, commands):
     fetch = _csv_rows(os.path.join(d, "fetch", "**", "*counter_collection.csv"))
     write = _csv_rows(os.path.join(d, "write", "**", "*counter_collection.csv"))
     if fetch and write:
-        gf = _per_dispatch(fetch, "mxgemm_amax_kernel", "FETCH_SIZE")
-        gw = _per_dispatch(write, "mxgemm_amax_kernel", "WRITE_SIZE")
+        gf = _per_dispatch(fetch, "gemm", "FETCH_SIZE")
+        gw = _per_dispatch(write, "gemm", "WRITE_SIZE")
         cf = _per_dispatch(fetch, "neg", "FETCH_SIZE")
         cw = _per_dispatch(write, "neg", "WRITE_SIZE")
         f_fac = COPY_PROBE_BYTES / (1024.0 * sum(cf) / len(cf))
