@@ -214,17 +214,14 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
                             max(__float_as_uint(v[2]) & 0x7FFFFFFFu, __float_as_uint(v[3]) & 0x7FFFFFFFu));
     lmax = max(lmax, m4 & (0u - (unsigned)ok));  // arithmetic mask: no branch
   };
-  // BN = 256: every block of `acc` at tile end, one block at a time (each block
-  // is pinned in the accumulation registers until its turn, so its copies out
-  // are made block by block rather than all at once)
-  // BN = 256: every block of `acc` at tile end, one block at a time (each block
-  // is pinned in the accumulation registers until its turn, so its copies out
-  // are made block by block rather than all at once).  A block goes through
-  // the wave's LDS area: lane (r, h) writes its row r, columns 8q + 4h; lane L
-  // then reads row 8k + L/8, columns 4(L%8) .. +4, so each of the 4 stores
-  // covers 8 rows x 128 contiguous bytes (whole cache lines) instead of
-  // 32 rows x 2 x 16 bytes.  Rows of 36 floats keep both passes free of bank
-  // conflicts.  The wave's own LDS operations run in order, so no barrier.
+  // BN = 256: every block of `acc` at tile end.  A block goes through the
+  // wave's LDS area: lane (r, h) writes its row r, columns 8q + 4h straight
+  // from the accumulation registers; lane L then reads row 8k + L/8, columns
+  // 4(L%8) .. +4, so each of the block's 4 stores covers 8 rows x 128
+  // contiguous bytes (whole cache lines) instead of 32 rows x 2 x 16 bytes.
+  // Rows of 36 floats keep both passes free of bank conflicts.  The wave's LDS
+  // operations execute in order, so block b+1 is written and read back while
+  // block b's stores go out (its reads precede those writes), with no barrier.
   auto store_all = [&](const StoreCtx& x) __attribute__((always_inline)) {
     const int ln = lane_opaque();
     uint8_t* epi = lds + 2 * Y::kStage + wave * (32 * Y::kEpiRow * 4);
@@ -233,34 +230,50 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
     const int rd_off = (rd_row * Y::kEpiRow + rd_col) * 4;                  // + 8 k rows
     const int col_base = kWN * wn + rd_col;                                  // tile column of the lane's run
     const unsigned vrow0 = ((unsigned)(128 * wm + rd_row) * (unsigned)p.N + (unsigned)(x.n0 + col_base)) * 4u;
+    auto put = [&](int i, int j) {
 #pragma unroll
-    for (int i = 0; i < kTM; ++i)
-#pragma unroll
-      for (int j = 0; j < kTN; ++j) {
-        asm volatile("" : "+a"(acc[i][j])::"memory");
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          v4f v;
-          v[0] = acc[i][j][4 * q];
-          v[1] = acc[i][j][4 * q + 1];
-          v[2] = acc[i][j][4 * q + 2];
-          v[3] = acc[i][j][4 * q + 3];
-          *reinterpret_cast<v4f*>(epi + wr_off + 32 * q) = v;
-        }
-        const bool cok = col_base + 32 * j < x.nvalid;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const v4f v = *reinterpret_cast<const v4f*>(epi + rd_off + k * 8 * Y::kEpiRow * 4);
-          const int row = 128 * wm + 32 * i + 8 * k + rd_row;
-          const bool ok = cok & (row < x.mvalid);
-          const unsigned off = vrow0 + (unsigned)(32 * i + 8 * k) * (unsigned)p.N * 4u + (unsigned)(32 * j * 4);
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), x.rc, ok ? (int)off : (int)x.c_bytes, 0, 0);
-          const unsigned m4 = max(max(__float_as_uint(v[0]) & 0x7FFFFFFFu, __float_as_uint(v[1]) & 0x7FFFFFFFu),
-                                  max(__float_as_uint(v[2]) & 0x7FFFFFFFu, __float_as_uint(v[3]) & 0x7FFFFFFFu));
-          lmax = max(lmax, m4 & (0u - (unsigned)ok));
-        }
-        __builtin_amdgcn_sched_barrier(0);
+      for (int q = 0; q < 4; ++q) {
+        v4f v;
+        v[0] = acc[i][j][4 * q];
+        v[1] = acc[i][j][4 * q + 1];
+        v[2] = acc[i][j][4 * q + 2];
+        v[3] = acc[i][j][4 * q + 3];
+        *reinterpret_cast<v4f*>(epi + wr_off + 32 * q) = v;
       }
+    };
+    auto get = [&](v4f (&out)[4]) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) out[k] = *reinterpret_cast<const v4f*>(epi + rd_off + k * 8 * Y::kEpiRow * 4);
+    };
+    auto emit = [&](const v4f (&v)[4], int i, int j) {
+      const bool cok = col_base + 32 * j < x.nvalid;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int row = 128 * wm + 32 * i + 8 * k + rd_row;
+        const bool ok = cok & (row < x.mvalid);
+        const unsigned off = vrow0 + (unsigned)(32 * i + 8 * k) * (unsigned)p.N * 4u + (unsigned)(32 * j * 4);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v[k]), x.rc, ok ? (int)off : (int)x.c_bytes, 0, 0);
+        const unsigned m4 = max(max(__float_as_uint(v[k][0]) & 0x7FFFFFFFu, __float_as_uint(v[k][1]) & 0x7FFFFFFFu),
+                                max(__float_as_uint(v[k][2]) & 0x7FFFFFFFu, __float_as_uint(v[k][3]) & 0x7FFFFFFFu));
+        lmax = max(lmax, m4 & (0u - (unsigned)ok));
+      }
+    };
+    v4f cur[4], nxt[4];
+    put(0, 0);
+    get(cur);
+#pragma unroll
+    for (int b = 0; b < kTM * kTN; ++b) {
+      const int i = b / kTN, j = b % kTN;
+      if (b + 1 < kTM * kTN) {
+        put((b + 1) / kTN, (b + 1) % kTN);
+        get(nxt);
+      }
+      emit(cur, i, j);
+      if (b + 1 < kTM * kTN) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) cur[k] = nxt[k];
+      }
+    }
   };
   // BN = 128: batch b (4 stores) of `prev`; b is a compile-time constant so
   // the registers are named statically
