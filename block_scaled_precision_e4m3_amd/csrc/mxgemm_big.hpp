@@ -315,8 +315,8 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
     for (int q = 0; q < Y::kDma; ++q) dma_ab(d0, q);
   }
 
-  // One K step of tile `cur`; queues the DMA of the next step (this tile's
-  // next K step or the next tile's first, `nt`).  On a tile's first step
+  // FP8 datapath: one K step of tile `cur`; queues the DMA of the next step
+  // (this tile's next K step or the next tile's first, `nt`).  On a tile's first step
   // (FIRST) the first MFMA of every accumulator takes a zero C operand instead
   // of the register, so the accumulators never need clearing and stay in the
   // matrix-core registers from tile to tile.
@@ -356,116 +356,48 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
         sb[j][i] = sf_tail(lds4(st + Y::kOffSFB + (brg * NSF + j) * 512 + 16 * g.r + 4 * (bdw + i)), ga, p.Kb);
     }
 
-    if constexpr (MODE == kModeBf16) {
-      // Software pipeline over the step's 8 MFMA slices (4 chunks of 32 K x
-      // 2 halves): while the MFMAs of slice n run, the wave converts slice n+1
-      // (2 or 3 conversions per MFMA) and, on even n, queues the fragment reads
-      // of chunk c+1 and a quarter of the next stage's DMA instructions.
-      // Scheduling-group barriers pin that interleave (1 MFMA, then VALU and
-      // LDS work) so the matrix core never waits for a conversion burst.
-      uint4 ra[2][kTM], rb[2][kTN];  // raw 16-byte fragments, by chunk parity
-      v8bf ab[2][kTM], bb[2][kTN];   // converted operands, by slice parity
-      float fa[kTM], fb[kTN];        // scale operands of the chunk being converted
-      auto load_raw = [&](int c) {
+    // FP8 datapath (bf16 uses step_bf16 below)
 #pragma unroll
-        for (int i = 0; i < kTM; ++i) ra[c & 1][i] = a_frag(i, 2 * c + g.h);
+    for (int S = 0; S < 2; ++S) {
+      v8i af[kTM], bf[kTN];
 #pragma unroll
-        for (int i = 0; i < kTN; ++i) rb[c & 1][i] = b_frag(i, 2 * c + g.h);
-      };
-      // chunk c's scale: sf=32 -> block c (byte c); sf=16 -> block 2c+h, byte
-      // 2(c&1)+h of atom c>>1
-      auto scales = [&](int c) {
-        const int j = SF == 32 ? 0 : (c >> 1);
-        const int sh = SF == 32 ? 8 * c : 8 * (2 * (c & 1) + g.h);
+      for (int i = 0; i < kTM; ++i) {
+        const uint4 lo = a_frag(i, 4 * S + g.h);
+        const uint4 hi = a_frag(i, 4 * S + 2 + g.h);
+        af[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
 #pragma unroll
-        for (int i = 0; i < kTM; ++i) fa[i] = e8m0_to_f32((sa[j][i] >> sh) & 0xFFu);
+      for (int i = 0; i < kTN; ++i) {
+        const uint4 lo = b_frag(i, 4 * S + g.h);
+        const uint4 hi = b_frag(i, 4 * S + 2 + g.h);
+        bf[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
 #pragma unroll
-        for (int i = 0; i < kTN; ++i) fb[i] = e8m0_to_f32((sb[j][i] >> sh) & 0xFFu);
-      };
-      // slice n = chunk n/2, bytes 0..7 (even n) or 8..15 (odd n) of each fragment
-      auto convert = [&](int n) {
-        const int c = n >> 1, t = n & 1;
-#pragma unroll
-        for (int i = 0; i < kTM; ++i)
-          ab[n & 1][i] = cvt8<FA>(t ? ra[c & 1][i].z : ra[c & 1][i].x, t ? ra[c & 1][i].w : ra[c & 1][i].y, fa[i]);
-#pragma unroll
-        for (int i = 0; i < kTN; ++i)
-          bb[n & 1][i] = cvt8<FB>(t ? rb[c & 1][i].z : rb[c & 1][i].x, t ? rb[c & 1][i].w : rb[c & 1][i].y, fb[i]);
-      };
-      load_raw(0);
-      scales(0);
-      convert(0);
-#pragma unroll
-      for (int n = 0; n < 8; ++n) {
-        const int c = n >> 1;
-        if ((n & 1) == 0 && c < 3) load_raw(c + 1);
-        if ((n & 1) == 0) {
-#pragma unroll
-          for (int q = 0; q < Y::kDma / 4; ++q) dma_ab(d, (Y::kDma / 4) * c + q);
-        }
-        if (n < 7) {
-          if (((n + 1) & 1) == 0) scales((n + 1) >> 1);
-          convert(n + 1);
-        }
+      for (int q = 0; q < Y::kDma / 2; ++q) dma_ab(d, (Y::kDma / 2) * S + q);
+      if constexpr (SF == 32) {
+        // lane r supplies block 2S (K [0,32) of the slice), lane r+32 block 2S+1
+        const int sh = 8 * (2 * S + g.h);
 #pragma unroll
         for (int i = 0; i < kTM; ++i)
 #pragma unroll
           for (int jj = 0; jj < kTN; ++jj)
-            acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bb[n & 1][jj], ab[n & 1][i],
-                                                                 (kFirst && n == 0) ? zero16 : acc[i][jj], 0, 0, 0);
-        // interleave: each MFMA followed by up to 3 VALU ops; the chunk's
-        // fragment reads go out one after each of the first MFMAs
-#pragma unroll
-        for (int k = 0; k < kTM * kTN; ++k) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
-          if (k < kTM + kTN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    } else {
-#pragma unroll
-      for (int S = 0; S < 2; ++S) {
-        v8i af[kTM], bf[kTN];
+            acc[i][jj] = mfma_f8<0, FA, FB>(bf[jj], af[i], (kFirst && S == 0) ? zero16 : acc[i][jj],
+                                            sb[0][jj] >> sh, sa[0][i] >> sh);
+      } else {
+        // 16-element blocks (atom S): the scale slot of K [0,32) gets block 0
+        // (MFMA 1, odd-block A lanes zeroed) or block 1 (MFMA 2, even-block
+        // A lanes zeroed); that of K [32,64) blocks 2 / 3
+        const v8i zero = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
         for (int i = 0; i < kTM; ++i) {
-          const uint4 lo = a_frag(i, 4 * S + g.h);
-          const uint4 hi = a_frag(i, 4 * S + 2 + g.h);
-          af[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        }
+          const v8i a_even = g.h ? zero : af[i];
+          const v8i a_odd = g.h ? af[i] : zero;
+          const unsigned sai = sa[S][i] >> (16 * g.h);
 #pragma unroll
-        for (int i = 0; i < kTN; ++i) {
-          const uint4 lo = b_frag(i, 4 * S + g.h);
-          const uint4 hi = b_frag(i, 4 * S + 2 + g.h);
-          bf[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        }
-#pragma unroll
-        for (int q = 0; q < Y::kDma / 2; ++q) dma_ab(d, (Y::kDma / 2) * S + q);
-        if constexpr (SF == 32) {
-          // lane r supplies block 2S (K [0,32) of the slice), lane r+32 block 2S+1
-          const int sh = 8 * (2 * S + g.h);
-#pragma unroll
-          for (int i = 0; i < kTM; ++i)
-#pragma unroll
-            for (int jj = 0; jj < kTN; ++jj)
-              acc[i][jj] = mfma_f8<0, FA, FB>(bf[jj], af[i], (kFirst && S == 0) ? zero16 : acc[i][jj],
-                                              sb[0][jj] >> sh, sa[0][i] >> sh);
-        } else {
-          // 16-element blocks (atom S): the scale slot of K [0,32) gets block 0
-          // (MFMA 1, odd-block A lanes zeroed) or block 1 (MFMA 2, even-block
-          // A lanes zeroed); that of K [32,64) blocks 2 / 3
-          const v8i zero = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-          for (int i = 0; i < kTM; ++i) {
-            const v8i a_even = g.h ? zero : af[i];
-            const v8i a_odd = g.h ? af[i] : zero;
-            const unsigned sai = sa[S][i] >> (16 * g.h);
-#pragma unroll
-            for (int jj = 0; jj < kTN; ++jj) {
-              const unsigned sbj = sb[S][jj] >> (16 * g.h);
-              acc[i][jj] = mfma_f8<0, FA, FB>(bf[jj], a_even, (kFirst && S == 0) ? zero16 : acc[i][jj], sbj, sai);
-              acc[i][jj] = mfma_f8<1, FA, FB>(bf[jj], a_odd, acc[i][jj], sbj, sai);
-            }
+          for (int jj = 0; jj < kTN; ++jj) {
+            const unsigned sbj = sb[S][jj] >> (16 * g.h);
+            acc[i][jj] = mfma_f8<0, FA, FB>(bf[jj], a_even, (kFirst && S == 0) ? zero16 : acc[i][jj], sbj, sai);
+            acc[i][jj] = mfma_f8<1, FA, FB>(bf[jj], a_odd, acc[i][jj], sbj, sai);
           }
         }
       }
@@ -479,6 +411,136 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
         store_one(x, kBatches - pend);
         --pend;
         after_dma += kBatch;
+      }
+    }
+    ++s;
+  };
+
+  // --- bf16 datapath: steps pipelined across step boundaries -----------------
+  // The next step's scale dwords and first 32-K chunk are read, and its first
+  // MFMA slice converted, while the current step's last slice runs, so a step
+  // starts issuing MFMAs at once.  Two barriers per step, each placed right
+  // after a slice's MFMAs are queued so its wait overlaps them:
+  //   B  (after slice 0): every wave has finished the previous step, so the
+  //      other stage is free and the DMA of the next step goes out (slices 1-3);
+  //   B' (after slice 6): every wave's DMA of the next step has landed (each
+  //      wave first waits for its own), so the next stage may be read.
+  unsigned sa[NSF][kTM], sb[NSF][kTN];  // scale dwords of the current step
+  uint4 ra[2][kTM], rb[2][kTN];         // raw 16-byte fragments, by chunk parity
+  v8bf ab[2][kTM], bb[2][kTN];          // converted operands, by slice parity
+  float fa[kTM], fb[kTN];               // scale operands of the chunk being converted
+  const int brg = (kWN * wn) >> 7, bdw = ((kWN * wn) >> 5) & 3;
+  // SF dwords of step kt from stage st: NSF atoms x (4 or kTN) fragment rows.
+  // A rows 128*wm + 32i + r: atom group wm, dword i; B rows kWN*wn + 32i + r:
+  // atom group (kWN*wn)/128, dword ((kWN*wn)/32)%4 + i.
+  auto load_sf = [&](const Geo& g, const uint8_t* st, int kt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < NSF; ++j) {
+      const int ga = NSF * kt + j;
+#pragma unroll
+      for (int i = 0; i < kTM; ++i)
+        sa[j][i] = sf_tail(lds4(st + Y::kOffSFA + (wm * NSF + j) * 512 + 16 * g.r + 4 * i), ga, p.Kb);
+#pragma unroll
+      for (int i = 0; i < kTN; ++i)
+        sb[j][i] = sf_tail(lds4(st + Y::kOffSFB + (brg * NSF + j) * 512 + 16 * g.r + 4 * (bdw + i)), ga, p.Kb);
+    }
+  };
+  // chunk c's fragments (32-row steps keep row & 7, so only the chunk is swizzled)
+  auto load_raw = [&](const Geo& g, const uint8_t* st, int c) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kTM; ++i) ra[c & 1][i] = lds16(st + g.a_off + (((2 * c + g.h) ^ g.xr) << 4) + 4096 * i);
+#pragma unroll
+    for (int i = 0; i < kTN; ++i) rb[c & 1][i] = lds16(st + g.b_off + (((2 * c + g.h) ^ g.xr) << 4) + 4096 * i);
+  };
+  // chunk c's scale: sf=32 -> block c (byte c); sf=16 -> block 2c+h, byte
+  // 2(c&1)+h of atom c>>1
+  auto scales = [&](const Geo& g, int c) __attribute__((always_inline)) {
+    const int j = SF == 32 ? 0 : (c >> 1);
+    const int sh = SF == 32 ? 8 * c : 8 * (2 * (c & 1) + g.h);
+#pragma unroll
+    for (int i = 0; i < kTM; ++i) fa[i] = e8m0_to_f32((sa[j][i] >> sh) & 0xFFu);
+#pragma unroll
+    for (int i = 0; i < kTN; ++i) fb[i] = e8m0_to_f32((sb[j][i] >> sh) & 0xFFu);
+  };
+  // slice n = chunk n/2, bytes 0..7 (even n) or 8..15 (odd n) of each fragment
+  auto convert = [&](int n) __attribute__((always_inline)) {
+    const int c = n >> 1, t = n & 1;
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+      ab[n & 1][i] = cvt8<FA>(t ? ra[c & 1][i].z : ra[c & 1][i].x, t ? ra[c & 1][i].w : ra[c & 1][i].y, fa[i]);
+#pragma unroll
+    for (int i = 0; i < kTN; ++i)
+      bb[n & 1][i] = cvt8<FB>(t ? rb[c & 1][i].z : rb[c & 1][i].x, t ? rb[c & 1][i].w : rb[c & 1][i].y, fb[i]);
+  };
+  // the first step's inputs (after its DMA, issued above, has landed everywhere)
+  auto prime = [&](int kt0) __attribute__((always_inline)) {
+    if constexpr (MODE == kModeBf16) {
+      wait_vm<0>();
+      barrier();
+      const Geo g = geo(lane_opaque());
+      load_sf(g, lds, kt0);
+      load_raw(g, lds, 0);
+      scales(g, 0);
+      convert(0);
+    }
+  };
+  auto step_bf16 = [&](auto first, int kt, const Tile& nt, int nkt, bool has_next) __attribute__((always_inline)) {
+    constexpr bool kFirst = decltype(first)::value;
+    const Geo g = geo(lane_opaque());
+    const uint8_t* st = lds + (s & 1) * Y::kStage;
+    const uint8_t* stn = lds + ((s & 1) ^ 1) * Y::kStage;
+    Dma d;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      const int c = n >> 1;
+      if ((n & 1) == 0 && c < 3) load_raw(g, st, c + 1);
+      if (n == 1) {
+        d = dma_setup(g, nt, nkt, has_next, lds0 + (unsigned)(((s & 1) ^ 1) * Y::kStage));
+        dma_sf(d);
+      }
+      if (n >= 1 && n <= 3) {
+        constexpr int kPer = (Y::kDma + 2) / 3;
+#pragma unroll
+        for (int q = 0; q < kPer; ++q)
+          if ((n - 1) * kPer + q < Y::kDma) dma_ab(d, (n - 1) * kPer + q);
+      }
+      if (n < 7) {
+        if (((n + 1) & 1) == 0) scales(g, (n + 1) >> 1);
+        convert(n + 1);
+      } else {
+        // the next step's first slice (its inputs were read after B')
+        scales(g, 0);
+        convert(0);
+      }
+#pragma unroll
+      for (int i = 0; i < kTM; ++i)
+#pragma unroll
+        for (int jj = 0; jj < kTN; ++jj)
+          acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bb[n & 1][jj], ab[n & 1][i],
+                                                               (kFirst && n == 0) ? zero16 : acc[i][jj], 0, 0, 0);
+      // interleave: each MFMA followed by up to 3 VALU ops; the chunk's
+      // fragment reads go out one after each of the first MFMAs
+#pragma unroll
+      for (int k = 0; k < kTM * kTN; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+        if (k < kTM + kTN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (n == 0) barrier();  // B
+      if (n == 6) {
+        wait_vm<0>();  // this wave's DMA of the next step (and anything older)
+        barrier();     // B'
+        load_sf(g, stn, nkt);
+        load_raw(g, stn, 0);
+      }
+    }
+    // BN = 128: one batch of the previous tile's stores
+    if constexpr (Y::kTrickle) {
+      if (pend > 0) {
+        const StoreCtx x = store_ctx(ptile);
+        store_one(x, kBatches - pend);
+        --pend;
       }
     }
     ++s;
@@ -506,16 +568,27 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
     }
   };
 
+  if (my_tiles > 0) prime(0);
   for (int i = 0; i < my_tiles; ++i) {
     const int tn = t0 + (i + 1) * G;
     const bool more = i + 1 < my_tiles;
     const Tile nxt = more ? make_tile<kBM, BN>(p, tn) : cur;
-    if (p.ksteps == 1) {
-      step(std::true_type{}, 0, nxt, more);
+    if constexpr (MODE == kModeBf16) {
+      if (p.ksteps == 1) {
+        step_bf16(std::true_type{}, 0, nxt, 0, more);
+      } else {
+        step_bf16(std::true_type{}, 0, cur, 1, true);
+        for (int kt = 1; kt + 1 < p.ksteps; ++kt) step_bf16(std::false_type{}, kt, cur, kt + 1, true);
+        step_bf16(std::false_type{}, p.ksteps - 1, nxt, 0, more);
+      }
     } else {
-      step(std::true_type{}, 0, cur, true);
-      for (int kt = 1; kt + 1 < p.ksteps; ++kt) step(std::false_type{}, kt, cur, true);
-      step(std::false_type{}, p.ksteps - 1, nxt, more);
+      if (p.ksteps == 1) {
+        step(std::true_type{}, 0, nxt, more);
+      } else {
+        step(std::true_type{}, 0, cur, true);
+        for (int kt = 1; kt + 1 < p.ksteps; ++kt) step(std::false_type{}, kt, cur, true);
+        step(std::false_type{}, p.ksteps - 1, nxt, more);
+      }
     }
     tile_end();
     cur = nxt;
