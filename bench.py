@@ -213,8 +213,8 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this path runs on one GPU only; multi-GPU runs are not part of this build "
-              "(see DESIGN.md for how it would shard)", file=sys.stderr)
+        print("bench.py: runs on one GPU only (--gpus 1); several GPUs would each run this kernel "
+              "on their own share of C tiles, which this benchmark does not launch", file=sys.stderr)
         sys.exit(2)
 
     import torch

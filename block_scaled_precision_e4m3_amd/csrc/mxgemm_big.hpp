@@ -54,8 +54,12 @@ struct Layout {
   static constexpr bool kTrickle = BN == 128;        // C stores spread over the next tile
   // BN = 256: per-wave LDS area where the epilogue transposes one 32x32 fp32
   // block (rows padded to 36 floats) so its stores write whole 128-byte lines
+  // The same area is where the scale DMA of waves that load no atoms
+  // (sf = 32: waves 2 and 3) writes its zeros: every wave issues the same
+  // instructions, so a step stays one branch-free block the scheduler can
+  // interleave.  The area is idle during the K loop.
   static constexpr int kEpiRow = 36;
-  static constexpr int kEpiBytes = kTrickle ? 0 : 4 * 32 * kEpiRow * 4;
+  static constexpr int kEpiBytes = kTrickle ? 2 * 1024 : 4 * 32 * kEpiRow * 4;
 };
 
 __device__ __forceinline__ uint4 lds16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
@@ -129,7 +133,9 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   // resources differ.  SF: sf=32 -> waves 0 and 1 load the A and B atoms of
   // both 128-row groups (lanes 0-31 group 0, 32-63 group 1); sf=16 -> waves
   // 0,1 (A,B) load row group 0's two atoms, waves 2,3 row group 1's.  Groups
-  // past the tile (B with BN = 128) or past the matrix read as zero.
+  // past the tile (B with BN = 128) or past the matrix read as zero.  With
+  // sf=32, waves 2 and 3 issue the same instruction on an empty resource into
+  // a scratch kilobyte of the epilogue area (no branch in the step).
   constexpr unsigned kOob = 0x80000000u;
   const bool sf_wave = NSF == 2 || wave < 2;
   const bool sf_is_b = (wave & 1) != 0;
@@ -149,7 +155,7 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
     const int mnb = sf_is_b ? p.MNbB : p.MNbA;
     const int g0 = mn0 >> 7;
     const int tile_groups = sf_is_b ? BN / 128 : 2;
-    const unsigned nrec = live ? (unsigned)min(tile_groups, mnb - g0) * (unsigned)p.Kg * 512u : 0u;
+    const unsigned nrec = ((int)live & (int)sf_wave) ? (unsigned)min(tile_groups, mnb - g0) * (unsigned)p.Kg * 512u : 0u;
     d.rs = make_rsrc((sf_is_b ? p.SFB : p.SFA) + ((int64_t)T.l * mnb + g0) * p.Kg * 512, nrec);
     const int kg = NSF * kt + g.sf_j;
     d.sf_voff = kg < p.Kg ? (unsigned)(g.sf_rg * p.Kg + kg) * 512u + g.sf_lane : kOob;
@@ -165,11 +171,11 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
     const unsigned dst = d.dst + (q >= 8 ? (unsigned)Y::kOffB : 0u) + (unsigned)(wave + 4 * qq) * 1024u;
     dma16_at(q >= 8 ? d.rb : d.ra, voff, dst);
   };
+  const unsigned sf_dummy = lds0 + 2u * (unsigned)Y::kStage + (unsigned)(wave & 1) * 1024u;
   auto dma_sf = [&](const Dma& d) {
-    if (sf_wave)
-      dma16_at(d.rs, d.sf_voff,
-               d.dst + (sf_is_b ? (unsigned)Y::kOffSFB : (unsigned)Y::kOffSFA) +
-                   (NSF == 1 ? 0u : (unsigned)(wave >> 1) * 1024u));
+    const unsigned dst = d.dst + (sf_is_b ? (unsigned)Y::kOffSFB : (unsigned)Y::kOffSFA) +
+                         (NSF == 1 ? 0u : (unsigned)(wave >> 1) * 1024u);
+    dma16_at(d.rs, d.sf_voff, sf_wave ? dst : sf_dummy);
   };
 
   v16f acc[kTM][kTN];   // written by each tile's first step before any read
