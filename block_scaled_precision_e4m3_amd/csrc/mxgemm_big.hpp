@@ -96,10 +96,14 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   // for every DMA in flight.
   struct Geo {
     int r, h;           // fragment row (lane % 32) and lane half
-    int xr;             // r & 7: the swizzle of every fragment row of this lane
+    int xr;             // the swizzle of every fragment row of this lane (see kchunk)
     int a_off, b_off;   // LDS offset of the lane's first A / B fragment row
     unsigned row_k;     // DMA: byte offset of the lane's row in its first 8-row group
     unsigned kchunk;    // DMA: the lane's 16-byte K chunk inside a 128-byte row
+    // LDS swizzle: 16-byte chunk c of tile row t sits at slot c ^ f(t), f(t) =
+    // (t & 7) ^ ((t >> 3) & 1).  The 16 rows that one pass of a 16-byte read
+    // serves then cover all 64 banks (rows t and t+1 differ in the 128-byte
+    // half, rows t and t+8 in f), and any 8 consecutive rows cover 32 banks.
     unsigned sf_lane;   // SF DMA: the lane's 16 bytes inside an atom
     int sf_rg, sf_j;    // SF DMA: 128-row group and atom along K of the lane's load
   };
@@ -107,12 +111,12 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
     Geo g;
     g.r = ln & 31;
     g.h = ln >> 5;
-    g.xr = ln & 7;
+    g.xr = (ln & 7) ^ ((ln >> 3) & 1);
     g.a_off = (128 * wm + g.r) * kBK;
     g.b_off = Y::kOffB + (kWN * wn + g.r) * kBK;
     const int dma_row = ln >> 3;
     g.row_k = (unsigned)(wave * 8 + dma_row) * (unsigned)p.K;
-    g.kchunk = (unsigned)(((ln & 7) ^ dma_row) << 4);
+    g.kchunk = (unsigned)(((ln & 7) ^ dma_row ^ (wave & 1)) << 4);
     g.sf_lane = 16u * (unsigned)(ln & 31);
     g.sf_rg = NSF == 1 ? (ln >> 5) : (wave >> 1);
     g.sf_j = NSF == 1 ? 0 : (ln >> 5);
@@ -339,7 +343,7 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
     barrier();
     const Geo g = geo(lane_opaque());
     const uint8_t* st = lds + (s & 1) * Y::kStage;
-    // fragment row i (32-row steps keep row & 7, so only the chunk is swizzled)
+    // fragment row i (32-row steps keep f, so only the chunk is swizzled)
     auto a_frag = [&](int i, int c) { return lds16(st + g.a_off + ((c ^ g.xr) << 4) + 4096 * i); };
     auto b_frag = [&](int i, int c) { return lds16(st + g.b_off + ((c ^ g.xr) << 4) + 4096 * i); };
 
@@ -451,7 +455,7 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
         sb[j][i] = sf_tail(lds4(st + Y::kOffSFB + (brg * NSF + j) * 512 + 16 * g.r + 4 * (bdw + i)), ga, p.Kb);
     }
   };
-  // chunk c's fragments (32-row steps keep row & 7, so only the chunk is swizzled)
+  // chunk c's fragments (32-row steps keep f, so only the chunk is swizzled)
   auto load_raw = [&](const Geo& g, const uint8_t* st, int c) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < kTM; ++i) ra[c & 1][i] = lds16(st + g.a_off + (((2 * c + g.h) ^ g.xr) << 4) + 4096 * i);
