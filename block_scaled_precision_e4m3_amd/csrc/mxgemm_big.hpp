@@ -55,11 +55,11 @@ struct Layout {
   // BN = 256: per-wave LDS area where the epilogue transposes one 32x32 fp32
   // block (rows padded to 36 floats) so its stores write whole 128-byte lines
   // The same area is where the scale DMA of waves that load no atoms
-  // (sf = 32: waves 2 and 3) writes its zeros: every wave issues the same
-  // instructions, so a step stays one branch-free block the scheduler can
-  // interleave.  The area is idle during the K loop.
+  // (sf = 32: waves 2 and 3) writes its zeros, each wave into its own part:
+  // every wave issues the same instructions, so a step stays one branch-free
+  // block the scheduler can interleave.
   static constexpr int kEpiRow = 36;
-  static constexpr int kEpiBytes = kTrickle ? 2 * 1024 : 4 * 32 * kEpiRow * 4;
+  static constexpr int kEpiBytes = kTrickle ? 4 * 1024 : 4 * 32 * kEpiRow * 4;
 };
 
 __device__ __forceinline__ uint4 lds16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
@@ -139,7 +139,7 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   // 0,1 (A,B) load row group 0's two atoms, waves 2,3 row group 1's.  Groups
   // past the tile (B with BN = 128) or past the matrix read as zero.  With
   // sf=32, waves 2 and 3 issue the same instruction on an empty resource into
-  // a scratch kilobyte of the epilogue area (no branch in the step).
+  // the wave's own kilobyte of the epilogue area (no branch in the step).
   constexpr unsigned kOob = 0x80000000u;
   const bool sf_wave = NSF == 2 || wave < 2;
   const bool sf_is_b = (wave & 1) != 0;
@@ -175,7 +175,10 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
     const unsigned dst = d.dst + (q >= 8 ? (unsigned)Y::kOffB : 0u) + (unsigned)(wave + 4 * qq) * 1024u;
     dma16_at(q >= 8 ? d.rb : d.ra, voff, dst);
   };
-  const unsigned sf_dummy = lds0 + 2u * (unsigned)Y::kStage + (unsigned)(wave & 1) * 1024u;
+  // each wave's own kilobyte, which only that wave's epilogue reuses (after
+  // the wave's DMA has been waited for)
+  const unsigned sf_dummy =
+      lds0 + 2u * (unsigned)Y::kStage + (unsigned)wave * (Y::kTrickle ? 1024u : (unsigned)(32 * Y::kEpiRow * 4));
   auto dma_sf = [&](const Dma& d) {
     const unsigned dst = d.dst + (sf_is_b ? (unsigned)Y::kOffSFB : (unsigned)Y::kOffSFA) +
                          (NSF == 1 ? 0u : (unsigned)(wave >> 1) * 1024u);
@@ -427,14 +430,16 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   };
 
   // --- bf16 datapath: steps pipelined across step boundaries -----------------
-  // The next step's scale dwords and first 32-K chunk are read, and its first
-  // MFMA slice converted, while the current step's last slice runs, so a step
-  // starts issuing MFMAs at once.  Two barriers per step, each placed right
-  // after a slice's MFMAs are queued so its wait overlaps them:
-  //   B  (after slice 0): every wave has finished the previous step, so the
-  //      other stage is free and the DMA of the next step goes out (slices 1-3);
-  //   B' (after slice 6): every wave's DMA of the next step has landed (each
-  //      wave first waits for its own), so the next stage may be read.
+  // The next step's scale dwords and first two 32-K chunks are read, and its
+  // first MFMA slice converted, while the current step's last slices run, so
+  // a step starts issuing MFMAs at once.  A wave reads a stage for the last
+  // time in slice 3 of the stage's step (chunk 3), and uses that data before
+  // slice 7.  One barrier per step, B' (after slice 6, placed right after
+  // the slice's MFMAs are queued so its wait overlaps them): every wave's DMA
+  // of the next step has landed (each wave first waits for its own), so the
+  // next stage may be read; and every wave is past its last read of the
+  // current stage, so the DMA of the step after next may go into it during
+  // the next step (it goes out in slices 1-3).
   unsigned sa[NSF][kTM], sb[NSF][kTN];  // scale dwords of the current step
   uint4 ra[2][kTM], rb[2][kTN];         // raw 16-byte fragments, by chunk parity
   v8bf ab[2][kTM], bb[2][kTN];          // converted operands, by slice parity
@@ -490,6 +495,7 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
       const Geo g = geo(lane_opaque());
       load_sf(g, lds, kt0);
       load_raw(g, lds, 0);
+      load_raw(g, lds, 1);
       scales(g, 0);
       convert(0);
     }
@@ -502,8 +508,11 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
     Dma d;
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
-      const int c = n >> 1;
-      if ((n & 1) == 0 && c < 3) load_raw(g, st, c + 1);
+      // chunk j is read two slices before its first conversion (slice 2j - 1):
+      // chunks 2 and 3 here, chunks 0 and 1 of the next step after B'
+      if (n == 1) load_raw(g, st, 2);
+      if (n == 3) load_raw(g, st, 3);
+      // the next step's DMA, spread over slices 1-3
       if (n == 1) {
         d = dma_setup(g, nt, nkt, has_next, lds0 + (unsigned)(((s & 1) ^ 1) * Y::kStage));
         dma_sf(d);
@@ -537,12 +546,12 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
         if (k < kTM + kTN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (n == 0) barrier();  // B
       if (n == 6) {
         wait_vm<0>();  // this wave's DMA of the next step (and anything older)
         barrier();     // B'
         load_sf(g, stn, nkt);
         load_raw(g, stn, 0);
+        load_raw(g, stn, 1);
       }
     }
     // BN = 128: one batch of the previous tile's stores
