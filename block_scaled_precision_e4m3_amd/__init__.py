@@ -30,7 +30,6 @@ MXG_FLAG_AMAX_ACCUMULATE = 1
 MXG_FLAG_FP8_MFMA = 2
 MXG_FLAG_TILE_128 = 4
 MXG_FLAG_TILE_256 = 8
-MXG_FLAG_TILE_256X128 = 16
 
 MXG_OK = 0
 MXG_ERR_NULL = -1
@@ -224,6 +223,6 @@ __all__ = [
     "mxgemm_amax", "mxgemm_amax_ex", "mxgemm_amax_reset", "mxgemm_check_support", "mxgemm_sf_bytes",
     "mxgemm_launch_config", "mxgemm_strerror", "gemm_amax", "LIB_PATH", "EXPORTED",
     "MXG_FMT_E4M3", "MXG_FMT_E5M2", "MXG_FLAG_AMAX_ACCUMULATE", "MXG_FLAG_FP8_MFMA", "MXG_FLAG_TILE_128",
-    "MXG_FLAG_TILE_256", "MXG_FLAG_TILE_256X128", "MxgemmError", "MxgemmValueError",
+    "MXG_FLAG_TILE_256", "MxgemmError", "MxgemmValueError",
     "MxgemmRuntimeError",
 ]

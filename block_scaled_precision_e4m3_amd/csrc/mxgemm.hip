@@ -84,19 +84,16 @@ bool on_device(const void* p, int dev) {
   return attr.device == dev;
 }
 
-// Three tile shapes.  128x128: two workgroups per CU, 4 waves of 64x64.
+// Two tile shapes.  128x128: two workgroups per CU, 4 waves of 64x64.
 // 256x256: one workgroup per CU, 4 waves of 128x128; half the L2->LDS bytes
-// per flop of 128x128, but a tile's C is stored in one burst at its end.
-// 256x128: one workgroup per CU, 4 waves of 128x64; its C stores are spread
-// over the next tile (measured slower than 256x256 on the large workloads; kept
-// for tests and tuning).  The automatic choice takes 256x256 when its tiles
+// per flop of 128x128.  The automatic choice takes 256x256 when its tiles
 // fill the CUs at least as evenly as 128x128 tiles fill two workgroups per CU
 // (and K > 0), otherwise 128x128.
 struct Config {
-  int kind;  // 0: 128x128, 1: 256x256, 2: 256x128
+  int kind;  // 0: 128x128, 1: 256x256
   int tile_m, tile_n, per_cu;
 };
-constexpr Config kSmall = {0, 128, 128, 2}, kBig = {1, 256, 256, 1}, kMid = {2, 256, 128, 1};
+constexpr Config kSmall = {0, 128, 128, 2}, kBig = {1, 256, 256, 1};
 
 double fill(int64_t tiles, int64_t slots) {
   if (tiles <= 0) return 0.0;
@@ -117,9 +114,7 @@ hipError_t launch_mode(const mxg::Params& p, int sf, int fa, int fb, int64_t gri
 #define MXG_LAUNCH(SF, FA, FB)                                                                         \
   do {                                                                                                 \
     if constexpr (KIND == 1)                                                                           \
-      hipLaunchKernelGGL((mxg::big::mxgemm_amax_big_kernel<SF, FA, FB, MODE, 256>), g, b, 0, s, p);    \
-    else if constexpr (KIND == 2)                                                                      \
-      hipLaunchKernelGGL((mxg::big::mxgemm_amax_big_kernel<SF, FA, FB, MODE, 128>), g, b, 0, s, p);    \
+      hipLaunchKernelGGL((mxg::big::mxgemm_amax_big_kernel<SF, FA, FB, MODE>), g, b, 0, s, p);         \
     else                                                                                               \
       hipLaunchKernelGGL((mxg::mxgemm_amax_kernel<SF, FA, FB, MODE>), g, b, 0, s, p);                  \
   } while (0)
@@ -194,9 +189,8 @@ int mxgemm_amax_ex(const void* A, const void* B, const uint8_t* SFA, const uint8
                    unsigned flags, void* stream) {
   int st = check_sizes(M, N, K, L, sf_vec_size, a_fmt, b_fmt);
   if (st != MXG_OK) return st;
-  const unsigned tile_flags = flags & (MXG_FLAG_TILE_128 | MXG_FLAG_TILE_256 | MXG_FLAG_TILE_256X128);
-  if (flags & ~(unsigned)(MXG_FLAG_AMAX_ACCUMULATE | MXG_FLAG_FP8_MFMA | MXG_FLAG_TILE_128 | MXG_FLAG_TILE_256 |
-                          MXG_FLAG_TILE_256X128))
+  const unsigned tile_flags = flags & (MXG_FLAG_TILE_128 | MXG_FLAG_TILE_256);
+  if (flags & ~(unsigned)(MXG_FLAG_AMAX_ACCUMULATE | MXG_FLAG_FP8_MFMA | MXG_FLAG_TILE_128 | MXG_FLAG_TILE_256))
     return MXG_ERR_FLAGS;
   if (tile_flags & (tile_flags - 1)) return MXG_ERR_FLAGS;  // more than one tile flag
   // A, B and the scales are read only when there is a non-empty C and a non-empty K
@@ -239,7 +233,6 @@ int mxgemm_amax_ex(const void* A, const void* B, const uint8_t* SFA, const uint8
   Config cfg = choose(M, N, K, L, cus);
   if (flags & MXG_FLAG_TILE_128) cfg = kSmall;
   if ((flags & MXG_FLAG_TILE_256) && K > 0) cfg = kBig;
-  if ((flags & MXG_FLAG_TILE_256X128) && K > 0) cfg = kMid;
   p.tilesM = (int)cdiv(M, cfg.tile_m);
   p.tilesN = (int)cdiv(N, cfg.tile_n);
   p.ksteps = (int)cdiv(K, 128);
@@ -252,9 +245,6 @@ int mxgemm_amax_ex(const void* A, const void* B, const uint8_t* SFA, const uint8
   if (cfg.kind == 1)
     e = fp8 ? launch_mode<mxg::kModeFp8, 1>(p, sf_vec_size, a_fmt, b_fmt, grid, s)
             : launch_mode<mxg::kModeBf16, 1>(p, sf_vec_size, a_fmt, b_fmt, grid, s);
-  else if (cfg.kind == 2)
-    e = fp8 ? launch_mode<mxg::kModeFp8, 2>(p, sf_vec_size, a_fmt, b_fmt, grid, s)
-            : launch_mode<mxg::kModeBf16, 2>(p, sf_vec_size, a_fmt, b_fmt, grid, s);
   else
     e = fp8 ? launch_mode<mxg::kModeFp8, 0>(p, sf_vec_size, a_fmt, b_fmt, grid, s)
             : launch_mode<mxg::kModeBf16, 0>(p, sf_vec_size, a_fmt, b_fmt, grid, s);

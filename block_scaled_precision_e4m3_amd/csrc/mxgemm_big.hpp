@@ -1,27 +1,24 @@
-// One-workgroup-per-CU variants of the block-scaled FP8 GEMM + amax kernel
-// for gfx950: 256x256 and 256x128 C tiles.
+// One-workgroup-per-CU variant of the block-scaled FP8 GEMM + amax kernel
+// for gfx950: 256x256 C tiles.
 //
 // Same operation, operand layouts, scale handling and amax as the 128x128
 // kernel in mxgemm_kernel.hpp ("GEMM + Amax (SM100)", sections "Equations"
 // and "Shapes"); what changes is the shape of the work:
 //
-// * One workgroup per CU (the LDS ring takes up to 136 KB of the 160 KB) owns
-//   a 256 x BN tile; its 4 waves, one per SIMD, each hold a 128 x BN/2 block in
-//   4 x BN/64 MFMA accumulators.  Per 128-K step a CU moves 32 KB of A,
-//   BN*128 bytes of B and the scale atoms from L2.
-// * The K loop is one straight block per step: the next stage's DMA
-//   instructions go out a few at a time between the 32-K chunks' MFMAs, the
-//   next chunk's fragment reads are queued ahead, and each slice's conversions
-//   run under the previous slice's MFMAs (scheduling-group barriers pin the
-//   interleave), so one wave per SIMD keeps the matrix core fed.
-// * C stores.  BN = 256: the 256 accumulators of a wave take all the matrix-
-//   core registers, so a tile's C is stored at its end.  Every CU ends its
-//   tiles at the same time, so these stores arrive as bursts that are bound
-//   by HBM write bandwidth.  BN = 128: the 128 accumulators are copied to a
-//   second set at tile end and their 32 stores per lane go out 4 per step
-//   during the next tile, after the step's DMA, spreading the C traffic over
-//   the whole run (the vector-memory counter retires in issue order, so a
-//   wave waiting for its next DMA never waits for stores queued after it).
+// * One workgroup per CU (the LDS ring takes 132-136 KB of the 160 KB) owns a
+//   256 x 256 tile; its 4 waves, one per SIMD, each hold a 128 x 128 block in
+//   4 x 4 MFMA accumulators (all 256 matrix-core registers).  Per 128-K step
+//   a CU moves 64 KB of A and B and the scale atoms from L2.
+// * The K loop is one straight block per step: the next chunk's fragment
+//   reads are queued ahead, and each slice's conversions run under the
+//   previous slice's MFMAs (scheduling-group barriers pin the interleave), so
+//   one wave per SIMD keeps the matrix core fed.
+// * C stores.  A tile's C is stored at its end, transposed through LDS so
+//   that every store writes whole 128-byte lines.  Every CU ends its tiles at
+//   about the same time, so the stores drain slowly; the stage DMA is issued
+//   two steps ahead, before those stores, so that the next steps wait for
+//   their DMA only and the stores drain under their MFMAs (the vector-memory
+//   counter retires in issue order).
 //
 // bf16 datapath, per 32-K chunk c of a step: lane (r, h) reads the 16 bytes
 // K [32c + 16h, +16) of its row for each of its A and B fragments; bytes
@@ -38,28 +35,32 @@ namespace mxg {
 namespace big {
 
 constexpr int kThreads = 256;
-constexpr int kBM = 256, kBK = 128;
-constexpr int kTM = 4;  // 32-row MFMA blocks per wave (128 rows)
+constexpr int kBM = 256, kBN = 256, kBK = 128;
+constexpr int kTM = 4, kTN = 4;  // 32x32 MFMA blocks per wave (128 x 128)
+constexpr int kWN = kBN / 2;     // wave tile columns
+// bf16 datapath: a step's DMA of the next stage goes out over its slices
+// 1 .. kDmaSlices (spread so that the texture unit's queue does not back up
+// into instruction issue; done early enough to land before the barrier)
+constexpr int kDmaSlices = 3;
 
-template <int SF, int BN>
+template <int SF>
 struct Layout {
   static constexpr int NSF = SF == 32 ? 1 : 2;       // atoms per 128-row group per step
   static constexpr int kSF = 2 * NSF * 512;          // atom bytes per operand per stage
   static constexpr int kOffB = kBM * kBK;            // A tile: 256 rows x 128 bytes
-  static constexpr int kOffSFA = kOffB + BN * kBK;   // B tile: BN rows x 128 bytes
+  static constexpr int kOffSFA = kOffB + kBN * kBK;  // B tile: 256 rows x 128 bytes
   static constexpr int kOffSFB = kOffSFA + kSF;
   static constexpr int kStage = kOffSFB + kSF;
-  static constexpr int kTN = BN / 64;                // 32-column MFMA blocks per wave
-  static constexpr int kDma = (kBM + BN) / 32;       // A/B DMA instructions per wave per step
-  static constexpr bool kTrickle = BN == 128;        // C stores spread over the next tile
-  // BN = 256: per-wave LDS area where the epilogue transposes one 32x32 fp32
-  // block (rows padded to 36 floats) so its stores write whole 128-byte lines
-  // The same area is where the scale DMA of waves that load no atoms
-  // (sf = 32: waves 2 and 3) writes its zeros, each wave into its own part:
-  // every wave issues the same instructions, so a step stays one branch-free
-  // block the scheduler can interleave.
+  static constexpr int kDma = (kBM + kBN) / 32;      // A/B DMA instructions per wave per step
+  // Per-wave LDS area where the epilogue transposes one 32x32 fp32 block
+  // (rows padded to 36 floats) so its stores write whole 128-byte lines.  Its
+  // first kilobyte is where the scale DMA of a wave that loads no atoms
+  // (sf = 32: waves 2 and 3) writes its zeros: every wave issues the same
+  // instructions, so a step stays one branch-free block the scheduler can
+  // interleave.
   static constexpr int kEpiRow = 36;
-  static constexpr int kEpiBytes = kTrickle ? 4 * 1024 : 4 * 32 * kEpiRow * 4;
+  static constexpr int kEpiWave = 32 * kEpiRow * 4;
+  static constexpr int kEpiBytes = 4 * kEpiWave;
 };
 
 __device__ __forceinline__ uint4 lds16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
@@ -73,12 +74,10 @@ __device__ __forceinline__ unsigned sf_tail(unsigned d, int g, int Kb) {
   return (d & keep) | (0x7F7F7F7Fu & ~keep);
 }
 
-template <int SF, int FA, int FB, int MODE, int BN>
+template <int SF, int FA, int FB, int MODE>
 __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) {
-  using Y = Layout<SF, BN>;
+  using Y = Layout<SF>;
   constexpr int NSF = Y::NSF;
-  constexpr int kTN = Y::kTN;
-  constexpr int kWN = BN / 2;  // wave tile columns
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * Y::kStage + Y::kEpiBytes];
 
   const int lane = threadIdx.x & 63;
@@ -130,16 +129,16 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
 
   // --- DMA of one stage ------------------------------------------------------
   // A/B: wave w fills the 8-row groups w, w+4, ... of each tile, one
-  // instruction (1 KB) per group: 8 for A, BN/32 for B.  A lane's offset is
+  // instruction (1 KB) per group: 8 for A, 8 for B.  A lane's offset is
   // row*K + k; rows past the tile's valid rows fall past the resource
   // (num_records = valid rows * K) and K chunks past K get an offset of 2^31
   // or more: both read as zero.  A and B rows use the same offsets, only the
   // resources differ.  SF: sf=32 -> waves 0 and 1 load the A and B atoms of
   // both 128-row groups (lanes 0-31 group 0, 32-63 group 1); sf=16 -> waves
   // 0,1 (A,B) load row group 0's two atoms, waves 2,3 row group 1's.  Groups
-  // past the tile (B with BN = 128) or past the matrix read as zero.  With
-  // sf=32, waves 2 and 3 issue the same instruction on an empty resource into
-  // the wave's own kilobyte of the epilogue area (no branch in the step).
+  // past the matrix read as zero.  With sf=32, waves 2 and 3 issue the same
+  // instruction on an empty resource into the wave's own kilobyte of the
+  // epilogue area (no branch in the step).
   constexpr unsigned kOob = 0x80000000u;
   const bool sf_wave = NSF == 2 || wave < 2;
   const bool sf_is_b = (wave & 1) != 0;
@@ -158,8 +157,7 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
     const int mn0 = sf_is_b ? T.n0 : T.m0;
     const int mnb = sf_is_b ? p.MNbB : p.MNbA;
     const int g0 = mn0 >> 7;
-    const int tile_groups = sf_is_b ? BN / 128 : 2;
-    const unsigned nrec = ((int)live & (int)sf_wave) ? (unsigned)min(tile_groups, mnb - g0) * (unsigned)p.Kg * 512u : 0u;
+    const unsigned nrec = ((int)live & (int)sf_wave) ? (unsigned)min(2, mnb - g0) * (unsigned)p.Kg * 512u : 0u;
     d.rs = make_rsrc((sf_is_b ? p.SFB : p.SFA) + ((int64_t)T.l * mnb + g0) * p.Kg * 512, nrec);
     const int kg = NSF * kt + g.sf_j;
     d.sf_voff = kg < p.Kg ? (unsigned)(g.sf_rg * p.Kg + kg) * 512u + g.sf_lane : kOob;
@@ -177,16 +175,14 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   };
   // each wave's own kilobyte, which only that wave's epilogue reuses (after
   // the wave's DMA has been waited for)
-  const unsigned sf_dummy =
-      lds0 + 2u * (unsigned)Y::kStage + (unsigned)wave * (Y::kTrickle ? 1024u : (unsigned)(32 * Y::kEpiRow * 4));
+  const unsigned sf_dummy = lds0 + 2u * (unsigned)Y::kStage + (unsigned)wave * (unsigned)Y::kEpiWave;
   auto dma_sf = [&](const Dma& d) {
     const unsigned dst = d.dst + (sf_is_b ? (unsigned)Y::kOffSFB : (unsigned)Y::kOffSFA) +
                          (NSF == 1 ? 0u : (unsigned)(wave >> 1) * 1024u);
     dma16_at(d.rs, d.sf_voff, sf_wave ? dst : sf_dummy);
   };
 
-  v16f acc[kTM][kTN];   // written by each tile's first step before any read
-  v16f prev[kTM][kTN];  // BN = 128: the previous tile, stored during this one
+  v16f acc[kTM][kTN];  // written by each tile's first step before any read
   const v16f zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   unsigned lmax = 0u;
 
@@ -198,36 +194,19 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   // values into the lane's amax.
   struct StoreCtx {
     __amdgpu_buffer_rsrc_t rc;
-    unsigned c_bytes, vbase;
-    int mrow, ncol, mvalid, nvalid, n0;
+    unsigned c_bytes;
+    int mvalid, nvalid, n0;
   };
   auto store_ctx = [&](const Tile& T) {
     StoreCtx x;
-    const int ln = lane_opaque();
     x.c_bytes = (unsigned)T.mvalid * (unsigned)p.N * 4u;
     x.rc = make_rsrc(p.C + ((int64_t)T.l * p.M + T.m0) * p.N, x.c_bytes);
-    x.mrow = 128 * wm + (ln & 31);
-    x.ncol = kWN * wn + 4 * (ln >> 5);
-    x.vbase = ((unsigned)x.mrow * (unsigned)p.N + (unsigned)(T.n0 + x.ncol)) * 4u;
     x.mvalid = T.mvalid;
     x.nvalid = T.nvalid;
     x.n0 = T.n0;
     return x;
   };
-  auto store4 = [&](const StoreCtx& x, const v16f& blk, int i, int j, int q) __attribute__((always_inline)) {
-    const bool ok = (x.mrow + 32 * i < x.mvalid) & (x.ncol + 32 * j + 8 * q < x.nvalid);
-    v4f v;
-    v[0] = blk[4 * q];
-    v[1] = blk[4 * q + 1];
-    v[2] = blk[4 * q + 2];
-    v[3] = blk[4 * q + 3];
-    const unsigned off = x.vbase + (unsigned)(32 * i) * (unsigned)p.N * 4u + (unsigned)((32 * j + 8 * q) * 4);
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), x.rc, ok ? (int)off : (int)x.c_bytes, 0, 0);
-    const unsigned m4 = max(max(__float_as_uint(v[0]) & 0x7FFFFFFFu, __float_as_uint(v[1]) & 0x7FFFFFFFu),
-                            max(__float_as_uint(v[2]) & 0x7FFFFFFFu, __float_as_uint(v[3]) & 0x7FFFFFFFu));
-    lmax = max(lmax, m4 & (0u - (unsigned)ok));  // arithmetic mask: no branch
-  };
-  // BN = 256: every block of `acc` at tile end.  A block goes through the
+  // Every block of `acc` at tile end.  A block goes through the
   // wave's LDS area: lane (r, h) writes its row r, columns 8q + 4h straight
   // from the accumulation registers; lane L then reads row 8k + L/8, columns
   // 4(L%8) .. +4, so each of the block's 4 stores covers 8 rows x 128
@@ -288,40 +267,11 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
       }
     }
   };
-  // BN = 128: batch b (4 stores) of `prev`; b is a compile-time constant so
-  // the registers are named statically
-  constexpr int kBatch = 4;
-  constexpr int kBatches = kTM * kTN * 4 / kBatch;
-  auto store_batch = [&](const StoreCtx& x, auto bc) __attribute__((always_inline)) {
-    constexpr int b = decltype(bc)::value;
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int idx = b * kBatch + u;
-      const int i = idx / (kTN * 4), j = (idx / 4) % kTN, q = idx % 4;
-      store4(x, prev[i][j], i, j, q);
-    }
-  };
-  auto store_one = [&](const StoreCtx& x, int b) __attribute__((always_inline)) {
-    static_assert(!Y::kTrickle || kBatches == 8, "batch dispatch below is written for 8 batches");
-    switch (b) {
-      case 0: store_batch(x, std::integral_constant<int, 0>{}); break;
-      case 1: store_batch(x, std::integral_constant<int, 1>{}); break;
-      case 2: store_batch(x, std::integral_constant<int, 2>{}); break;
-      case 3: store_batch(x, std::integral_constant<int, 3>{}); break;
-      case 4: store_batch(x, std::integral_constant<int, 4>{}); break;
-      case 5: store_batch(x, std::integral_constant<int, 5>{}); break;
-      case 6: store_batch(x, std::integral_constant<int, 6>{}); break;
-      default: store_batch(x, std::integral_constant<int, 7>{}); break;
-    }
-  };
-
   Tile cur = {0, 0, 0, 0, 0};
-  Tile ptile = {0, 0, 0, 0, 0};  // BN = 128: the tile held in `prev`
-  int pend = 0;                  // BN = 128: batches of `prev` not yet stored
-  int after_dma = 0;             // store instructions queued after the last DMA
+  int after_dma = 0;             // FP8 datapath: store instructions queued after the last DMA
   int s = 0;                     // global step index: selects the ring stage
   if (my_tiles > 0) {
-    cur = make_tile<kBM, BN>(p, t0);
+    cur = make_tile<kBM, kBN>(p, t0);
     const Dma d0 = dma_setup(geo(lane), cur, 0, true, lds0);
     dma_sf(d0);
 #pragma unroll
@@ -339,9 +289,7 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
     // queued after it); the barrier extends that to every wave and frees the
     // other stage
     if (after_dma == 0) wait_vm<0>();
-    else if (after_dma == kBatch) wait_vm<kBatch>();
-    else if (after_dma <= 63) wait_vm<63>();
-    else wait_vm<0>();
+    else wait_vm<63>();
     after_dma = 0;
     barrier();
     const Geo g = geo(lane_opaque());
@@ -415,39 +363,29 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
         }
       }
     }
-
-    // BN = 128: one batch of the previous tile's stores, after all of this
-    // step's DMA
-    if constexpr (Y::kTrickle) {
-      if (pend > 0) {
-        const StoreCtx x = store_ctx(ptile);
-        store_one(x, kBatches - pend);
-        --pend;
-        after_dma += kBatch;
-      }
-    }
     ++s;
   };
 
   // --- bf16 datapath: steps pipelined across step boundaries -----------------
-  // The next step's scale dwords and first two 32-K chunks are read, and its
-  // first MFMA slice converted, while the current step's last slices run, so
-  // a step starts issuing MFMAs at once.  A wave reads a stage for the last
-  // time in slice 3 of the stage's step (chunk 3), and uses that data before
-  // slice 7.  One barrier per step, B' (after slice 6, placed right after
-  // the slice's MFMAs are queued so its wait overlaps them): every wave's DMA
-  // of the next step has landed (each wave first waits for its own), so the
-  // next stage may be read; and every wave is past its last read of the
-  // current stage, so the DMA of the step after next may go into it during
-  // the next step (it goes out in slices 1-3).
+  // Global step s reads ring stage s & 1.  The next step's scale dwords and
+  // first 32-K chunk are read, and its first MFMA slice converted, while the
+  // current step's last slice runs, so a step issues MFMAs from its first
+  // cycle.  A wave reads a stage for the last time in slice 4 of the stage's
+  // step (chunk 3) and has used that data by the end of slice 6.  One
+  // barrier per step, B' (after slice 6, right after the slice's MFMAs are
+  // queued, so its wait overlaps them).  Past B':
+  //   * every wave's DMA of step s+1 has landed (each wave first waits for
+  //     its own), so stage (s+1) & 1 may be read;
+  //   * every wave is done with stage s & 1, so DMA into it may start: the
+  //     next step queues the DMA of step s+2 over its slices 1 .. kDmaSlices.
   unsigned sa[NSF][kTM], sb[NSF][kTN];  // scale dwords of the current step
   uint4 ra[2][kTM], rb[2][kTN];         // raw 16-byte fragments, by chunk parity
   v8bf ab[2][kTM], bb[2][kTN];          // converted operands, by slice parity
   float fa[kTM], fb[kTN];               // scale operands of the chunk being converted
   const int brg = (kWN * wn) >> 7, bdw = ((kWN * wn) >> 5) & 3;
-  // SF dwords of step kt from stage st: NSF atoms x (4 or kTN) fragment rows.
-  // A rows 128*wm + 32i + r: atom group wm, dword i; B rows kWN*wn + 32i + r:
-  // atom group (kWN*wn)/128, dword ((kWN*wn)/32)%4 + i.
+  // SF dwords of step kt from stage st: NSF atoms x 4 fragment rows per
+  // operand.  A rows 128*wm + 32i + r: atom group wm, dword i; B rows
+  // kWN*wn + 32i + r: atom group (kWN*wn)/128, dword ((kWN*wn)/32)%4 + i.
   auto load_sf = [&](const Geo& g, const uint8_t* st, int kt) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < NSF; ++j) {
@@ -487,38 +425,38 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
     for (int i = 0; i < kTN; ++i)
       bb[n & 1][i] = cvt8<FB>(t ? rb[c & 1][i].z : rb[c & 1][i].x, t ? rb[c & 1][i].w : rb[c & 1][i].y, fb[i]);
   };
-  // the first step's inputs (after its DMA, issued above, has landed everywhere)
-  auto prime = [&](int kt0) __attribute__((always_inline)) {
-    if constexpr (MODE == kModeBf16) {
-      wait_vm<0>();
-      barrier();
-      const Geo g = geo(lane_opaque());
-      load_sf(g, lds, kt0);
-      load_raw(g, lds, 0);
-      load_raw(g, lds, 1);
-      scales(g, 0);
-      convert(0);
-    }
+  // step 0's inputs (after its DMA, issued above, has landed everywhere)
+  auto prime = [&]() __attribute__((always_inline)) {
+    const Geo g = geo(lane_opaque());
+    wait_vm<0>();
+    barrier();
+    load_sf(g, lds, 0);
+    load_raw(g, lds, 0);
+    scales(g, 0);
+    convert(0);
   };
-  auto step_bf16 = [&](auto first, int kt, const Tile& nt, int nkt, bool has_next) __attribute__((always_inline)) {
+  // One K step of tile `cur`.  FIRST: the tile's first step (its first MFMA
+  // per accumulator takes a zero C operand).  (nt, nkt, has_next): step s+1,
+  // whose DMA this step queues (nkt is also the K step of the scale tail
+  // read at B').
+  auto step_bf16 = [&](auto first, const Tile& nt, int nkt, bool has_next) __attribute__((always_inline)) {
     constexpr bool kFirst = decltype(first)::value;
     const Geo g = geo(lane_opaque());
-    const uint8_t* st = lds + (s & 1) * Y::kStage;
     const uint8_t* stn = lds + ((s & 1) ^ 1) * Y::kStage;
+    const uint8_t* st = lds + (s & 1) * Y::kStage;
     Dma d;
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
-      // chunk j is read two slices before its first conversion (slice 2j - 1):
-      // chunks 2 and 3 here, chunks 0 and 1 of the next step after B'
-      if (n == 1) load_raw(g, st, 2);
-      if (n == 3) load_raw(g, st, 3);
-      // the next step's DMA, spread over slices 1-3
+      // chunk c+1 is read during slice 2c, a slice before its first
+      // conversion; chunk 0 of the next step after B'
+      if ((n & 1) == 0 && (n >> 1) < 3) load_raw(g, st, (n >> 1) + 1);
+      // the DMA of step s+1, spread over slices 1 .. kDmaSlices
       if (n == 1) {
         d = dma_setup(g, nt, nkt, has_next, lds0 + (unsigned)(((s & 1) ^ 1) * Y::kStage));
         dma_sf(d);
       }
-      if (n >= 1 && n <= 3) {
-        constexpr int kPer = (Y::kDma + 2) / 3;
+      if (n >= 1 && n <= kDmaSlices) {
+        constexpr int kPer = (Y::kDma + kDmaSlices - 1) / kDmaSlices;
 #pragma unroll
         for (int q = 0; q < kPer; ++q)
           if ((n - 1) * kPer + q < Y::kDma) dma_ab(d, (n - 1) * kPer + q);
@@ -547,77 +485,44 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
       }
       __builtin_amdgcn_sched_barrier(0);
       if (n == 6) {
-        wait_vm<0>();  // this wave's DMA of the next step (and anything older)
-        barrier();     // B'
+        // this wave's DMA of step s+1 (issued at the previous B') has landed
+        wait_vm<0>();
+        barrier();  // B'
         load_sf(g, stn, nkt);
         load_raw(g, stn, 0);
-        load_raw(g, stn, 1);
-      }
-    }
-    // BN = 128: one batch of the previous tile's stores
-    if constexpr (Y::kTrickle) {
-      if (pend > 0) {
-        const StoreCtx x = store_ctx(ptile);
-        store_one(x, kBatches - pend);
-        --pend;
       }
     }
     ++s;
   };
 
-  // tile end: BN = 256 stores `acc` now; BN = 128 finishes the previous
-  // tile's stores if K was too short to spread them, then moves `acc` to
-  // `prev` for the next tile to store
-  auto tile_end = [&]() __attribute__((always_inline)) {
-    if constexpr (Y::kTrickle) {
-      if (pend > 0) {
-        const StoreCtx x = store_ctx(ptile);
-        for (; pend > 0; --pend) store_one(x, kBatches - pend);
-        after_dma = 64;  // an unusual count: the next wait drains everything
-      }
-#pragma unroll
-      for (int i = 0; i < kTM; ++i)
-#pragma unroll
-        for (int j = 0; j < kTN; ++j) prev[i][j] = acc[i][j];
-      ptile = cur;
-      pend = kBatches;
-    } else {
-      store_all(store_ctx(cur));
-      after_dma = 63;  // 64 stores: waiting for 63 covers every earlier DMA
-    }
-  };
-
-  if (my_tiles > 0) prime(0);
+  const std::true_type yes;
+  const std::false_type no;
+  if constexpr (MODE == kModeBf16) {
+    if (my_tiles > 0) prime();
+  }
   for (int i = 0; i < my_tiles; ++i) {
-    const int tn = t0 + (i + 1) * G;
     const bool more = i + 1 < my_tiles;
-    const Tile nxt = more ? make_tile<kBM, BN>(p, tn) : cur;
+    const Tile nxt = more ? make_tile<kBM, kBN>(p, t0 + (i + 1) * G) : cur;
     if constexpr (MODE == kModeBf16) {
       if (p.ksteps == 1) {
-        step_bf16(std::true_type{}, 0, nxt, 0, more);
+        step_bf16(yes, nxt, 0, more);
       } else {
-        step_bf16(std::true_type{}, 0, cur, 1, true);
-        for (int kt = 1; kt + 1 < p.ksteps; ++kt) step_bf16(std::false_type{}, kt, cur, kt + 1, true);
-        step_bf16(std::false_type{}, p.ksteps - 1, nxt, 0, more);
+        step_bf16(yes, cur, 1, true);
+        for (int kt = 1; kt + 1 < p.ksteps; ++kt) step_bf16(no, cur, kt + 1, true);
+        step_bf16(no, nxt, 0, more);
       }
     } else {
       if (p.ksteps == 1) {
-        step(std::true_type{}, 0, nxt, more);
+        step(yes, 0, nxt, more);
       } else {
-        step(std::true_type{}, 0, cur, true);
-        for (int kt = 1; kt + 1 < p.ksteps; ++kt) step(std::false_type{}, kt, cur, true);
-        step(std::false_type{}, p.ksteps - 1, nxt, more);
+        step(yes, 0, cur, true);
+        for (int kt = 1; kt + 1 < p.ksteps; ++kt) step(no, kt, cur, true);
+        step(no, p.ksteps - 1, nxt, more);
       }
     }
-    tile_end();
+    store_all(store_ctx(cur));
+    after_dma = 63;  // FP8 datapath: 64 stores; waiting for 63 covers every earlier DMA
     cur = nxt;
-  }
-  if constexpr (Y::kTrickle) {
-    // the last tile's stores
-    if (pend > 0) {
-      const StoreCtx x = store_ctx(ptile);
-      for (; pend > 0; --pend) store_one(x, kBatches - pend);
-    }
   }
   // no DMA may still be writing this workgroup's LDS when it exits
   wait_vm<0>();

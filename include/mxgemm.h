@@ -95,12 +95,9 @@ enum {
   /* Force the tile configuration instead of the automatic choice (for tests
      and tuning; results agree within the tolerance either way).  TILE_128:
      128x128 tiles, two workgroups per CU.  TILE_256: 256x256 tiles, one
-     workgroup per CU.  TILE_256X128: 256x128 tiles, one workgroup per CU.
-     The last two are ignored when K == 0.  Setting more than one is an
-     error. */
+     workgroup per CU; ignored when K == 0.  Setting both is an error. */
   MXG_FLAG_TILE_128 = 4u,
-  MXG_FLAG_TILE_256 = 8u,
-  MXG_FLAG_TILE_256X128 = 16u
+  MXG_FLAG_TILE_256 = 8u
 };
 
 /*
@@ -133,7 +130,7 @@ int mxgemm_amax(const void* A, const void* B, const uint8_t* SFA, const uint8_t*
  * mxgemm_amax; MXG_FLAG_AMAX_ACCUMULATE skips the clearing kernel and
  * max-reduces into the existing Amax (queues the GEMM kernel only);
  * MXG_FLAG_FP8_MFMA selects the reduced-precision FP8 matrix path;
- * MXG_FLAG_TILE_128 / _256 / _256X128 force a tile configuration.
+ * MXG_FLAG_TILE_128 / _256 force a tile configuration.
  * Returns MXG_ERR_FLAGS for unknown bits or more than one tile flag.
  *
  * Exactness of the default path: every dequantised element is exact when

@@ -91,7 +91,7 @@ def test_errors_before_device_work(lib):
     assert f(*([good + 8] + args[1:]), *dims, 32, 0, 0, 0, None) == lib.MXG_ERR_ALIGN
     assert f(*(args[:4] + [good + 4] + args[5:]), *dims, 32, 0, 0, 0, None) == lib.MXG_ERR_ALIGN
     assert f(*args, *dims, 32, 0, 0, 32, None) == lib.MXG_ERR_FLAGS
-    assert f(*args, *dims, 32, 0, 0, 24, None) == lib.MXG_ERR_FLAGS   # two tile flags
+    assert f(*args, *dims, 32, 0, 0, 16, None) == lib.MXG_ERR_FLAGS   # unknown bit
     assert f(*args, *dims, 32, 0, 0, 12, None) == lib.MXG_ERR_FLAGS   # both tile flags
     assert f(*args, 256, 256, 256, 1, 64, 0, 0, 0, None) == lib.MXG_ERR_SFVEC
     assert f(*args, 256, 256, 256, 1, 32, 0, 9, 0, None) == lib.MXG_ERR_FMT
