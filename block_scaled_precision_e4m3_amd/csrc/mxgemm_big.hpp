@@ -409,11 +409,11 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   // 2(c&1)+h of atom c>>1
   auto scales = [&](const Geo& g, int c) __attribute__((always_inline)) {
     const int j = SF == 32 ? 0 : (c >> 1);
-    const int sh = SF == 32 ? 8 * c : 8 * (2 * (c & 1) + g.h);
+    const unsigned k = SF == 32 ? (unsigned)c : (unsigned)(2 * (c & 1) + g.h);
 #pragma unroll
-    for (int i = 0; i < kTM; ++i) fa[i] = e8m0_to_f32((sa[j][i] >> sh) & 0xFFu);
+    for (int i = 0; i < kTM; ++i) fa[i] = e8m0_byte_operand(sa[j][i], k);
 #pragma unroll
-    for (int i = 0; i < kTN; ++i) fb[i] = e8m0_to_f32((sb[j][i] >> sh) & 0xFFu);
+    for (int i = 0; i < kTN; ++i) fb[i] = e8m0_byte_operand(sb[j][i], k);
   };
   // slice n = chunk n/2, bytes 0..7 (even n) or 8..15 (odd n) of each fragment
   auto convert = [&](int n) __attribute__((always_inline)) {

@@ -142,13 +142,20 @@ __device__ __forceinline__ void wait_vm() {
 // reaches the next barrier.
 __device__ __forceinline__ void barrier() { __builtin_amdgcn_s_barrier(); }
 
-// E8M0 byte b (low 8 bits) -> the f32 scale operand of the scaled
-// conversions v_cvt_scalef32_pk_bf16_{fp8,bf8}.  Those instructions read only
-// the exponent field of their scale and give it E8M0 meaning: exponent e
-// scales by 2^(e-127), exponent 0 by 2^-127 and exponent 255 makes every
-// result NaN (measured on MI355X for all 256 bytes, mantissa bits ignored).
-// So the byte moved into the exponent field is the operand: one shift.
-__device__ __forceinline__ float e8m0_to_f32(unsigned b) { return __uint_as_float(b << 23); }
+// E8M0 scale bytes as the f32 scale operand of the scaled conversions
+// v_cvt_scalef32_pk_bf16_{fp8,bf8}.  Those instructions read only the
+// exponent field (bits 23..30) of their scale and give it E8M0 meaning:
+// exponent e scales by 2^(e-127), exponent 0 by 2^-127 and exponent 255 makes
+// every result NaN (measured on MI355X for all 256 bytes).  The sign and
+// mantissa bits are ignored: results are bitwise equal for every exponent,
+// 40 sign/mantissa patterns, all 256 codes, both halves, E4M3 and E5M2.  So
+// byte k (0..3) of a dword w becomes the operand by rotating w until bits
+// 8k..8k+7 sit on the exponent field; the neighbouring bytes left in the
+// other bits do no harm.  One v_alignbit, with a shift that may differ per
+// lane.
+__device__ __forceinline__ float e8m0_byte_operand(unsigned w, unsigned k) {
+  return __uint_as_float(__builtin_amdgcn_alignbit(w, w, (8u * k + 9u) & 31u));
+}
 
 template <int OPSEL, int FA, int FB>
 __device__ __forceinline__ v16f mfma_f8(const v8i& b, const v8i& a, const v16f& c, unsigned sb, unsigned sa) {

@@ -183,18 +183,16 @@ __device__ __forceinline__ void compute_slice(v16f (&acc)[kTM][kTN], const uint8
     // scales: sf=32 -> the lane's 32 K are block blk+h; sf=16 -> blocks 2h
     // (bytes 0..15) and 2h+1 (bytes 16..31) of the slice's atom
     float sa0[kTM], sa1[kTM], sb0[kTN], sb1[kTN];
-    const int sh = (SF == 32) ? 8 * (blk + h) : 16 * h;
+    const unsigned k0 = (SF == 32) ? (unsigned)(blk + h) : 2u * (unsigned)h;  // byte of the first block
 #pragma unroll
     for (int i = 0; i < kTM; ++i) {
-      const unsigned d = sfa[i] >> sh;
-      sa0[i] = e8m0_to_f32(d & 0xFFu);
-      sa1[i] = (SF == 32) ? sa0[i] : e8m0_to_f32((d >> 8) & 0xFFu);
+      sa0[i] = e8m0_byte_operand(sfa[i], k0);
+      sa1[i] = (SF == 32) ? sa0[i] : e8m0_byte_operand(sfa[i], k0 + 1);
     }
 #pragma unroll
     for (int j = 0; j < kTN; ++j) {
-      const unsigned d = sfb[j] >> sh;
-      sb0[j] = e8m0_to_f32(d & 0xFFu);
-      sb1[j] = (SF == 32) ? sb0[j] : e8m0_to_f32((d >> 8) & 0xFFu);
+      sb0[j] = e8m0_byte_operand(sfb[j], k0);
+      sb1[j] = (SF == 32) ? sb0[j] : e8m0_byte_operand(sfb[j], k0 + 1);
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
