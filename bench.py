@@ -96,11 +96,11 @@ def _is_gemm(name):
     return "mxgemm_amax" in name and "reset" not in name
 
 
-def _per_dispatch(rows, kernel_substr, counter):
+def _per_dispatch(rows, kernel_substr, counter, kernel_name_exact=False):
     per = {}
     for r in rows:
         name = r["Kernel_Name"]
-        hit = _is_gemm(name) if kernel_substr == "gemm" else kernel_substr in name
+        hit = name == kernel_substr if kernel_name_exact else kernel_substr in name
         if hit and r["Counter_Name"] == counter:
             per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
     return list(per.values())
@@ -119,23 +119,27 @@ def rocprof_summary(d, workload, fp8_mfma, commands):
     stats = _csv_rows(os.path.join(d, "kt", "**", "*kernel_stats.csv"))
     out.append("kernel trace (--kernel-trace --stats):")
     avg_us = None
+    gemm_name, gemm_total = None, -1.0
     for r in stats:
         name = r["Name"]
         out.append(f"  {name[:100]:100s} calls {int(r['Calls']):5d}  avg {float(r['AverageNs']) / 1e3:10.2f} us  "
                    f"min {float(r['MinNs']) / 1e3:10.2f}  max {float(r['MaxNs']) / 1e3:10.2f}  "
                    f"{float(r['Percentage']):5.1f}%")
-        if _is_gemm(name):
+        # the GEMM kernel that ran the workload: the one with the largest total time
+        if _is_gemm(name) and float(r["TotalDurationNs"]) > gemm_total:
+            gemm_name, gemm_total = name, float(r["TotalDurationNs"])
             avg_us = float(r["AverageNs"]) / 1e3
     out.append("")
     fl = W.flops(M, N, K, L)
     if avg_us:
+        out.append(f"gemm_kernel: {gemm_name}")
         out.append(f"gemm_avg_duration_us: {avg_us:.2f}")
         out.append(f"gemm_tflops_at_avg_duration: {fl / (avg_us * 1e-6) / 1e12:.1f}")
     fetch = _csv_rows(os.path.join(d, "fetch", "**", "*counter_collection.csv"))
     write = _csv_rows(os.path.join(d, "write", "**", "*counter_collection.csv"))
-    if fetch and write:
-        gf = _per_dispatch(fetch, "gemm", "FETCH_SIZE")
-        gw = _per_dispatch(write, "gemm", "WRITE_SIZE")
+    if fetch and write and gemm_name:
+        gf = _per_dispatch(fetch, gemm_name, "FETCH_SIZE", kernel_name_exact=True)
+        gw = _per_dispatch(write, gemm_name, "WRITE_SIZE", kernel_name_exact=True)
         cf = _per_dispatch(fetch, "neg", "FETCH_SIZE")
         cw = _per_dispatch(write, "neg", "WRITE_SIZE")
         f_fac = COPY_PROBE_BYTES / (1024.0 * sum(cf) / len(cf))
@@ -192,6 +196,28 @@ def cpu_baseline(p, target_s=12.0):
     }
 
 
+def host_overhead(lib, A, B, SFA, SFB, C, Amax, stream_handle, a_fmt, b_fmt, sf, batches=5, calls=200):
+    """CPU time of one mxgemm_amax call through the C ABI: validation, the Amax clear and the kernel
+    launch, without waiting for the GPU.  A 128x128x128 problem over the workload's own buffers (every
+    workload is at least that large), called straight through ctypes with prepared integer arguments;
+    the mean over `batches` batches of `calls` calls, the queue drained between batches (untimed)."""
+    import torch
+    f = lib._lib.mxgemm_amax
+    args = (A.data_ptr(), B.data_ptr(), SFA.data_ptr(), SFB.data_ptr(), C.data_ptr(), Amax.data_ptr(),
+            128, 128, 128, 1, sf, a_fmt, b_fmt, stream_handle)
+    assert f(*args) == lib.MXG_OK
+    torch.cuda.synchronize()
+    total = 0.0
+    for _ in range(batches):
+        t0 = time.perf_counter()
+        for _ in range(calls):
+            f(*args)
+        total += time.perf_counter() - t0
+        torch.cuda.synchronize()
+    return {"us_per_call": round(total / (batches * calls) * 1e6, 2), "calls": batches * calls,
+            "shape": "128x128x128", "what": "mxgemm_amax via ctypes: validate, clear Amax, launch; no wait"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -200,6 +226,8 @@ def main():
     ap.add_argument("--workload", type=int, default=5)
     ap.add_argument("--fp8-mfma", action="store_true", help="time the reduced-precision FP8 MFMA path")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-host-overhead", action="store_true",
+                    help="skip the 1000 small calls that time the host side (keeps profiles to the workload)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the timed steps, run the copy kernel that calibrates the HBM byte counters")
     ap.add_argument("--rocprof-summary", metavar="DIR",
@@ -290,6 +318,8 @@ def main():
                      "algorithmic_bytes": abytes,
                      "algorithmic_GBps": round(abytes / (kernel_ms * 1e-3) / 1e9, 1)},
     }
+    if not args.no_host_overhead:
+        out["host_overhead"] = host_overhead(lib, A, B, SFA, SFB, C, Amax, sh, p["a_fmt"], p["b_fmt"], sf)
     if args.copy_probe:
         copy_probe()
     if not args.no_cpu_baseline:
