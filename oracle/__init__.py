@@ -19,6 +19,9 @@ in float64, where every decoded product is exact.  Modules:
                    arrays") into one scale per (row, K-block).
 * ``gemm_amax`` -- dequantisation, the fp64 contraction, the |A|.|B| bound
                    used by the tolerance, and the amax.
+* ``mx_quantize`` -- MX block quantisation of float32 data into codes and
+                   E8M0 scales in the atom layout (the step that produces
+                   the GEMM's inputs).
 
 Every function has a pin in ``tests/test_oracle_*.py``; see each module's
 header for which pin covers it.
@@ -28,9 +31,11 @@ from .codecs import decode, decode_e4m3, decode_e5m2, decode_e8m0, FMT_E4M3, FMT
 from .sf_atom import sf_physical_shape, sf_logical_shape, sf_logical_view, expand_scales
 from .gemm_amax import (dequantize, gemm_amax, gemm_amax_loops, gemm_rows, gemm_entries,
                         amax_of)
+from .mx_quantize import mx_quantize, block_max, block_exponent, encode_rne, place_scales
 
 __all__ = [
     "decode", "decode_e4m3", "decode_e5m2", "decode_e8m0", "FMT_E4M3", "FMT_E5M2",
     "sf_physical_shape", "sf_logical_shape", "sf_logical_view", "expand_scales",
     "dequantize", "gemm_amax", "gemm_amax_loops", "gemm_rows", "gemm_entries", "amax_of",
+    "mx_quantize", "block_max", "block_exponent", "encode_rne", "place_scales",
 ]
