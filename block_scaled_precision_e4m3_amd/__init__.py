@@ -42,7 +42,7 @@ MXG_ERR_LAUNCH = -7
 MXG_ERR_FLAGS = -8
 
 EXPORTED = ("mxgemm_amax", "mxgemm_amax_ex", "mxgemm_amax_reset", "mxgemm_check_support",
-            "mxgemm_sf_bytes", "mxgemm_launch_config", "mxgemm_strerror")
+            "mxgemm_sf_bytes", "mxgemm_launch_config", "mxgemm_strerror", "mxgemm_mx_quantize")
 
 
 class MxgemmError(Exception):
@@ -82,6 +82,8 @@ def _load():
     lib.mxgemm_launch_config.restype = ci
     lib.mxgemm_strerror.argtypes = [ci]
     lib.mxgemm_strerror.restype = ctypes.c_char_p
+    lib.mxgemm_mx_quantize.argtypes = [vp, vp, vp, i64, i64, i64, ci, ci, vp]
+    lib.mxgemm_mx_quantize.restype = ci
     return lib
 
 
@@ -219,9 +221,42 @@ def gemm_amax(a, b, sfa, sfb, c=None, amax=None, sf_vec_size=32, stream=None, ac
     return c, amax
 
 
+def mxgemm_mx_quantize(X, Q, SF, MN, K, L, sf_vec_size, fmt, stream=None):
+    """C-ABI mxgemm_mx_quantize on torch tensors or raw device addresses; raises on a nonzero status."""
+    st = _lib.mxgemm_mx_quantize(_ptr(X), _ptr(Q), _ptr(SF), MN, K, L, sf_vec_size, fmt, _stream(stream))
+    if st != MXG_OK:
+        _raise(st)
+
+
+def mx_quantize(x, sf_vec_size=32, fmt=MXG_FMT_E4M3, q=None, sf=None, stream=None):
+    """MX-quantise a contiguous float32 CUDA tensor x of shape (MN, K) or (L, MN, K).
+
+    Returns (q, sf): q uint8 codes of x's shape (view it as torch.float8_e4m3fn /
+    float8_e5m2 for gemm_amax) and sf, the physical atom-layout scale buffer
+    (L, ceil(MN/128), ceil(K/(4 sf)), 32, 4, 4) uint8, which gemm_amax accepts
+    as SFA / SFB.  Preallocated q / sf are used when given.
+    """
+    import torch
+    if x.dtype != torch.float32 or not x.is_contiguous() or x.dim() not in (2, 3):
+        raise MxgemmValueError(MXG_ERR_ALIGN, "x must be a contiguous float32 (MN, K) or (L, MN, K) tensor")
+    l, mn, k = (1,) + tuple(x.shape) if x.dim() == 2 else tuple(x.shape)
+    shape = (l, -(-mn // 128), -(-k // (4 * sf_vec_size)), 32, 4, 4)
+    if q is None:
+        q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if sf is None:
+        sf = torch.empty(shape, dtype=torch.uint8, device=x.device)
+    if q.numel() != x.numel() or not q.is_contiguous() or q.element_size() != 1:
+        raise MxgemmValueError(MXG_ERR_SHAPE, "q must be a contiguous one-byte tensor with x's element count")
+    if sf.numel() != 512 * shape[0] * shape[1] * shape[2] or not sf.is_contiguous():
+        raise MxgemmValueError(MXG_ERR_SHAPE, f"sf must be a contiguous buffer of {512 * shape[0] * shape[1] * shape[2]} bytes")
+    mxgemm_mx_quantize(x, q, sf, mn, k, l, sf_vec_size, fmt, stream)
+    return q, sf
+
+
 __all__ = [
     "mxgemm_amax", "mxgemm_amax_ex", "mxgemm_amax_reset", "mxgemm_check_support", "mxgemm_sf_bytes",
     "mxgemm_launch_config", "mxgemm_strerror", "gemm_amax", "LIB_PATH", "EXPORTED",
+    "mxgemm_mx_quantize", "mx_quantize",
     "MXG_FMT_E4M3", "MXG_FMT_E5M2", "MXG_FLAG_AMAX_ACCUMULATE", "MXG_FLAG_FP8_MFMA", "MXG_FLAG_TILE_128",
     "MXG_FLAG_TILE_256", "MxgemmError", "MxgemmValueError",
     "MxgemmRuntimeError",

@@ -5,11 +5,13 @@
 // caching, and errors"), the per-shape tile choice, and the launches.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <mutex>
 #include <stdlib.h>
 #include <string.h>
 
 #include "../../include/mxgemm.h"
+#include "mx_quantize.hpp"
 #include "mxgemm_big.hpp"
 #include "mxgemm_kernel.hpp"
 
@@ -139,6 +141,32 @@ int64_t grid_for(int64_t tiles, int cus, int occ) {
   return g;
 }
 
+// --- MX block quantisation ------------------------------------------------------
+
+// Size/format validation of mxgemm_mx_quantize (no HIP call).
+int check_quantize(int64_t MN, int64_t K, int64_t L, int sf, int fmt) {
+  if (MN < 0 || K < 0 || L < 0) return MXG_ERR_SHAPE;
+  if (sf != 16 && sf != 32) return MXG_ERR_SFVEC;
+  if (fmt != MXG_FMT_E4M3 && fmt != MXG_FMT_E5M2) return MXG_ERR_FMT;
+  if (!fits_i32(MN) || !fits_i32(L)) return MXG_ERR_SHAPE;
+  // an atom's 128 rows of float32 must be addressable with 32-bit buffer offsets
+  if (K >= (1LL << 23)) return MXG_ERR_SHAPE;
+  if (MN && K && L && (MN * K > (INT64_MAX / 8) / L)) return MXG_ERR_SHAPE;
+  if (L * cdiv(MN, 128) * cdiv(K, 4 * sf) > 0x7FFFFFFFLL) return MXG_ERR_SHAPE;
+  if (K % 16 != 0) return MXG_ERR_ALIGN;
+  return MXG_OK;
+}
+
+template <int SF>
+hipError_t launch_quantize(const mxg::quant::QParams& p, int fmt, int64_t grid, hipStream_t s) {
+  const dim3 g((unsigned)grid), b(mxg::quant::kThreads);
+  if (fmt == MXG_FMT_E4M3)
+    hipLaunchKernelGGL((mxg::quant::mx_quantize_kernel<SF, 0>), g, b, 0, s, p);
+  else
+    hipLaunchKernelGGL((mxg::quant::mx_quantize_kernel<SF, 1>), g, b, 0, s, p);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 extern "C" {
@@ -248,6 +276,34 @@ int mxgemm_amax_ex(const void* A, const void* B, const uint8_t* SFA, const uint8
   else
     e = fp8 ? launch_mode<mxg::kModeFp8, 0>(p, sf_vec_size, a_fmt, b_fmt, grid, s)
             : launch_mode<mxg::kModeBf16, 0>(p, sf_vec_size, a_fmt, b_fmt, grid, s);
+  return e == hipSuccess ? MXG_OK : MXG_ERR_LAUNCH;
+}
+
+int mxgemm_mx_quantize(const float* X, void* Q, uint8_t* SF, int64_t MN, int64_t K, int64_t L, int sf_vec_size,
+                       int fmt, void* stream) {
+  int st = check_quantize(MN, K, L, sf_vec_size, fmt);
+  if (st != MXG_OK) return st;
+  if (MN == 0 || K == 0 || L == 0) return MXG_OK;  // nothing to read or write
+  if (!X || !Q || !SF) return MXG_ERR_NULL;
+  if (!aligned16(X) || !aligned16(Q) || !aligned16(SF)) return MXG_ERR_ALIGN;
+  int dev = 0, cus = 0;
+  st = device_check(&dev, &cus);
+  if (st != MXG_OK) return st;
+  if (!on_device(X, dev) || !on_device(Q, dev) || !on_device(SF, dev)) return MXG_ERR_DEVICE;
+
+  mxg::quant::QParams p;
+  p.X = X;
+  p.Q = static_cast<uint8_t*>(Q);
+  p.SF = SF;
+  p.MN = (int)MN;
+  p.K = (int)K;
+  p.MNb = (int)cdiv(MN, 128);
+  p.Kg = (int)cdiv(K, 4 * sf_vec_size);
+  p.num_atoms = (int)(L * p.MNb * p.Kg);
+  // 256-thread workgroups, up to 8 per CU resident; each loops over atoms
+  const int64_t grid = std::min<int64_t>(p.num_atoms, 8LL * cus);
+  hipStream_t s = (hipStream_t)stream;
+  const hipError_t e = sf_vec_size == 32 ? launch_quantize<32>(p, fmt, grid, s) : launch_quantize<16>(p, fmt, grid, s);
   return e == hipSuccess ? MXG_OK : MXG_ERR_LAUNCH;
 }
 

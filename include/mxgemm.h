@@ -173,6 +173,38 @@ size_t mxgemm_sf_bytes(int64_t MN, int64_t K, int64_t L, int sf_vec_size);
 int mxgemm_launch_config(int64_t M, int64_t N, int64_t K, int64_t L, int sf_vec_size,
                          int* tile_m, int* tile_n, int64_t* grid);
 
+/*
+ * mxgemm_mx_quantize -- MX block quantisation of float32 data into the
+ * GEMM's input form: element codes plus E8M0 block scales in the physical
+ * atom layout ("GEMM + RoPE + MXFP8 Projection (SM100)", section
+ * "Equations": MXFP8 quantisation with an E8M0 scale per block of 32 and
+ * E4M3 data; E5M2 and blocks of 16 follow the same rule).
+ *
+ *   X   : (L, MN, K) float32, K contiguous (an A or B operand before
+ *         quantisation).
+ *   Q   : (L, MN, K) element codes, one byte each (the layout of A / B).
+ *   SF  : mxgemm_sf_bytes(MN, K, L, sf_vec_size) bytes, the physical atom
+ *         layout described above for SFA / SFB.  Every byte is written:
+ *         padding entries (rows >= MN, K-blocks >= ceil(K/sf)) get 127.
+ *   fmt : MXG_FMT_E4M3 (FMAX = 448) or MXG_FMT_E5M2 (FMAX = 57344).
+ *
+ * Per row and block of sf_vec_size consecutive K elements (the last block
+ * may be partial): bm = max |x|; e = the smallest integer with
+ * FMAX * 2^e >= bm, clamped to [-127, 127], and e = 0 when bm = 0; scale
+ * byte = e + 127; code = x * 2^-e rounded to the nearest code, ties to even
+ * (nothing saturates: |x * 2^-e| <= FMAX).  The pages give no formula for
+ * the scale; this rule is the one the GEMM's test inputs are made with (a
+ * scale of 2^ceil(log2(blockmax / FMAX))).  Results for non-finite inputs
+ * are unspecified.
+ *
+ * Errors (before any work): MXG_ERR_SHAPE (a negative size, K >= 2^23 or
+ * too many atoms), MXG_ERR_SFVEC, MXG_ERR_FMT, MXG_ERR_ALIGN (K % 16 or a
+ * pointer not 16-byte aligned), MXG_ERR_NULL, MXG_ERR_DEVICE.  MN, K or
+ * L == 0 queues nothing and returns MXG_OK.  Q and SF must not overlap X.
+ */
+int mxgemm_mx_quantize(const float* X, void* Q, uint8_t* SF, int64_t MN, int64_t K, int64_t L,
+                       int sf_vec_size, int fmt, void* stream);
+
 /* mxgemm_strerror -- static text for a status code. No HIP call. */
 const char* mxgemm_strerror(int status);
 

@@ -108,3 +108,25 @@ def test_python_errors_map_to_exceptions(lib):
         lib.mxgemm_amax(None, None, None, None, None, None, 16, 16, 16, 1, 32, 0, 0, stream=0)
     assert "sf_vec_size" in lib.mxgemm_strerror(lib.MXG_ERR_SFVEC)
     assert lib.mxgemm_strerror(-99) == "unknown status"
+
+
+def test_quantize_errors_before_device_work(lib):
+    c = ctypes.CDLL(lib.LIB_PATH)
+    f = c.mxgemm_mx_quantize
+    vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    f.argtypes = [vp, vp, vp, i64, i64, i64, ci, ci, vp]
+    f.restype = ci
+    good = 0x7F0000000000
+    assert f(None, good, good, 128, 128, 1, 32, 0, None) == lib.MXG_ERR_NULL
+    assert f(good, good, None, 128, 128, 1, 32, 0, None) == lib.MXG_ERR_NULL
+    assert f(good + 4, good, good, 128, 128, 1, 32, 0, None) == lib.MXG_ERR_ALIGN
+    assert f(good, good, good + 8, 128, 128, 1, 32, 0, None) == lib.MXG_ERR_ALIGN
+    assert f(good, good, good, 128, 120, 1, 32, 0, None) == lib.MXG_ERR_ALIGN        # K % 16
+    assert f(good, good, good, 128, 128, 1, 64, 0, None) == lib.MXG_ERR_SFVEC
+    assert f(good, good, good, 128, 128, 1, 32, 2, None) == lib.MXG_ERR_FMT
+    assert f(good, good, good, -1, 128, 1, 32, 0, None) == lib.MXG_ERR_SHAPE
+    assert f(good, good, good, 128, 1 << 23, 1, 32, 0, None) == lib.MXG_ERR_SHAPE   # 128 rows past 32-bit offsets
+    # empty problems queue nothing and need no pointers
+    assert f(None, None, None, 0, 128, 1, 32, 0, None) == lib.MXG_OK
+    assert f(None, None, None, 128, 0, 1, 32, 0, None) == lib.MXG_OK
+    assert f(None, None, None, 128, 128, 0, 32, 0, None) == lib.MXG_OK
