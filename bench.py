@@ -52,13 +52,15 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def profile_name(workload_name, fp8_mfma):
+def profile_name(workload_name, fp8_mfma, op="gemm"):
+    if op == "quantize":
+        return f"mx_quantize_kernel__{workload_name}_operands.txt"
     return f"mxgemm_amax_kernel_{'fp8' if fp8_mfma else 'bf16'}__{workload_name}.txt"
 
 
-def read_traffic(workload_name, fp8_mfma):
+def read_traffic(workload_name, fp8_mfma, op="gemm"):
     """HBM bytes per launch from the committed counter summary, or None if absent or taken on other sources."""
-    path = os.path.join(PROFILES, profile_name(workload_name, fp8_mfma))
+    path = os.path.join(PROFILES, profile_name(workload_name, fp8_mfma, op))
     if not os.path.exists(path):
         return None
     kv = {}
@@ -96,6 +98,27 @@ def _is_gemm(name):
     return "mxgemm_amax" in name and "reset" not in name
 
 
+def _is_quantize(name):
+    return "mx_quantize_kernel" in name
+
+
+def quantize_operands_shape(workload):
+    """The stacked float32 operands of a GEMM workload, quantised as one (L, M + N, K) tensor.
+
+    A's rows then B's rows: M is a multiple of 128 for the workloads this is used on, so the
+    scale atoms of the stack are exactly those of A followed by those of B."""
+    import workloads as W
+    cfg = W.WORKLOADS[workload]
+    assert cfg["M"] % 128 == 0, "stacking needs A's rows to end on an atom boundary"
+    return cfg["L"], cfg["M"] + cfg["N"], cfg["K"], cfg["sf"]
+
+
+def quantize_bytes(mn, k, l, sf):
+    """Algorithmic bytes of one MX quantisation: float32 in, one code byte out per element, plus the atoms."""
+    import workloads as W
+    return 4 * l * mn * k + l * mn * k + W.sf_bytes(mn, k, l, sf)
+
+
 def _per_dispatch(rows, kernel_substr, counter, kernel_name_exact=False):
     per = {}
     for r in rows:
@@ -106,13 +129,20 @@ def _per_dispatch(rows, kernel_substr, counter, kernel_name_exact=False):
     return list(per.values())
 
 
-def rocprof_summary(d, workload, fp8_mfma, commands):
+def rocprof_summary(d, workload, fp8_mfma, commands, op="gemm"):
     """Text summary of a rocprofv3 kernel trace (d/kt) and two counter passes (d/fetch, d/write)."""
     import workloads as W
     cfg = W.WORKLOADS[workload]
     M, N, K, L, sf = cfg["M"], cfg["N"], cfg["K"], cfg["L"], cfg["sf"]
-    out = [f"# rocprofv3 summary: the GEMM + amax kernel ({'fp8 MFMA' if fp8_mfma else 'bf16 MFMA'} path), "
-           f"workload {cfg['name']} (M={M} N={N} K={K} L={L} sf={sf})", ""]
+    if op == "quantize":
+        ql, qmn, qk, qsf = quantize_operands_shape(workload)
+        out = [f"# rocprofv3 summary: the MX quantisation kernel, the float32 operands of workload {cfg['name']} "
+               f"stacked as one ({ql}, {qmn}, {qk}) tensor (A's {M} rows, then B's {N}), sf={qsf}, E4M3", ""]
+        is_target = _is_quantize
+    else:
+        out = [f"# rocprofv3 summary: the GEMM + amax kernel ({'fp8 MFMA' if fp8_mfma else 'bf16 MFMA'} path), "
+               f"workload {cfg['name']} (M={M} N={N} K={K} L={L} sf={sf})", ""]
+        is_target = _is_gemm
     out.append("commands (from the repository root; rocprofv3 runs from /tmp with TMPDIR=/tmp):")
     out.extend("  " + c for c in commands)
     out.append("")
@@ -125,13 +155,18 @@ def rocprof_summary(d, workload, fp8_mfma, commands):
         out.append(f"  {name[:100]:100s} calls {int(r['Calls']):5d}  avg {float(r['AverageNs']) / 1e3:10.2f} us  "
                    f"min {float(r['MinNs']) / 1e3:10.2f}  max {float(r['MaxNs']) / 1e3:10.2f}  "
                    f"{float(r['Percentage']):5.1f}%")
-        # the GEMM kernel that ran the workload: the one with the largest total time
-        if _is_gemm(name) and float(r["TotalDurationNs"]) > gemm_total:
+        # the kernel that ran the workload: the one with the largest total time
+        if is_target(name) and float(r["TotalDurationNs"]) > gemm_total:
             gemm_name, gemm_total = name, float(r["TotalDurationNs"])
             avg_us = float(r["AverageNs"]) / 1e3
     out.append("")
-    fl = W.flops(M, N, K, L)
-    if avg_us:
+    if avg_us and op == "quantize":
+        out.append(f"kernel: {gemm_name}")
+        out.append(f"avg_duration_us: {avg_us:.2f}")
+        out.append(f"algorithmic_GBps_at_avg_duration: "
+                   f"{quantize_bytes(qmn, qk, ql, qsf) / (avg_us * 1e-6) / 1e9:.1f}")
+    elif avg_us:
+        fl = W.flops(M, N, K, L)
         out.append(f"gemm_kernel: {gemm_name}")
         out.append(f"gemm_avg_duration_us: {avg_us:.2f}")
         out.append(f"gemm_tflops_at_avg_duration: {fl / (avg_us * 1e-6) / 1e12:.1f}")
@@ -146,11 +181,11 @@ def rocprof_summary(d, workload, fp8_mfma, commands):
         w_fac = COPY_PROBE_BYTES / (1024.0 * sum(cw) / len(cw))
         fb = sum(gf) / len(gf) * 1024.0 * f_fac
         wb = sum(gw) / len(gw) * 1024.0 * w_fac
-        ab = W.algorithmic_bytes(M, N, K, L, sf)
+        ab = quantize_bytes(qmn, qk, ql, qsf) if op == "quantize" else W.algorithmic_bytes(M, N, K, L, sf)
         out += ["",
                 "HBM traffic (--pmc FETCH_SIZE, then --pmc WRITE_SIZE; KiB per dispatch):",
-                f"  gemm FETCH_SIZE per dispatch (KiB, mean of {len(gf)}): {sum(gf) / len(gf):.0f}",
-                f"  gemm WRITE_SIZE per dispatch (KiB, mean of {len(gw)}): {sum(gw) / len(gw):.0f}",
+                f"  kernel FETCH_SIZE per dispatch (KiB, mean of {len(gf)}): {sum(gf) / len(gf):.0f}",
+                f"  kernel WRITE_SIZE per dispatch (KiB, mean of {len(gw)}): {sum(gw) / len(gw):.0f}",
                 f"  copy probe (y = -x, {COPY_PROBE_BYTES} B read + {COPY_PROBE_BYTES} B written): "
                 f"FETCH_SIZE {sum(cf) / len(cf):.0f} KiB, WRITE_SIZE {sum(cw) / len(cw):.0f} KiB",
                 f"  calibration factors (true bytes / counter bytes): fetch {f_fac:.4f}, write {w_fac:.4f}",
@@ -160,6 +195,11 @@ def rocprof_summary(d, workload, fp8_mfma, commands):
                 f"algorithmic_bytes_per_launch: {ab}",
                 f"traffic_over_algorithmic: {(fb + wb) / ab:.3f}"]
     out += ["", f"kernel_source_sha256: {kernel_source_hash()}"]
+    bench_line = os.path.join(d, "bench.json")
+    if os.path.exists(bench_line):
+        with open(bench_line) as f:
+            out += ["", f"bench.py line of the same run ({commands[0].split('  ')[0] if commands else 'bench.py'}):",
+                    f.read().strip()]
     return "\n".join(out) + "\n"
 
 
@@ -218,12 +258,103 @@ def host_overhead(lib, A, B, SFA, SFB, C, Amax, stream_handle, a_fmt, b_fmt, sf,
             "shape": "128x128x128", "what": "mxgemm_amax via ctypes: validate, clear Amax, launch; no wait"}
 
 
+def bench_quantize(args):
+    """One JSON line for the MX quantisation kernel: a step quantises the workload's float32 A and B,
+    stacked as one tensor (see quantize_operands_shape), resident in HBM."""
+    import math
+
+    import numpy as np
+    import torch
+
+    import block_scaled_precision_e4m3_amd as lib
+    import workloads as W
+    cfg = W.WORKLOADS[args.workload]
+    l, mn, k, sf = quantize_operands_shape(args.workload)
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.workload)
+    x = torch.randn((l, mn, k), generator=gen, device=dev, dtype=torch.float32)
+    if cfg["name"] == "projection":
+        x[:, cfg["M"]:, :] /= math.sqrt(k)          # B ~ N(0,1)/sqrt(K), A ~ N(0,1), as in the workload
+    q = torch.empty((l, mn, k), dtype=torch.uint8, device=dev)
+    sfb = torch.empty(W.sf_bytes(mn, k, l, sf), dtype=torch.uint8, device=dev)
+    fmt = lib.MXG_FMT_E4M3
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def step():
+        lib.mxgemm_mx_quantize(x, q, sfb, mn, k, l, sf, fmt, sh)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    nbytes = quantize_bytes(mn, k, l, sf)
+    ms_per_step = wall * 1e3 / args.steps
+    achieved = nbytes / (kernel_ms * 1e-3) / 1e9
+    out = {
+        "metric": "MX block quantisation GB/s (float32 in; E4M3 codes and E8M0 scale atoms out)",
+        "value": round(nbytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32 in, e4m3 codes + e8m0 scales out",
+        "data": "synthetic (seeded normal; the workload's operand distributions)",
+        "config": {"workload": f"{cfg['name']} operands (A {cfg['M']}x{k} and B {cfg['N']}x{k} stacked)",
+                   "MN": mn, "K": k, "L": l, "sf_vec_size": sf, "fmt": "e4m3"},
+        "kernel_ms": round(kernel_ms, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_GBS, 4),
+                     "traffic": read_traffic(cfg["name"], False, "quantize"),
+                     "algorithmic_bytes": nbytes},
+    }
+    if args.copy_probe:
+        copy_probe()
+    if not args.no_cpu_baseline:
+        import oracle
+        xh = x.cpu().numpy()
+        rng = np.random.default_rng(0)
+        t_total, done = 0.0, 0
+        while t_total < 10.0:
+            r0 = 128 * int(rng.integers(0, mn // 128))
+            t1 = time.perf_counter()
+            oracle.mx_quantize(xh[:, r0:r0 + 1024], sf, fmt)
+            t_total += time.perf_counter() - t1
+            done += xh[:, r0:r0 + 1024].shape[1]
+        try:
+            cores = len(os.sched_getaffinity(0))
+        except AttributeError:
+            cores = os.cpu_count()
+        out["cpu_baseline"] = {
+            "value": quantize_bytes(done, k, l, sf) / t_total / 1e9, "unit": "GB/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"oracle.mx_quantize on {done} rows x {k} (blocks of up to 1024 rows at random atom "
+                      f"boundaries), {t_total:.1f} s; value counts the same algorithmic bytes per row"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=5)
+    ap.add_argument("--op", choices=["gemm", "quantize"], default="gemm",
+                    help="gemm: the GEMM + amax step (default); quantize: the MX quantisation of the "
+                         "workload's float32 operands")
     ap.add_argument("--fp8-mfma", action="store_true", help="time the reduced-precision FP8 MFMA path")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-host-overhead", action="store_true",
@@ -237,13 +368,17 @@ def main():
     args = ap.parse_args()
 
     if args.rocprof_summary:
-        print(rocprof_summary(args.rocprof_summary, args.workload, args.fp8_mfma, args.command), end="")
+        print(rocprof_summary(args.rocprof_summary, args.workload, args.fp8_mfma, args.command, args.op), end="")
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: runs on one GPU only (--gpus 1); several GPUs would each run this kernel "
               "on their own share of C tiles, which this benchmark does not launch", file=sys.stderr)
         sys.exit(2)
+
+    if args.op == "quantize":
+        bench_quantize(args)
+        return
 
     import torch
 
