@@ -30,6 +30,8 @@ MXG_FLAG_AMAX_ACCUMULATE = 1
 MXG_FLAG_FP8_MFMA = 2
 MXG_FLAG_TILE_128 = 4
 MXG_FLAG_TILE_256 = 8
+MXG_FLAG_C_BF16 = 32
+MXG_FLAG_C_F16 = 64
 
 MXG_OK = 0
 MXG_ERR_NULL = -1
@@ -199,8 +201,12 @@ def _sf_phys(t, mn, k, l, sf):
     return t
 
 
-def gemm_amax(a, b, sfa, sfb, c=None, amax=None, sf_vec_size=32, stream=None, accumulate=False, fp8_mfma=False):
-    """(c, amax) = block-scaled GEMM + amax of torch FP8 tensors; see the module docstring."""
+def gemm_amax(a, b, sfa, sfb, c=None, amax=None, sf_vec_size=32, stream=None, accumulate=False, fp8_mfma=False,
+              c_dtype=None):
+    """(c, amax) = block-scaled GEMM + amax of torch FP8 tensors; see the module docstring.
+
+    C is float32 by default; c_dtype (or a preallocated c) of torch.bfloat16 / torch.float16
+    stores the accumulators rounded to nearest even (amax still from the float32 values)."""
     import torch
     a_base, m, k, l = _as_lrk(a, "A")
     b_base, n, kb, lb = _as_lrk(b, "B")
@@ -210,13 +216,15 @@ def gemm_amax(a, b, sfa, sfb, c=None, amax=None, sf_vec_size=32, stream=None, ac
     sfa_p = _sf_phys(sfa, m, k, l, sf_vec_size)
     sfb_p = _sf_phys(sfb, n, k, l, sf_vec_size)
     if c is None:
-        c = torch.empty((l, m, n), dtype=torch.float32, device=a.device).permute(1, 2, 0)
+        c = torch.empty((l, m, n), dtype=c_dtype or torch.float32, device=a.device).permute(1, 2, 0)
     c_base = c.permute(2, 0, 1) if c.dim() == 3 else c.unsqueeze(0)
-    if c.dtype != torch.float32 or not c_base.is_contiguous():
-        raise MxgemmValueError(MXG_ERR_ALIGN, "C must be float32, n-major (M, N, L) with strides (N, 1, M*N)")
+    c_flag = {torch.float32: 0, torch.bfloat16: MXG_FLAG_C_BF16, torch.float16: MXG_FLAG_C_F16}.get(c.dtype)
+    if c_flag is None or not c_base.is_contiguous():
+        raise MxgemmValueError(MXG_ERR_ALIGN, "C must be float32, bfloat16 or float16, n-major (M, N, L) with "
+                                              "strides (N, 1, M*N)")
     if amax is None:
         amax = torch.zeros((1, 1, 1), dtype=torch.float32, device=a.device)
-    flags = (MXG_FLAG_AMAX_ACCUMULATE if accumulate else 0) | (MXG_FLAG_FP8_MFMA if fp8_mfma else 0)
+    flags = (MXG_FLAG_AMAX_ACCUMULATE if accumulate else 0) | (MXG_FLAG_FP8_MFMA if fp8_mfma else 0) | c_flag
     mxgemm_amax_ex(a_base, b_base, sfa_p, sfb_p, c_base, amax, m, n, k, l, sf_vec_size, fa, fb, flags, stream)
     return c, amax
 
@@ -258,6 +266,6 @@ __all__ = [
     "mxgemm_launch_config", "mxgemm_strerror", "gemm_amax", "LIB_PATH", "EXPORTED",
     "mxgemm_mx_quantize", "mx_quantize",
     "MXG_FMT_E4M3", "MXG_FMT_E5M2", "MXG_FLAG_AMAX_ACCUMULATE", "MXG_FLAG_FP8_MFMA", "MXG_FLAG_TILE_128",
-    "MXG_FLAG_TILE_256", "MxgemmError", "MxgemmValueError",
+    "MXG_FLAG_TILE_256", "MXG_FLAG_C_BF16", "MXG_FLAG_C_F16", "MxgemmError", "MxgemmValueError",
     "MxgemmRuntimeError",
 ]

@@ -110,15 +110,15 @@ Config choose(int64_t M, int64_t N, int64_t K, int64_t L, int cus) {
   return kSmall;
 }
 
-template <int MODE, int KIND>
+template <int MODE, int KIND, int CT>
 hipError_t launch_mode(const mxg::Params& p, int sf, int fa, int fb, int64_t grid, hipStream_t s) {
   const dim3 g((unsigned)grid), b(KIND ? mxg::big::kThreads : mxg::kThreads);
 #define MXG_LAUNCH(SF, FA, FB)                                                                         \
   do {                                                                                                 \
     if constexpr (KIND == 1)                                                                           \
-      hipLaunchKernelGGL((mxg::big::mxgemm_amax_big_kernel<SF, FA, FB, MODE>), g, b, 0, s, p);         \
+      hipLaunchKernelGGL((mxg::big::mxgemm_amax_big_kernel<SF, FA, FB, MODE, CT>), g, b, 0, s, p);     \
     else                                                                                               \
-      hipLaunchKernelGGL((mxg::mxgemm_amax_kernel<SF, FA, FB, MODE>), g, b, 0, s, p);                  \
+      hipLaunchKernelGGL((mxg::mxgemm_amax_kernel<SF, FA, FB, MODE, CT>), g, b, 0, s, p);              \
   } while (0)
   if (sf == 32) {
     if (fa == 0 && fb == 0) MXG_LAUNCH(32, 0, 0);
@@ -218,9 +218,13 @@ int mxgemm_amax_ex(const void* A, const void* B, const uint8_t* SFA, const uint8
   int st = check_sizes(M, N, K, L, sf_vec_size, a_fmt, b_fmt);
   if (st != MXG_OK) return st;
   const unsigned tile_flags = flags & (MXG_FLAG_TILE_128 | MXG_FLAG_TILE_256);
-  if (flags & ~(unsigned)(MXG_FLAG_AMAX_ACCUMULATE | MXG_FLAG_FP8_MFMA | MXG_FLAG_TILE_128 | MXG_FLAG_TILE_256))
+  const unsigned c_flags = flags & (MXG_FLAG_C_BF16 | MXG_FLAG_C_F16);
+  if (flags & ~(unsigned)(MXG_FLAG_AMAX_ACCUMULATE | MXG_FLAG_FP8_MFMA | MXG_FLAG_TILE_128 | MXG_FLAG_TILE_256 |
+                          MXG_FLAG_C_BF16 | MXG_FLAG_C_F16))
     return MXG_ERR_FLAGS;
   if (tile_flags & (tile_flags - 1)) return MXG_ERR_FLAGS;  // more than one tile flag
+  if (c_flags & (c_flags - 1)) return MXG_ERR_FLAGS;        // both 16-bit C types
+  if (c_flags && (flags & MXG_FLAG_FP8_MFMA)) return MXG_ERR_FLAGS;  // 16-bit C: bf16 datapath only
   // A, B and the scales are read only when there is a non-empty C and a non-empty K
   const bool need_c = M > 0 && N > 0 && L > 0;
   const bool need_a = need_c && K > 0, need_b = need_a;
@@ -269,13 +273,19 @@ int mxgemm_amax_ex(const void* A, const void* B, const uint8_t* SFA, const uint8
   p.xcd_remap = (grid % 8 == 0) ? 1 : 0;
 
   const bool fp8 = (flags & MXG_FLAG_FP8_MFMA) != 0;
+  const int ct = (flags & MXG_FLAG_C_BF16) ? 1 : (flags & MXG_FLAG_C_F16) ? 2 : 0;
   hipError_t e;
-  if (cfg.kind == 1)
-    e = fp8 ? launch_mode<mxg::kModeFp8, 1>(p, sf_vec_size, a_fmt, b_fmt, grid, s)
-            : launch_mode<mxg::kModeBf16, 1>(p, sf_vec_size, a_fmt, b_fmt, grid, s);
-  else
-    e = fp8 ? launch_mode<mxg::kModeFp8, 0>(p, sf_vec_size, a_fmt, b_fmt, grid, s)
-            : launch_mode<mxg::kModeBf16, 0>(p, sf_vec_size, a_fmt, b_fmt, grid, s);
+  if (cfg.kind == 1) {
+    if (fp8) e = launch_mode<mxg::kModeFp8, 1, 0>(p, sf_vec_size, a_fmt, b_fmt, grid, s);
+    else if (ct == 1) e = launch_mode<mxg::kModeBf16, 1, 1>(p, sf_vec_size, a_fmt, b_fmt, grid, s);
+    else if (ct == 2) e = launch_mode<mxg::kModeBf16, 1, 2>(p, sf_vec_size, a_fmt, b_fmt, grid, s);
+    else e = launch_mode<mxg::kModeBf16, 1, 0>(p, sf_vec_size, a_fmt, b_fmt, grid, s);
+  } else {
+    if (fp8) e = launch_mode<mxg::kModeFp8, 0, 0>(p, sf_vec_size, a_fmt, b_fmt, grid, s);
+    else if (ct == 1) e = launch_mode<mxg::kModeBf16, 0, 1>(p, sf_vec_size, a_fmt, b_fmt, grid, s);
+    else if (ct == 2) e = launch_mode<mxg::kModeBf16, 0, 2>(p, sf_vec_size, a_fmt, b_fmt, grid, s);
+    else e = launch_mode<mxg::kModeBf16, 0, 0>(p, sf_vec_size, a_fmt, b_fmt, grid, s);
+  }
   return e == hipSuccess ? MXG_OK : MXG_ERR_LAUNCH;
 }
 

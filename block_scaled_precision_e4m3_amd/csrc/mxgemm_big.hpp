@@ -74,9 +74,10 @@ __device__ __forceinline__ unsigned sf_tail(unsigned d, int g, int Kb) {
   return (d & keep) | (0x7F7F7F7Fu & ~keep);
 }
 
-template <int SF, int FA, int FB, int MODE>
+template <int SF, int FA, int FB, int MODE, int CT>
 __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) {
   using Y = Layout<SF>;
+  constexpr int kEs = kCBytes<CT>;  // bytes per C element
   constexpr int NSF = Y::NSF;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * Y::kStage + Y::kEpiBytes];
 
@@ -199,8 +200,8 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   };
   auto store_ctx = [&](const Tile& T) {
     StoreCtx x;
-    x.c_bytes = (unsigned)T.mvalid * (unsigned)p.N * 4u;
-    x.rc = make_rsrc(p.C + ((int64_t)T.l * p.M + T.m0) * p.N, x.c_bytes);
+    x.c_bytes = (unsigned)T.mvalid * (unsigned)p.N * (unsigned)kEs;
+    x.rc = make_rsrc(reinterpret_cast<uint8_t*>(p.C) + ((int64_t)T.l * p.M + T.m0) * p.N * kEs, x.c_bytes);
     x.mvalid = T.mvalid;
     x.nvalid = T.nvalid;
     x.n0 = T.n0;
@@ -210,7 +211,8 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   // wave's LDS area: lane (r, h) writes its row r, columns 8q + 4h straight
   // from the accumulation registers; lane L then reads row 8k + L/8, columns
   // 4(L%8) .. +4, so each of the block's 4 stores covers 8 rows x 128
-  // contiguous bytes (whole cache lines) instead of 32 rows x 2 x 16 bytes.
+  // contiguous bytes (whole cache lines; 64 bytes with a 16-bit C) instead
+  // of 32 rows x 2 x 16 bytes.
   // Rows of 36 floats keep both passes free of bank conflicts.  The wave's LDS
   // operations execute in order, so block b+1 is written and read back while
   // block b's stores go out (its reads precede those writes), with no barrier.
@@ -221,7 +223,7 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
     const int rd_row = ln >> 3, rd_col = 4 * (ln & 7);
     const int rd_off = (rd_row * Y::kEpiRow + rd_col) * 4;                  // + 8 k rows
     const int col_base = kWN * wn + rd_col;                                  // tile column of the lane's run
-    const unsigned vrow0 = ((unsigned)(128 * wm + rd_row) * (unsigned)p.N + (unsigned)(x.n0 + col_base)) * 4u;
+    const unsigned vrow0 = ((unsigned)(128 * wm + rd_row) * (unsigned)p.N + (unsigned)(x.n0 + col_base)) * (unsigned)kEs;
     auto put = [&](int i, int j) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -243,8 +245,9 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
       for (int k = 0; k < 4; ++k) {
         const int row = 128 * wm + 32 * i + 8 * k + rd_row;
         const bool ok = cok & (row < x.mvalid);
-        const unsigned off = vrow0 + (unsigned)(32 * i + 8 * k) * (unsigned)p.N * 4u + (unsigned)(32 * j * 4);
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v[k]), x.rc, ok ? (int)off : (int)x.c_bytes, 0, 0);
+        const unsigned off =
+            vrow0 + (unsigned)(32 * i + 8 * k) * (unsigned)p.N * (unsigned)kEs + (unsigned)(32 * j * kEs);
+        store_c4<CT>(v[k], x.rc, ok ? (int)off : (int)x.c_bytes, 0);
         const unsigned m4 = max(max(__float_as_uint(v[k][0]) & 0x7FFFFFFFu, __float_as_uint(v[k][1]) & 0x7FFFFFFFu),
                                 max(__float_as_uint(v[k][2]) & 0x7FFFFFFFu, __float_as_uint(v[k][3]) & 0x7FFFFFFFu));
         lmax = max(lmax, m4 & (0u - (unsigned)ok));

@@ -17,6 +17,9 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 
 constexpr int kGroupM = 8;           // tile rows per raster group
 constexpr int kRsrcFlags = 0x00020000;
@@ -184,6 +187,26 @@ __device__ __forceinline__ v8bf cvt8(unsigned w0, unsigned w1, float scale) {
   u[2] = cvt2<FMT, false>(w1, scale);
   u[3] = cvt2<FMT, true>(w1, scale);
   return __builtin_bit_cast(v8bf, u);
+}
+
+// C element type, a kernel template parameter CT: 0 float32, 1 bfloat16,
+// 2 float16.  The accumulators are float32 either way; a 16-bit C receives
+// them rounded to nearest even (v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32), and
+// the amax is taken over the float32 values.
+template <int CT>
+constexpr int kCBytes = CT == 0 ? 4 : 2;
+
+// Four consecutive outputs of one C row, given in float32, stored as C's
+// element type at byte offset voff + soff of resource rc.
+template <int CT>
+__device__ __forceinline__ void store_c4(const v4f& v, __amdgpu_buffer_rsrc_t rc, int voff, int soff) {
+  if constexpr (CT == 0)
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), rc, voff, soff, 0);
+  else if constexpr (CT == 1)
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, __builtin_convertvector(v, v4bf)), rc, voff, soff,
+                                          0);
+  else
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, __builtin_convertvector(v, v4h)), rc, voff, soff, 0);
 }
 
 // Clears the Amax bits (queued before a GEMM that does not accumulate).

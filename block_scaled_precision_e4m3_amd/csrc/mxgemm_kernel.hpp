@@ -212,8 +212,9 @@ __device__ __forceinline__ void compute_slice(v16f (&acc)[kTM][kTN], const uint8
 
 // --- the kernel --------------------------------------------------------------
 
-template <int SF, int FA, int FB, int MODE>
+template <int SF, int FA, int FB, int MODE, int CT>
 __global__ __launch_bounds__(kThreads, 2) void mxgemm_amax_kernel(Params p) {
+  constexpr int kEs = kCBytes<CT>;           // bytes per C element
   constexpr int WM = kBM / 2, WN = kBN / 2;  // wave tile
   constexpr int NSF = (SF == 32) ? 1 : 2;    // atoms per step
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * kStage];
@@ -302,9 +303,11 @@ __global__ __launch_bounds__(kThreads, 2) void mxgemm_amax_kernel(Params p) {
   // which stores nothing, so every lane issues exactly kStoresPerStep stores
   auto store_batch = [&](const Tile& P, auto Bc) {
     constexpr int b = decltype(Bc)::value;
-    const unsigned c_bytes = (unsigned)P.mvalid * (unsigned)p.N * 4u;
-    const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.C + ((int64_t)P.l * p.M + P.m0) * p.N, c_bytes);
-    const unsigned vbase = ((unsigned)(wm * WM + r) * (unsigned)p.N + (unsigned)(P.n0 + wn * WN + 4 * h)) * 4u;
+    const unsigned c_bytes = (unsigned)P.mvalid * (unsigned)p.N * (unsigned)kEs;
+    const __amdgpu_buffer_rsrc_t rc =
+        make_rsrc(reinterpret_cast<uint8_t*>(p.C) + ((int64_t)P.l * p.M + P.m0) * p.N * kEs, c_bytes);
+    const unsigned vbase =
+        ((unsigned)(wm * WM + r) * (unsigned)p.N + (unsigned)(P.n0 + wn * WN + 4 * h)) * (unsigned)kEs;
 #pragma unroll
     for (int u = 0; u < kStoresPerStep; ++u) {
       const int idx = b * kStoresPerStep + u;  // 0 .. kNStores-1
@@ -315,9 +318,7 @@ __global__ __launch_bounds__(kThreads, 2) void mxgemm_amax_kernel(Params p) {
       v[1] = prev[i][j][4 * q + 1];
       v[2] = prev[i][j][4 * q + 2];
       v[3] = prev[i][j][4 * q + 3];
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), rc,
-                                             ok ? (int)(vbase + (32 * j + 8 * q) * 4) : (int)c_bytes,
-                                             ok ? 32 * i * p.N * 4 : 0, 0);
+      store_c4<CT>(v, rc, ok ? (int)(vbase + (32 * j + 8 * q) * kEs) : (int)c_bytes, ok ? 32 * i * p.N * kEs : 0);
       const unsigned m4 = max(max(__float_as_uint(v[0]) & 0x7FFFFFFFu, __float_as_uint(v[1]) & 0x7FFFFFFFu),
                               max(__float_as_uint(v[2]) & 0x7FFFFFFFu, __float_as_uint(v[3]) & 0x7FFFFFFFu));
       lmax = ok ? max(lmax, m4) : lmax;

@@ -97,7 +97,17 @@ enum {
      128x128 tiles, two workgroups per CU.  TILE_256: 256x256 tiles, one
      workgroup per CU; ignored when K == 0.  Setting both is an error. */
   MXG_FLAG_TILE_128 = 4u,
-  MXG_FLAG_TILE_256 = 8u
+  MXG_FLAG_TILE_256 = 8u,
+  /* A 16-bit C ("GEMM + Amax (SM100)", section "Parameters": the C tensor
+     may be float16 or bfloat16 as well as float32): C then holds (L, M, N)
+     bfloat16 (C_BF16) or float16 (C_F16) elements, each the float32
+     accumulator rounded to nearest even (float16 overflows to +-inf).  Amax
+     is still taken over the float32 accumulators (the pages do not say which;
+     the fused epilogue sees those).  The C pointer keeps its float* type in
+     the signature and must still be 16-byte aligned.  Not with
+     MXG_FLAG_FP8_MFMA; setting both C flags is an error. */
+  MXG_FLAG_C_BF16 = 32u,
+  MXG_FLAG_C_F16 = 64u
 };
 
 /*
@@ -130,8 +140,9 @@ int mxgemm_amax(const void* A, const void* B, const uint8_t* SFA, const uint8_t*
  * mxgemm_amax; MXG_FLAG_AMAX_ACCUMULATE skips the clearing kernel and
  * max-reduces into the existing Amax (queues the GEMM kernel only);
  * MXG_FLAG_FP8_MFMA selects the reduced-precision FP8 matrix path;
- * MXG_FLAG_TILE_128 / _256 force a tile configuration.
- * Returns MXG_ERR_FLAGS for unknown bits or more than one tile flag.
+ * MXG_FLAG_TILE_128 / _256 force a tile configuration; MXG_FLAG_C_BF16 /
+ * _F16 store a 16-bit C.  Returns MXG_ERR_FLAGS for unknown bits, more than
+ * one tile flag, both C flags, or a C flag with MXG_FLAG_FP8_MFMA.
  *
  * Exactness of the default path: every dequantised element is exact when
  * its scale byte lies in 3..246 (E4M3) or 10..239 (E5M2), i.e. when the

@@ -90,7 +90,9 @@ def test_errors_before_device_work(lib):
     assert f(*(args[:5] + [None]), *dims, 32, 0, 0, 0, None) == lib.MXG_ERR_NULL
     assert f(*([good + 8] + args[1:]), *dims, 32, 0, 0, 0, None) == lib.MXG_ERR_ALIGN
     assert f(*(args[:4] + [good + 4] + args[5:]), *dims, 32, 0, 0, 0, None) == lib.MXG_ERR_ALIGN
-    assert f(*args, *dims, 32, 0, 0, 32, None) == lib.MXG_ERR_FLAGS
+    assert f(*args, *dims, 32, 0, 0, 128, None) == lib.MXG_ERR_FLAGS    # unknown bit
+    assert f(*args, *dims, 32, 0, 0, 96, None) == lib.MXG_ERR_FLAGS     # both 16-bit C types
+    assert f(*args, *dims, 32, 0, 0, 34, None) == lib.MXG_ERR_FLAGS     # 16-bit C with the FP8 datapath
     assert f(*args, *dims, 32, 0, 0, 16, None) == lib.MXG_ERR_FLAGS   # unknown bit
     assert f(*args, *dims, 32, 0, 0, 12, None) == lib.MXG_ERR_FLAGS   # both tile flags
     assert f(*args, 256, 256, 256, 1, 64, 0, 0, 0, None) == lib.MXG_ERR_SFVEC
