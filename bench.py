@@ -356,6 +356,8 @@ def main():
                     help="gemm: the GEMM + amax step (default); quantize: the MX quantisation of the "
                          "workload's float32 operands")
     ap.add_argument("--fp8-mfma", action="store_true", help="time the reduced-precision FP8 MFMA path")
+    ap.add_argument("--c-dtype", choices=["f32", "bf16", "f16"], default="f32",
+                    help="C element type (f32, the default, is the operation's own output)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-host-overhead", action="store_true",
                     help="skip the 1000 small calls that time the host side (keeps profiles to the workload)")
@@ -396,7 +398,8 @@ def main():
     Amax = torch.zeros(4, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
-    mode_flag = lib.MXG_FLAG_FP8_MFMA if args.fp8_mfma else 0
+    mode_flag = (lib.MXG_FLAG_FP8_MFMA if args.fp8_mfma else 0) | \
+        {"f32": 0, "bf16": lib.MXG_FLAG_C_BF16, "f16": lib.MXG_FLAG_C_F16}[args.c_dtype]
 
     def step():
         lib.mxgemm_amax_ex(A, B, SFA, SFB, C, Amax, M, N, K, L, sf, p["a_fmt"], p["b_fmt"], mode_flag, sh)
@@ -444,7 +447,7 @@ def main():
         "config": {"workload": W.WORKLOADS[args.workload]["name"], "M": M, "N": N, "K": K, "L": L,
                    "sf_vec_size": sf, "a_fmt": "e4m3" if p["a_fmt"] == 0 else "e5m2",
                    "b_fmt": "e4m3" if p["b_fmt"] == 0 else "e5m2", "tile": f"{tile_m}x{tile_n}", "grid": grid,
-                   "path": "fp8-mfma" if args.fp8_mfma else "bf16-mfma"},
+                   "path": "fp8-mfma" if args.fp8_mfma else "bf16-mfma", "c_dtype": args.c_dtype},
         "pct_of_mxfp8_peak": round(100.0 * achieved / PEAK_FP8, 2),
         "kernel_ms": round(kernel_ms, 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
