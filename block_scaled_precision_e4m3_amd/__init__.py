@@ -44,7 +44,8 @@ MXG_ERR_LAUNCH = -7
 MXG_ERR_FLAGS = -8
 
 EXPORTED = ("mxgemm_amax", "mxgemm_amax_ex", "mxgemm_amax_reset", "mxgemm_check_support",
-            "mxgemm_sf_bytes", "mxgemm_launch_config", "mxgemm_strerror", "mxgemm_mx_quantize")
+            "mxgemm_sf_bytes", "mxgemm_launch_config", "mxgemm_strerror", "mxgemm_mx_quantize",
+            "mxgemm_sf_rowwise_to_atoms")
 
 
 class MxgemmError(Exception):
@@ -86,6 +87,8 @@ def _load():
     lib.mxgemm_strerror.restype = ctypes.c_char_p
     lib.mxgemm_mx_quantize.argtypes = [vp, vp, vp, i64, i64, i64, ci, ci, vp]
     lib.mxgemm_mx_quantize.restype = ci
+    lib.mxgemm_sf_rowwise_to_atoms.argtypes = [vp, vp, i64, i64, i64, ci, vp]
+    lib.mxgemm_sf_rowwise_to_atoms.restype = ci
     return lib
 
 
@@ -236,6 +239,33 @@ def mxgemm_mx_quantize(X, Q, SF, MN, K, L, sf_vec_size, fmt, stream=None):
         _raise(st)
 
 
+def mxgemm_sf_rowwise_to_atoms(rowwise, SF, MN, K, L, sf_vec_size, stream=None):
+    """C-ABI mxgemm_sf_rowwise_to_atoms on torch tensors or raw device addresses; raises on a nonzero status."""
+    st = _lib.mxgemm_sf_rowwise_to_atoms(_ptr(rowwise), _ptr(SF), MN, K, L, sf_vec_size, _stream(stream))
+    if st != MXG_OK:
+        _raise(st)
+
+
+def sf_from_rowwise(rowwise, k, sf_vec_size=32, sf=None, stream=None):
+    """Atom-layout scales (L, ceil(MN/128), ceil(K/(4 sf)), 32, 4, 4) uint8 from a contiguous row-wise
+    uint8 CUDA tensor (MN, ceil(K/sf)) or (L, MN, ceil(K/sf)) of E8M0 bytes (e.g. the pages' x_scale)."""
+    import torch
+    if rowwise.element_size() != 1 or not rowwise.is_contiguous() or rowwise.dim() not in (2, 3):
+        raise MxgemmValueError(MXG_ERR_SHAPE, "row-wise scales must be a contiguous one-byte (MN, Kb) or "
+                                              "(L, MN, Kb) tensor")
+    l, mn, kb = (1,) + tuple(rowwise.shape) if rowwise.dim() == 2 else tuple(rowwise.shape)
+    if kb != -(-k // sf_vec_size):
+        raise MxgemmValueError(MXG_ERR_SHAPE, f"row-wise scales have {kb} blocks per row, K={k} needs "
+                                              f"{-(-k // sf_vec_size)}")
+    shape = (l, -(-mn // 128), -(-k // (4 * sf_vec_size)), 32, 4, 4)
+    if sf is None:
+        sf = torch.empty(shape, dtype=torch.uint8, device=rowwise.device)
+    if sf.numel() != 512 * shape[0] * shape[1] * shape[2] or not sf.is_contiguous():
+        raise MxgemmValueError(MXG_ERR_SHAPE, "sf must be a contiguous buffer of the atom layout's size")
+    mxgemm_sf_rowwise_to_atoms(rowwise, sf, mn, k, l, sf_vec_size, stream)
+    return sf
+
+
 def mx_quantize(x, sf_vec_size=32, fmt=MXG_FMT_E4M3, q=None, sf=None, stream=None):
     """MX-quantise a contiguous float32 CUDA tensor x of shape (MN, K) or (L, MN, K).
 
@@ -264,7 +294,7 @@ def mx_quantize(x, sf_vec_size=32, fmt=MXG_FMT_E4M3, q=None, sf=None, stream=Non
 __all__ = [
     "mxgemm_amax", "mxgemm_amax_ex", "mxgemm_amax_reset", "mxgemm_check_support", "mxgemm_sf_bytes",
     "mxgemm_launch_config", "mxgemm_strerror", "gemm_amax", "LIB_PATH", "EXPORTED",
-    "mxgemm_mx_quantize", "mx_quantize",
+    "mxgemm_mx_quantize", "mx_quantize", "mxgemm_sf_rowwise_to_atoms", "sf_from_rowwise",
     "MXG_FMT_E4M3", "MXG_FMT_E5M2", "MXG_FLAG_AMAX_ACCUMULATE", "MXG_FLAG_FP8_MFMA", "MXG_FLAG_TILE_128",
     "MXG_FLAG_TILE_256", "MXG_FLAG_C_BF16", "MXG_FLAG_C_F16", "MxgemmError", "MxgemmValueError",
     "MxgemmRuntimeError",

@@ -12,6 +12,7 @@
 
 #include "../../include/mxgemm.h"
 #include "mx_quantize.hpp"
+#include "sf_repack.hpp"
 #include "mxgemm_big.hpp"
 #include "mxgemm_kernel.hpp"
 
@@ -315,6 +316,33 @@ int mxgemm_mx_quantize(const float* X, void* Q, uint8_t* SF, int64_t MN, int64_t
   hipStream_t s = (hipStream_t)stream;
   const hipError_t e = sf_vec_size == 32 ? launch_quantize<32>(p, fmt, grid, s) : launch_quantize<16>(p, fmt, grid, s);
   return e == hipSuccess ? MXG_OK : MXG_ERR_LAUNCH;
+}
+
+int mxgemm_sf_rowwise_to_atoms(const uint8_t* rowwise, uint8_t* SF, int64_t MN, int64_t K, int64_t L,
+                               int sf_vec_size, void* stream) {
+  if (MN < 0 || K < 0 || L < 0) return MXG_ERR_SHAPE;
+  if (sf_vec_size != 16 && sf_vec_size != 32) return MXG_ERR_SFVEC;
+  if (!fits_i32(MN) || !fits_i32(K) || !fits_i32(L)) return MXG_ERR_SHAPE;
+  if (L * cdiv(MN, 128) * cdiv(K, 4 * sf_vec_size) > 0x7FFFFFFFLL) return MXG_ERR_SHAPE;
+  if (MN == 0 || K == 0 || L == 0) return MXG_OK;
+  if (!rowwise || !SF) return MXG_ERR_NULL;
+  if (!aligned16(SF)) return MXG_ERR_ALIGN;
+  int dev = 0, cus = 0;
+  int st = device_check(&dev, &cus);
+  if (st != MXG_OK) return st;
+  if (!on_device(rowwise, dev) || !on_device(SF, dev)) return MXG_ERR_DEVICE;
+  mxg::repack::RParams p;
+  p.R = rowwise;
+  p.SF = SF;
+  p.MN = (int)MN;
+  p.Kb = (int)cdiv(K, sf_vec_size);
+  p.MNb = (int)cdiv(MN, 128);
+  p.Kg = (int)cdiv(K, 4 * sf_vec_size);
+  p.num_atoms = (int)(L * p.MNb * p.Kg);
+  const int64_t grid = std::min<int64_t>(p.num_atoms, 16LL * cus);
+  hipLaunchKernelGGL(mxg::repack::rowwise_to_atoms_kernel, dim3((unsigned)grid), dim3(mxg::repack::kThreads), 0,
+                     (hipStream_t)stream, p);
+  return hipGetLastError() == hipSuccess ? MXG_OK : MXG_ERR_LAUNCH;
 }
 
 int mxgemm_amax(const void* A, const void* B, const uint8_t* SFA, const uint8_t* SFB, float* C, float* Amax,

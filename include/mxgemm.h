@@ -216,6 +216,24 @@ int mxgemm_launch_config(int64_t M, int64_t N, int64_t K, int64_t L, int sf_vec_
 int mxgemm_mx_quantize(const float* X, void* Q, uint8_t* SF, int64_t MN, int64_t K, int64_t L,
                        int sf_vec_size, int fmt, void* stream);
 
+/*
+ * mxgemm_sf_rowwise_to_atoms -- row-wise E8M0 block scales into the
+ * physical atom layout that mxgemm_amax reads (for operands quantised with
+ * row-wise scales: "GEMM + RoPE + MXFP8 Projection (SM100)", section
+ * "Shapes", x_scale (tokens, Q_LORA/32) and w_scale (rows, Q_LORA/32)).
+ *
+ *   rowwise : (L, MN, ceil(K/sf)) bytes, contiguous; byte (l, row, kb) is
+ *             the scale of row `row`, K elements [kb*sf, (kb+1)*sf).
+ *   SF      : mxgemm_sf_bytes(MN, K, L, sf_vec_size) bytes, 16-byte aligned;
+ *             every byte is written, padding entries (rows >= MN, K-blocks
+ *             >= ceil(K/sf)) get 127.
+ *
+ * Errors (before any work): MXG_ERR_SHAPE, MXG_ERR_SFVEC, MXG_ERR_NULL,
+ * MXG_ERR_ALIGN (SF), MXG_ERR_DEVICE.  MN, K or L == 0 queues nothing.
+ */
+int mxgemm_sf_rowwise_to_atoms(const uint8_t* rowwise, uint8_t* SF, int64_t MN, int64_t K, int64_t L,
+                               int sf_vec_size, void* stream);
+
 /* mxgemm_strerror -- static text for a status code. No HIP call. */
 const char* mxgemm_strerror(int status);
 

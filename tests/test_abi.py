@@ -14,9 +14,9 @@ HEADER = os.path.join(ROOT, "include", "mxgemm.h")
 
 @pytest.fixture(scope="module")
 def lib():
-    from block_scaled_precision_e4m3_amd import _build
-    if not os.path.exists(_build.LIB):
-        _build.build()
+    import __graft_entry__
+    if not os.path.exists(os.path.join(ROOT, "block_scaled_precision_e4m3_amd", "libmxgemm.so")):
+        __graft_entry__.build()
     import block_scaled_precision_e4m3_amd as lib
     return lib
 
@@ -132,3 +132,18 @@ def test_quantize_errors_before_device_work(lib):
     assert f(None, None, None, 0, 128, 1, 32, 0, None) == lib.MXG_OK
     assert f(None, None, None, 128, 0, 1, 32, 0, None) == lib.MXG_OK
     assert f(None, None, None, 128, 128, 0, 32, 0, None) == lib.MXG_OK
+
+
+def test_rowwise_repack_errors_before_device_work(lib):
+    c = ctypes.CDLL(lib.LIB_PATH)
+    f = c.mxgemm_sf_rowwise_to_atoms
+    vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    f.argtypes = [vp, vp, i64, i64, i64, ci, vp]
+    f.restype = ci
+    good = 0x7F0000000000
+    assert f(None, good, 128, 128, 1, 32, None) == lib.MXG_ERR_NULL
+    assert f(good, None, 128, 128, 1, 32, None) == lib.MXG_ERR_NULL
+    assert f(good, good + 4, 128, 128, 1, 32, None) == lib.MXG_ERR_ALIGN
+    assert f(good, good, 128, 128, 1, 8, None) == lib.MXG_ERR_SFVEC
+    assert f(good, good, -3, 128, 1, 32, None) == lib.MXG_ERR_SHAPE
+    assert f(None, None, 0, 128, 1, 32, None) == lib.MXG_OK
