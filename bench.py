@@ -356,6 +356,9 @@ def main():
                     help="gemm: the GEMM + amax step (default); quantize: the MX quantisation of the "
                          "workload's float32 operands")
     ap.add_argument("--fp8-mfma", action="store_true", help="time the reduced-precision FP8 MFMA path")
+    ap.add_argument("--sf-rowwise", action="store_true",
+                    help="scales arrive row-wise (rows, ceil(K/sf)) bytes, as on the projection page's MXFP8 "
+                         "input path; a step repacks both into the atom layout, then runs the GEMM")
     ap.add_argument("--c-dtype", choices=["f32", "bf16", "f16"], default="f32",
                     help="C element type (f32, the default, is the operation's own output)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -401,7 +404,24 @@ def main():
     mode_flag = (lib.MXG_FLAG_FP8_MFMA if args.fp8_mfma else 0) | \
         {"f32": 0, "bf16": lib.MXG_FLAG_C_BF16, "f16": lib.MXG_FLAG_C_F16}[args.c_dtype]
 
+    if args.sf_rowwise:
+        import numpy as np
+        kb = W.cdiv(K, sf)
+        # the workload's scales, re-expressed row-wise: byte (l, row, kb) of the atom layout
+        def rowwise_of(phys, mn):
+            mnb, kg = W.cdiv(mn, 128), W.cdiv(K, 4 * sf)
+            v = np.asarray(phys).reshape(L, mnb, kg, 32, 4, 4).transpose(0, 1, 4, 3, 2, 5)
+            return np.ascontiguousarray(v.reshape(L, mnb * 128, kg * 4)[:, :mn, :kb])
+        RA = torch.from_numpy(rowwise_of(p["SFA"], M)).to(dev)
+        RB = torch.from_numpy(rowwise_of(p["SFB"], N)).to(dev)
+
+    def repack():
+        lib.mxgemm_sf_rowwise_to_atoms(RA, SFA, M, K, L, sf, sh)
+        lib.mxgemm_sf_rowwise_to_atoms(RB, SFB, N, K, L, sf, sh)
+
     def step():
+        if args.sf_rowwise:
+            repack()
         lib.mxgemm_amax_ex(A, B, SFA, SFB, C, Amax, M, N, K, L, sf, p["a_fmt"], p["b_fmt"], mode_flag, sh)
 
     for _ in range(args.warmup):
@@ -411,8 +431,14 @@ def main():
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    rp_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for i in range(args.steps):
-        # one step == mxgemm_amax: the Amax-clearing kernel, then the GEMM kernel
+        # one step == mxgemm_amax: the Amax-clearing kernel, then the GEMM kernel (after the
+        # scale repacks when the scales arrive row-wise)
+        if args.sf_rowwise:
+            rp_ev[i][0].record(stream)
+            repack()
+            rp_ev[i][1].record(stream)
         lib.mxgemm_amax_reset(Amax, sh)
         ev[i][0].record(stream)
         lib.mxgemm_amax_ex(A, B, SFA, SFB, C, Amax, M, N, K, L, sf, p["a_fmt"], p["b_fmt"],
@@ -447,7 +473,8 @@ def main():
         "config": {"workload": W.WORKLOADS[args.workload]["name"], "M": M, "N": N, "K": K, "L": L,
                    "sf_vec_size": sf, "a_fmt": "e4m3" if p["a_fmt"] == 0 else "e5m2",
                    "b_fmt": "e4m3" if p["b_fmt"] == 0 else "e5m2", "tile": f"{tile_m}x{tile_n}", "grid": grid,
-                   "path": "fp8-mfma" if args.fp8_mfma else "bf16-mfma", "c_dtype": args.c_dtype},
+                   "path": "fp8-mfma" if args.fp8_mfma else "bf16-mfma", "c_dtype": args.c_dtype,
+                   "sf_layout": "row-wise, repacked each step" if args.sf_rowwise else "atoms"},
         "pct_of_mxfp8_peak": round(100.0 * achieved / PEAK_FP8, 2),
         "kernel_ms": round(kernel_ms, 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
@@ -456,6 +483,8 @@ def main():
                      "algorithmic_bytes": abytes,
                      "algorithmic_GBps": round(abytes / (kernel_ms * 1e-3) / 1e9, 1)},
     }
+    if args.sf_rowwise:
+        out["repack_ms"] = round(sum(a.elapsed_time(b) for a, b in rp_ev) / args.steps, 4)
     if not args.no_host_overhead:
         out["host_overhead"] = host_overhead(lib, A, B, SFA, SFB, C, Amax, sh, p["a_fmt"], p["b_fmt"], sf)
     if args.copy_probe:
