@@ -254,8 +254,23 @@ def host_overhead(lib, A, B, SFA, SFB, C, Amax, stream_handle, a_fmt, b_fmt, sf,
             f(*args)
         total += time.perf_counter() - t0
         torch.cuda.synchronize()
-    return {"us_per_call": round(total / (batches * calls) * 1e6, 2), "calls": batches * calls,
-            "shape": "128x128x128", "what": "mxgemm_amax via ctypes: validate, clear Amax, launch; no wait"}
+    # the same through a plan: validation and configuration done once, pointer checks per call
+    plan = lib.Plan(128, 128, 128, 1, sf, a_fmt, b_fmt)
+    fp = lib._lib.mxgemm_plan_execute
+    pargs = (plan._ref,) + args[:6] + (stream_handle,)
+    assert fp(*pargs) == lib.MXG_OK
+    torch.cuda.synchronize()
+    ptotal = 0.0
+    for _ in range(batches):
+        t0 = time.perf_counter()
+        for _ in range(calls):
+            fp(*pargs)
+        ptotal += time.perf_counter() - t0
+        torch.cuda.synchronize()
+    return {"us_per_call": round(total / (batches * calls) * 1e6, 2),
+            "plan_us_per_call": round(ptotal / (batches * calls) * 1e6, 2), "calls": batches * calls,
+            "shape": "128x128x128", "what": "mxgemm_amax via ctypes: validate, clear Amax, launch; no wait "
+                                            "(plan: mxgemm_plan_execute)"}
 
 
 def bench_quantize(args):

@@ -45,7 +45,7 @@ MXG_ERR_FLAGS = -8
 
 EXPORTED = ("mxgemm_amax", "mxgemm_amax_ex", "mxgemm_amax_reset", "mxgemm_check_support",
             "mxgemm_sf_bytes", "mxgemm_launch_config", "mxgemm_strerror", "mxgemm_mx_quantize",
-            "mxgemm_sf_rowwise_to_atoms")
+            "mxgemm_sf_rowwise_to_atoms", "mxgemm_plan_init", "mxgemm_plan_execute")
 
 
 class MxgemmError(Exception):
@@ -89,6 +89,10 @@ def _load():
     lib.mxgemm_mx_quantize.restype = ci
     lib.mxgemm_sf_rowwise_to_atoms.argtypes = [vp, vp, i64, i64, i64, ci, vp]
     lib.mxgemm_sf_rowwise_to_atoms.restype = ci
+    lib.mxgemm_plan_init.argtypes = [vp, i64, i64, i64, i64, ci, ci, ci, cu]
+    lib.mxgemm_plan_init.restype = ci
+    lib.mxgemm_plan_execute.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.mxgemm_plan_execute.restype = ci
     return lib
 
 
@@ -239,6 +243,30 @@ def mxgemm_mx_quantize(X, Q, SF, MN, K, L, sf_vec_size, fmt, stream=None):
         _raise(st)
 
 
+class Plan:
+    """A validated, configured GEMM + amax launch (C-ABI mxgemm_plan): the pages' class API
+    (check_support -> compile -> execute), with the per-call host work reduced to pointer checks.
+
+    plan = Plan(M, N, K, L, sf_vec_size, a_fmt, b_fmt, flags); plan(A, B, SFA, SFB, C, Amax, stream)
+    """
+
+    class _C(ctypes.Structure):
+        _fields_ = [("opaque", ctypes.c_uint64 * 32)]
+
+    def __init__(self, M, N, K, L, sf_vec_size, a_fmt, b_fmt, flags=0):
+        self._plan = Plan._C()
+        self._ref = ctypes.byref(self._plan)
+        st = _lib.mxgemm_plan_init(self._ref, M, N, K, L, sf_vec_size, a_fmt, b_fmt, flags)
+        if st != MXG_OK:
+            _raise(st)
+
+    def __call__(self, A, B, SFA, SFB, C, Amax, stream=None):
+        st = _lib.mxgemm_plan_execute(self._ref, _ptr(A), _ptr(B), _ptr(SFA), _ptr(SFB), _ptr(C), _ptr(Amax),
+                                      _stream(stream))
+        if st != MXG_OK:
+            _raise(st)
+
+
 def mxgemm_sf_rowwise_to_atoms(rowwise, SF, MN, K, L, sf_vec_size, stream=None):
     """C-ABI mxgemm_sf_rowwise_to_atoms on torch tensors or raw device addresses; raises on a nonzero status."""
     st = _lib.mxgemm_sf_rowwise_to_atoms(_ptr(rowwise), _ptr(SF), MN, K, L, sf_vec_size, _stream(stream))
@@ -294,7 +322,7 @@ def mx_quantize(x, sf_vec_size=32, fmt=MXG_FMT_E4M3, q=None, sf=None, stream=Non
 __all__ = [
     "mxgemm_amax", "mxgemm_amax_ex", "mxgemm_amax_reset", "mxgemm_check_support", "mxgemm_sf_bytes",
     "mxgemm_launch_config", "mxgemm_strerror", "gemm_amax", "LIB_PATH", "EXPORTED",
-    "mxgemm_mx_quantize", "mx_quantize", "mxgemm_sf_rowwise_to_atoms", "sf_from_rowwise",
+    "mxgemm_mx_quantize", "mx_quantize", "mxgemm_sf_rowwise_to_atoms", "sf_from_rowwise", "Plan",
     "MXG_FMT_E4M3", "MXG_FMT_E5M2", "MXG_FLAG_AMAX_ACCUMULATE", "MXG_FLAG_FP8_MFMA", "MXG_FLAG_TILE_128",
     "MXG_FLAG_TILE_256", "MXG_FLAG_C_BF16", "MXG_FLAG_C_F16", "MxgemmError", "MxgemmValueError",
     "MxgemmRuntimeError",

@@ -168,6 +168,123 @@ hipError_t launch_quantize(const mxg::quant::QParams& p, int fmt, int64_t grid, 
   return hipGetLastError();
 }
 
+// --- validated, configured GEMM launch (shared by mxgemm_amax_ex and plans) ---
+
+constexpr uint32_t kPlanMagic = 0x4D584731u;  // "MXG1"
+
+struct Prepared {
+  uint32_t magic;
+  int dev;                  // plans: the device the plan was made for
+  mxg::Params p;            // sizes and tiling; pointers filled at launch
+  int sf, fa, fb, kind, ct;
+  unsigned flags;
+  int64_t grid;
+  bool fp8, accumulate, need_c, need_a;
+};
+
+// Validates sizes, formats and flags and fills everything that does not depend on
+// the device; with query_device, also the device and the tiling (configure()).
+int prepare(Prepared* pr, int64_t M, int64_t N, int64_t K, int64_t L, int sf_vec_size, int a_fmt, int b_fmt,
+            unsigned flags, bool query_device);
+
+void configure(Prepared* pr, int cus) {
+  mxg::Params& p = pr->p;
+  const int64_t M = p.M, N = p.N, K = p.K, L = p.L;
+  Config cfg = choose(M, N, K, L, cus);
+  if (pr->flags & MXG_FLAG_TILE_128) cfg = kSmall;
+  if ((pr->flags & MXG_FLAG_TILE_256) && K > 0) cfg = kBig;
+  pr->kind = cfg.kind;
+  p.tilesM = (int)cdiv(M, cfg.tile_m);
+  p.tilesN = (int)cdiv(N, cfg.tile_n);
+  p.ksteps = (int)cdiv(K, 128);
+  p.num_tiles = (int)(L * p.tilesM * p.tilesN);
+  pr->grid = grid_for(p.num_tiles, cus, cfg.per_cu);
+  p.xcd_remap = (pr->grid % 8 == 0) ? 1 : 0;
+}
+
+int prepare(Prepared* pr, int64_t M, int64_t N, int64_t K, int64_t L, int sf_vec_size, int a_fmt, int b_fmt,
+            unsigned flags, bool query_device) {
+  int st = check_sizes(M, N, K, L, sf_vec_size, a_fmt, b_fmt);
+  if (st != MXG_OK) return st;
+  const unsigned tile_flags = flags & (MXG_FLAG_TILE_128 | MXG_FLAG_TILE_256);
+  const unsigned c_flags = flags & (MXG_FLAG_C_BF16 | MXG_FLAG_C_F16);
+  if (flags & ~(unsigned)(MXG_FLAG_AMAX_ACCUMULATE | MXG_FLAG_FP8_MFMA | MXG_FLAG_TILE_128 | MXG_FLAG_TILE_256 |
+                          MXG_FLAG_C_BF16 | MXG_FLAG_C_F16))
+    return MXG_ERR_FLAGS;
+  if (tile_flags & (tile_flags - 1)) return MXG_ERR_FLAGS;  // more than one tile flag
+  if (c_flags & (c_flags - 1)) return MXG_ERR_FLAGS;        // both 16-bit C types
+  if (c_flags && (flags & MXG_FLAG_FP8_MFMA)) return MXG_ERR_FLAGS;  // 16-bit C: bf16 datapath only
+  memset(pr, 0, sizeof(*pr));
+  pr->magic = kPlanMagic;
+  pr->flags = flags;
+  pr->sf = sf_vec_size;
+  pr->fa = a_fmt;
+  pr->fb = b_fmt;
+  pr->fp8 = (flags & MXG_FLAG_FP8_MFMA) != 0;
+  pr->accumulate = (flags & MXG_FLAG_AMAX_ACCUMULATE) != 0;
+  pr->ct = (flags & MXG_FLAG_C_BF16) ? 1 : (flags & MXG_FLAG_C_F16) ? 2 : 0;
+  // A, B and the scales are read only when there is a non-empty C and a non-empty K
+  pr->need_c = M > 0 && N > 0 && L > 0;
+  pr->need_a = pr->need_c && K > 0;
+  mxg::Params& p = pr->p;
+  p.M = (int)M;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.L = (int)L;
+  p.Kb = (int)cdiv(K, sf_vec_size);
+  p.Kg = (int)cdiv(K, 4 * sf_vec_size);
+  p.MNbA = (int)cdiv(M, 128);
+  p.MNbB = (int)cdiv(N, 128);
+  if (query_device) {
+    int cus = 0;
+    st = device_check(&pr->dev, &cus);
+    if (st != MXG_OK) return st;
+    configure(pr, cus);
+  }
+  return MXG_OK;
+}
+
+// Null and alignment checks of the operands a prepared launch reads and writes.
+int check_ptrs(const Prepared& pr, const void* A, const void* B, const void* SFA, const void* SFB, const void* C,
+               const void* Amax) {
+  if (!Amax || (pr.need_a && (!A || !SFA || !B || !SFB)) || (pr.need_c && !C)) return MXG_ERR_NULL;
+  if (!aligned16(Amax) || (pr.need_a && (!aligned16(A) || !aligned16(SFA) || !aligned16(B) || !aligned16(SFB))) ||
+      (pr.need_c && !aligned16(C)))
+    return MXG_ERR_ALIGN;
+  return MXG_OK;
+}
+
+int launch_prepared(const Prepared& pr, const void* A, const void* B, const uint8_t* SFA, const uint8_t* SFB,
+                    float* C, float* Amax, hipStream_t s) {
+  if (!pr.accumulate) {
+    hipLaunchKernelGGL(mxg::amax_reset_kernel, dim3(1), dim3(64), 0, s, reinterpret_cast<unsigned*>(Amax));
+    if (hipGetLastError() != hipSuccess) return MXG_ERR_LAUNCH;
+  }
+  if (!pr.need_c) return MXG_OK;
+  mxg::Params p = pr.p;
+  p.A = static_cast<const uint8_t*>(A);
+  p.B = static_cast<const uint8_t*>(B);
+  p.SFA = SFA;
+  p.SFB = SFB;
+  p.C = C;
+  p.amax_bits = reinterpret_cast<unsigned*>(Amax);
+  const int sf = pr.sf, fa = pr.fa, fb = pr.fb;
+  const int64_t grid = pr.grid;
+  hipError_t e;
+  if (pr.kind == 1) {
+    if (pr.fp8) e = launch_mode<mxg::kModeFp8, 1, 0>(p, sf, fa, fb, grid, s);
+    else if (pr.ct == 1) e = launch_mode<mxg::kModeBf16, 1, 1>(p, sf, fa, fb, grid, s);
+    else if (pr.ct == 2) e = launch_mode<mxg::kModeBf16, 1, 2>(p, sf, fa, fb, grid, s);
+    else e = launch_mode<mxg::kModeBf16, 1, 0>(p, sf, fa, fb, grid, s);
+  } else {
+    if (pr.fp8) e = launch_mode<mxg::kModeFp8, 0, 0>(p, sf, fa, fb, grid, s);
+    else if (pr.ct == 1) e = launch_mode<mxg::kModeBf16, 0, 1>(p, sf, fa, fb, grid, s);
+    else if (pr.ct == 2) e = launch_mode<mxg::kModeBf16, 0, 2>(p, sf, fa, fb, grid, s);
+    else e = launch_mode<mxg::kModeBf16, 0, 0>(p, sf, fa, fb, grid, s);
+  }
+  return e == hipSuccess ? MXG_OK : MXG_ERR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -216,78 +333,45 @@ int mxgemm_amax_reset(float* Amax, void* stream) {
 int mxgemm_amax_ex(const void* A, const void* B, const uint8_t* SFA, const uint8_t* SFB, float* C, float* Amax,
                    int64_t M, int64_t N, int64_t K, int64_t L, int sf_vec_size, int a_fmt, int b_fmt,
                    unsigned flags, void* stream) {
-  int st = check_sizes(M, N, K, L, sf_vec_size, a_fmt, b_fmt);
+  Prepared pr;
+  int st = prepare(&pr, M, N, K, L, sf_vec_size, a_fmt, b_fmt, flags, /*query_device=*/false);
   if (st != MXG_OK) return st;
-  const unsigned tile_flags = flags & (MXG_FLAG_TILE_128 | MXG_FLAG_TILE_256);
-  const unsigned c_flags = flags & (MXG_FLAG_C_BF16 | MXG_FLAG_C_F16);
-  if (flags & ~(unsigned)(MXG_FLAG_AMAX_ACCUMULATE | MXG_FLAG_FP8_MFMA | MXG_FLAG_TILE_128 | MXG_FLAG_TILE_256 |
-                          MXG_FLAG_C_BF16 | MXG_FLAG_C_F16))
-    return MXG_ERR_FLAGS;
-  if (tile_flags & (tile_flags - 1)) return MXG_ERR_FLAGS;  // more than one tile flag
-  if (c_flags & (c_flags - 1)) return MXG_ERR_FLAGS;        // both 16-bit C types
-  if (c_flags && (flags & MXG_FLAG_FP8_MFMA)) return MXG_ERR_FLAGS;  // 16-bit C: bf16 datapath only
-  // A, B and the scales are read only when there is a non-empty C and a non-empty K
-  const bool need_c = M > 0 && N > 0 && L > 0;
-  const bool need_a = need_c && K > 0, need_b = need_a;
-  if (!Amax || (need_a && (!A || !SFA)) || (need_b && (!B || !SFB)) || (need_c && !C)) return MXG_ERR_NULL;
-  if (!aligned16(Amax) || (need_a && (!aligned16(A) || !aligned16(SFA))) ||
-      (need_b && (!aligned16(B) || !aligned16(SFB))) || (need_c && !aligned16(C)))
-    return MXG_ERR_ALIGN;
-
+  st = check_ptrs(pr, A, B, SFA, SFB, C, Amax);
+  if (st != MXG_OK) return st;
   int dev = 0, cus = 0;
   st = device_check(&dev, &cus);
   if (st != MXG_OK) return st;
-  if (!on_device(Amax, dev) || (need_a && (!on_device(A, dev) || !on_device(SFA, dev))) ||
-      (need_b && (!on_device(B, dev) || !on_device(SFB, dev))) || (need_c && !on_device(C, dev)))
+  if (!on_device(Amax, dev) || (pr.need_a && (!on_device(A, dev) || !on_device(SFA, dev) || !on_device(B, dev) ||
+                                               !on_device(SFB, dev))) ||
+      (pr.need_c && !on_device(C, dev)))
     return MXG_ERR_DEVICE;
+  configure(&pr, cus);
+  return launch_prepared(pr, A, B, SFA, SFB, C, Amax, (hipStream_t)stream);
+}
 
-  hipStream_t s = (hipStream_t)stream;
-  if (!(flags & MXG_FLAG_AMAX_ACCUMULATE)) {
-    hipLaunchKernelGGL(mxg::amax_reset_kernel, dim3(1), dim3(64), 0, s, reinterpret_cast<unsigned*>(Amax));
-    if (hipGetLastError() != hipSuccess) return MXG_ERR_LAUNCH;
-  }
-  if (!need_c) return MXG_OK;
+int mxgemm_plan_init(mxgemm_plan* plan, int64_t M, int64_t N, int64_t K, int64_t L, int sf_vec_size, int a_fmt,
+                     int b_fmt, unsigned flags) {
+  if (!plan) return MXG_ERR_NULL;
+  static_assert(sizeof(Prepared) <= sizeof(mxgemm_plan), "mxgemm_plan too small for the prepared launch");
+  memset(plan, 0, sizeof(*plan));
+  Prepared pr;
+  int st = prepare(&pr, M, N, K, L, sf_vec_size, a_fmt, b_fmt, flags, /*query_device=*/true);
+  if (st != MXG_OK) return st;
+  memcpy(plan, &pr, sizeof(pr));
+  return MXG_OK;
+}
 
-  mxg::Params p;
-  p.A = static_cast<const uint8_t*>(A);
-  p.B = static_cast<const uint8_t*>(B);
-  p.SFA = SFA;
-  p.SFB = SFB;
-  p.C = C;
-  p.amax_bits = reinterpret_cast<unsigned*>(Amax);
-  p.M = (int)M;
-  p.N = (int)N;
-  p.K = (int)K;
-  p.L = (int)L;
-  p.Kb = (int)cdiv(K, sf_vec_size);
-  p.Kg = (int)cdiv(K, 4 * sf_vec_size);
-  p.MNbA = (int)cdiv(M, 128);
-  p.MNbB = (int)cdiv(N, 128);
-  Config cfg = choose(M, N, K, L, cus);
-  if (flags & MXG_FLAG_TILE_128) cfg = kSmall;
-  if ((flags & MXG_FLAG_TILE_256) && K > 0) cfg = kBig;
-  p.tilesM = (int)cdiv(M, cfg.tile_m);
-  p.tilesN = (int)cdiv(N, cfg.tile_n);
-  p.ksteps = (int)cdiv(K, 128);
-  p.num_tiles = (int)(L * p.tilesM * p.tilesN);
-  const int64_t grid = grid_for(p.num_tiles, cus, cfg.per_cu);
-  p.xcd_remap = (grid % 8 == 0) ? 1 : 0;
-
-  const bool fp8 = (flags & MXG_FLAG_FP8_MFMA) != 0;
-  const int ct = (flags & MXG_FLAG_C_BF16) ? 1 : (flags & MXG_FLAG_C_F16) ? 2 : 0;
-  hipError_t e;
-  if (cfg.kind == 1) {
-    if (fp8) e = launch_mode<mxg::kModeFp8, 1, 0>(p, sf_vec_size, a_fmt, b_fmt, grid, s);
-    else if (ct == 1) e = launch_mode<mxg::kModeBf16, 1, 1>(p, sf_vec_size, a_fmt, b_fmt, grid, s);
-    else if (ct == 2) e = launch_mode<mxg::kModeBf16, 1, 2>(p, sf_vec_size, a_fmt, b_fmt, grid, s);
-    else e = launch_mode<mxg::kModeBf16, 1, 0>(p, sf_vec_size, a_fmt, b_fmt, grid, s);
-  } else {
-    if (fp8) e = launch_mode<mxg::kModeFp8, 0, 0>(p, sf_vec_size, a_fmt, b_fmt, grid, s);
-    else if (ct == 1) e = launch_mode<mxg::kModeBf16, 0, 1>(p, sf_vec_size, a_fmt, b_fmt, grid, s);
-    else if (ct == 2) e = launch_mode<mxg::kModeBf16, 0, 2>(p, sf_vec_size, a_fmt, b_fmt, grid, s);
-    else e = launch_mode<mxg::kModeBf16, 0, 0>(p, sf_vec_size, a_fmt, b_fmt, grid, s);
-  }
-  return e == hipSuccess ? MXG_OK : MXG_ERR_LAUNCH;
+int mxgemm_plan_execute(const mxgemm_plan* plan, const void* A, const void* B, const uint8_t* SFA,
+                        const uint8_t* SFB, float* C, float* Amax, void* stream) {
+  if (!plan) return MXG_ERR_NULL;
+  Prepared pr;
+  memcpy(&pr, plan, sizeof(pr));
+  if (pr.magic != kPlanMagic) return MXG_ERR_NULL;  // never initialised (or not by mxgemm_plan_init)
+  int st = check_ptrs(pr, A, B, SFA, SFB, C, Amax);
+  if (st != MXG_OK) return st;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != pr.dev) return MXG_ERR_DEVICE;
+  return launch_prepared(pr, A, B, SFA, SFB, C, Amax, (hipStream_t)stream);
 }
 
 int mxgemm_mx_quantize(const float* X, void* Q, uint8_t* SF, int64_t MN, int64_t K, int64_t L, int sf_vec_size,

@@ -185,6 +185,35 @@ int mxgemm_launch_config(int64_t M, int64_t N, int64_t K, int64_t L, int sf_vec_
                          int* tile_m, int* tile_n, int64_t* grid);
 
 /*
+ * Plans ("GEMM + Amax (SM100)", sections on the class API: check_support,
+ * compile, then execute per call, and its note on per-launch CPU cost).
+ * mxgemm_plan_init validates sizes, formats and flags once (the checks of
+ * mxgemm_check_support plus the flag rules of mxgemm_amax_ex), queries the
+ * current device and fixes the tile configuration.  mxgemm_plan_execute then
+ * runs mxgemm_amax_ex with those sizes and flags on the given buffers,
+ * checking only null pointers, 16-byte alignment and that the current device
+ * is the plan's; it does not ask HIP where each pointer lives, so the caller
+ * guarantees the buffers are device memory of that device (as the pages'
+ * execute takes tensors already placed for the compiled kernel).
+ *
+ * mxgemm_plan is plain caller-owned memory (no allocation, nothing to free);
+ * a plan may be copied and used from several threads and streams.  Results
+ * are identical to mxgemm_amax_ex with the same arguments.  Errors:
+ * init returns mxgemm_amax_ex's validation statuses (and MXG_ERR_DEVICE
+ * without a gfx950 device); execute returns MXG_ERR_NULL (also for a plan
+ * never initialised), MXG_ERR_ALIGN, MXG_ERR_DEVICE (another current
+ * device) or MXG_ERR_LAUNCH.
+ */
+typedef struct mxgemm_plan {
+  uint64_t opaque[32];
+} mxgemm_plan;
+
+int mxgemm_plan_init(mxgemm_plan* plan, int64_t M, int64_t N, int64_t K, int64_t L, int sf_vec_size,
+                     int a_fmt, int b_fmt, unsigned flags);
+int mxgemm_plan_execute(const mxgemm_plan* plan, const void* A, const void* B, const uint8_t* SFA,
+                        const uint8_t* SFB, float* C, float* Amax, void* stream);
+
+/*
  * mxgemm_mx_quantize -- MX block quantisation of float32 data into the
  * GEMM's input form: element codes plus E8M0 block scales in the physical
  * atom layout ("GEMM + RoPE + MXFP8 Projection (SM100)", section

@@ -147,3 +147,24 @@ def test_rowwise_repack_errors_before_device_work(lib):
     assert f(good, good, 128, 128, 1, 8, None) == lib.MXG_ERR_SFVEC
     assert f(good, good, -3, 128, 1, 32, None) == lib.MXG_ERR_SHAPE
     assert f(None, None, 0, 128, 1, 32, None) == lib.MXG_OK
+
+
+def test_plan_validation_before_device_work(lib):
+    c = ctypes.CDLL(lib.LIB_PATH)
+    init, ex = c.mxgemm_plan_init, c.mxgemm_plan_execute
+    vp, i64, ci, cu = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint
+    init.argtypes = [vp, i64, i64, i64, i64, ci, ci, ci, cu]
+    init.restype = ci
+    ex.argtypes = [vp] * 8
+    ex.restype = ci
+    plan = (ctypes.c_uint64 * 32)()
+    assert init(None, 256, 256, 256, 1, 32, 0, 0, 0) == lib.MXG_ERR_NULL
+    assert init(plan, 256, 256, 200, 1, 32, 0, 0, 0) == lib.MXG_ERR_ALIGN
+    assert init(plan, 256, 256, 256, 1, 64, 0, 0, 0) == lib.MXG_ERR_SFVEC
+    assert init(plan, 256, 256, 256, 1, 32, 0, 0, 96) == lib.MXG_ERR_FLAGS
+    assert init(plan, -1, 256, 256, 1, 32, 0, 0, 0) == lib.MXG_ERR_SHAPE
+    # a plan that was never initialised is refused before any device call
+    zero = (ctypes.c_uint64 * 32)()
+    good = 0x7F0000000000
+    assert ex(zero, good, good, good, good, good, good, None) == lib.MXG_ERR_NULL
+    assert ex(None, good, good, good, good, good, good, None) == lib.MXG_ERR_NULL
