@@ -27,15 +27,17 @@ Every function has a pin in ``tests/test_oracle_*.py``; see each module's
 header for which pin covers it.
 """
 
-from .codecs import decode, decode_e4m3, decode_e5m2, decode_e8m0, FMT_E4M3, FMT_E5M2
+from .codecs import (decode, decode_e4m3, decode_e5m2, decode_e8m0, decode_e2m1, unpack_e2m1, element_codes,
+                     bytes_per_row, FMT_E4M3, FMT_E5M2, FMT_E2M1)
 from .sf_atom import sf_physical_shape, sf_logical_shape, sf_logical_view, expand_scales
 from .gemm_amax import (dequantize, gemm_amax, gemm_amax_loops, gemm_rows, gemm_entries,
                         amax_of)
-from .mx_quantize import mx_quantize, block_max, block_exponent, encode_rne, place_scales
+from .mx_quantize import mx_quantize, block_max, block_exponent, encode_rne, place_scales, pack_e2m1
 
 __all__ = [
-    "decode", "decode_e4m3", "decode_e5m2", "decode_e8m0", "FMT_E4M3", "FMT_E5M2",
+    "decode", "decode_e4m3", "decode_e5m2", "decode_e8m0", "decode_e2m1", "unpack_e2m1", "element_codes",
+    "bytes_per_row", "FMT_E4M3", "FMT_E5M2", "FMT_E2M1",
     "sf_physical_shape", "sf_logical_shape", "sf_logical_view", "expand_scales",
     "dequantize", "gemm_amax", "gemm_amax_loops", "gemm_rows", "gemm_entries", "amax_of",
-    "mx_quantize", "block_max", "block_exponent", "encode_rne", "place_scales",
+    "mx_quantize", "block_max", "block_exponent", "encode_rne", "place_scales", "pack_e2m1",
 ]

@@ -16,8 +16,11 @@ Microscaling (MX) format definitions those dtype names refer to:
 * E8M0 (unsigned exponent): value 2^(byte - 127); byte 255 is NaN; no sign,
   no zero.
 
-Each decoder is a 256-entry float64 table built one code at a time from these
-bit fields; every entry is exact in float64.
+* E2M1 (packed FP4, two per byte): sign, 2 exponent bits (bias 1), 1
+  mantissa bit; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; no inf or NaN.
+
+Each decoder is a float64 table (256 entries; 16 for E2M1) built one code at
+a time from these bit fields; every entry is exact in float64.
 
 Pins: ``tests/test_oracle_codecs.py`` compares all 256 codes of each format
 with torch's own float8 dtypes (an independent library decoder) and checks
@@ -30,9 +33,11 @@ import numpy as np
 
 FMT_E4M3 = 0
 FMT_E5M2 = 1
+FMT_E2M1 = 2
 
 _FMT_NAMES = {"e4m3": FMT_E4M3, "float8_e4m3fn": FMT_E4M3,
-              "e5m2": FMT_E5M2, "float8_e5m2": FMT_E5M2}
+              "e5m2": FMT_E5M2, "float8_e5m2": FMT_E5M2,
+              "e2m1": FMT_E2M1, "float4_e2m1fn_x2": FMT_E2M1}
 
 
 def _e4m3(code):
@@ -61,6 +66,18 @@ def _e5m2(code):
     return sign * math.ldexp(4 + man, exp - 17)
 
 
+def _e2m1(code):
+    # 4-bit: sign, 2 exponent bits (bias 1), 1 mantissa bit; no inf or NaN
+    sign = -1.0 if code & 0x8 else 1.0
+    exp = (code >> 1) & 0x3
+    man = code & 0x1
+    if exp == 0:
+        # subnormal: man/2 * 2^(1 - 1)
+        return sign * math.ldexp(man, -1)
+    # normal: (2 + man)/2 * 2^(exp - 1)
+    return sign * math.ldexp(2 + man, exp - 2)
+
+
 def _e8m0(code):
     if code == 0xFF:
         return math.nan
@@ -70,13 +87,14 @@ def _e8m0(code):
 E4M3_TABLE = np.array([_e4m3(c) for c in range(256)], dtype=np.float64)
 E5M2_TABLE = np.array([_e5m2(c) for c in range(256)], dtype=np.float64)
 E8M0_TABLE = np.array([_e8m0(c) for c in range(256)], dtype=np.float64)
+E2M1_TABLE = np.array([_e2m1(c) for c in range(16)], dtype=np.float64)
 
 
 def fmt_id(fmt):
     """Map a format name or id to FMT_E4M3 / FMT_E5M2."""
     if isinstance(fmt, str):
         return _FMT_NAMES[fmt.lower()]
-    if fmt in (FMT_E4M3, FMT_E5M2):
+    if fmt in (FMT_E4M3, FMT_E5M2, FMT_E2M1):
         return int(fmt)
     raise ValueError(f"unknown element format {fmt!r}")
 
@@ -93,6 +111,36 @@ def decode_e8m0(codes):
     return E8M0_TABLE[np.asarray(codes, dtype=np.uint8)]
 
 
+def decode_e2m1(nibbles):
+    return E2M1_TABLE[np.asarray(nibbles, dtype=np.uint8) & 0xF]
+
+
+def unpack_e2m1(packed, k):
+    """Packed E2M1 bytes (..., ceil(k/2)) -> one 4-bit code per element (..., k).
+
+    Reading (the pages call the container "packed fp4x2" without fixing the
+    order): element 2i is the low nibble of byte i, element 2i+1 the high one."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(packed.shape[:-1] + (2 * packed.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = packed & 0xF
+    out[..., 1::2] = packed >> 4
+    return out[..., :k]
+
+
+def bytes_per_row(k, fmt):
+    """Bytes of one operand row of K elements: K for the 8-bit formats, K/2 for packed E2M1."""
+    return (k + 1) // 2 if fmt_id(fmt) == FMT_E2M1 else k
+
+
+def element_codes(codes, fmt, rows, k, l):
+    """Per-element codes (L, rows, K) of an operand buffer (L, rows, bytes_per_row(K))."""
+    c = np.asarray(codes, dtype=np.uint8).reshape(l, rows, bytes_per_row(k, fmt))
+    return unpack_e2m1(c, k) if fmt_id(fmt) == FMT_E2M1 else c
+
+
 def decode(codes, fmt):
-    """Decode element codes of format ``fmt`` ('e4m3'/'e5m2' or 0/1) to float64."""
-    return decode_e4m3(codes) if fmt_id(fmt) == FMT_E4M3 else decode_e5m2(codes)
+    """Decode per-element codes of format ``fmt`` (E4M3, E5M2, or E2M1 nibbles) to float64."""
+    f = fmt_id(fmt)
+    if f == FMT_E2M1:
+        return decode_e2m1(codes)
+    return decode_e4m3(codes) if f == FMT_E4M3 else decode_e5m2(codes)

@@ -31,7 +31,7 @@ swap gives C^T; K-block permutation invariance; amax closed form.
 
 import numpy as np
 
-from .codecs import decode
+from .codecs import decode, element_codes
 from .sf_atom import expand_scales
 
 
@@ -41,7 +41,7 @@ def _cdiv(a, b):
 
 def dequantize(codes, fmt, sf_phys, rows, k, l, sf_vec_size):
     """A_hat or B_hat in float64, shape (L, rows, K), from codes (L, rows, K) and the physical SF."""
-    codes = np.asarray(codes, dtype=np.uint8).reshape(l, rows, k)
+    codes = element_codes(codes, fmt, rows, k, l)
     scale = expand_scales(sf_phys, rows, k, l, sf_vec_size)          # (L, rows, Kb)
     per_k = np.repeat(scale, sf_vec_size, axis=2)[:, :, :k]           # (L, rows, K)
     return decode(codes, fmt) * per_k
@@ -92,8 +92,8 @@ def gemm_rows(a, b, sfa, sfb, m, n, k, l, sf_vec_size, a_fmt, b_fmt, batch, row_
     can sample outputs of shapes too large for the full oracle.
     """
     row_idx = np.asarray(row_idx, dtype=np.int64)
-    a3 = np.asarray(a, dtype=np.uint8).reshape(l, m, k)
-    b3 = np.asarray(b, dtype=np.uint8).reshape(l, n, k)
+    a3 = element_codes(a, a_fmt, m, k, l)
+    b3 = element_codes(b, b_fmt, n, k, l)
     sa = expand_scales(sfa, m, k, l, sf_vec_size)[batch, row_idx]       # (r, Kb)
     sb = expand_scales(sfb, n, k, l, sf_vec_size)[batch]                # (N, Kb)
     ah = decode(a3[batch, row_idx], a_fmt) * np.repeat(sa, sf_vec_size, axis=1)[:, :k]
@@ -109,8 +109,8 @@ def gemm_entries(a, b, sfa, sfb, m, n, k, l, sf_vec_size, a_fmt, b_fmt, idx_l, i
     idx_l = np.asarray(idx_l, dtype=np.int64)
     idx_m = np.asarray(idx_m, dtype=np.int64)
     idx_n = np.asarray(idx_n, dtype=np.int64)
-    a3 = np.asarray(a, dtype=np.uint8).reshape(l, m, k)
-    b3 = np.asarray(b, dtype=np.uint8).reshape(l, n, k)
+    a3 = element_codes(a, a_fmt, m, k, l)
+    b3 = element_codes(b, b_fmt, n, k, l)
     sa_all = expand_scales(sfa, m, k, l, sf_vec_size)
     sb_all = expand_scales(sfb, n, k, l, sf_vec_size)
     ah = decode(a3[idx_l, idx_m], a_fmt) * np.repeat(sa_all[idx_l, idx_m], sf_vec_size, axis=1)[:, :k]

@@ -14,7 +14,7 @@ rule the GEMM's own test configurations state for their inputs (a scale of
   elements past K in the last block are absent;
 * bm = max |x| over the block;
 * e = the smallest integer with FMAX * 2^e >= bm, clamped to [-127, 127]
-  (FMAX = 448 for E4M3, 57344 for E5M2); e = 0 when bm = 0;
+  (FMAX = 448 for E4M3, 57344 for E5M2, 6 for E2M1); e = 0 when bm = 0;
 * scale byte = e + 127;
 * code = x * 2^-e rounded to the nearest finite code of the format, ties to
   the code with the even mantissa (the even code), sign kept (a negative
@@ -40,10 +40,10 @@ agreement with the separately written quantiser of the input generator.
 
 import numpy as np
 
-from .codecs import FMT_E4M3, FMT_E5M2, decode
+from .codecs import FMT_E2M1, FMT_E4M3, FMT_E5M2, decode
 from .sf_atom import sf_logical_view, sf_physical_shape
 
-FMAX = {FMT_E4M3: 448.0, FMT_E5M2: 57344.0}
+FMAX = {FMT_E4M3: 448.0, FMT_E5M2: 57344.0, FMT_E2M1: 6.0}
 
 
 def _cdiv(a, b):
@@ -80,7 +80,7 @@ def block_exponent(bm, fmt):
 
 def _positive_table(fmt):
     """Finite non-negative values of the format in code order (which is value order) and their codes."""
-    codes = np.arange(128, dtype=np.uint8)
+    codes = np.arange(8 if fmt == FMT_E2M1 else 128, dtype=np.uint8)
     vals = decode(codes, fmt)
     keep = np.isfinite(vals)
     vals, codes = vals[keep], codes[keep]
@@ -101,7 +101,8 @@ def encode_rne(q, fmt):
     pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (codes[hi] % 2 == 0))
     pick_hi = np.where(a == vals[hi], True, pick_hi)      # exact hits
     c = np.where(pick_hi, codes[hi], codes[lo]).astype(np.uint8)
-    return np.where(np.signbit(q), c | 0x80, c).astype(np.uint8)
+    sign = 0x8 if fmt == FMT_E2M1 else 0x80
+    return np.where(np.signbit(q), c | sign, c).astype(np.uint8)
 
 
 def place_scales(scale_bytes, mn, k, l, sf_vec_size, pad_byte=127):
@@ -117,11 +118,18 @@ def place_scales(scale_bytes, mn, k, l, sf_vec_size, pad_byte=127):
     return phys
 
 
+def pack_e2m1(nibbles):
+    """One 4-bit code per element (..., K), K even -> packed bytes (..., K/2), element 2i low."""
+    n = np.asarray(nibbles, dtype=np.uint8)
+    return (n[..., 0::2] | (n[..., 1::2] << 4)).astype(np.uint8)
+
+
 def mx_quantize(x, sf_vec_size, fmt):
     """MX-quantise float32 x (L, MN, K) or (MN, K).
 
     Returns (codes uint8 (L, MN, K), physical SF buffer uint8 (flat), per-block
-    exponents int64 (L, MN, ceil(K/sf))).
+    exponents int64 (L, MN, ceil(K/sf))).  For E2M1 the codes are one 4-bit
+    code per element (pack with ``pack_e2m1``).
     """
     x = np.asarray(x, dtype=np.float32)
     if x.ndim == 2:

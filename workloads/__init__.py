@@ -42,7 +42,8 @@ import numpy as np
 
 FMT_E4M3 = 0
 FMT_E5M2 = 1
-FMAX = {FMT_E4M3: 448.0, FMT_E5M2: 57344.0}
+FMT_E2M1 = 2     # packed FP4: two elements per byte, element 2i in the low nibble
+FMAX = {FMT_E4M3: 448.0, FMT_E5M2: 57344.0, FMT_E2M1: 6.0}
 
 WORKLOADS = {
     1: dict(name="tiny", M=256, N=256, K=256, L=1, sf=32, a_fmt=FMT_E4M3, b_fmt=FMT_E4M3),
@@ -88,8 +89,24 @@ def block_exponents(x, sf_vec_size, fmt):
     return e.astype(np.int32)
 
 
+def _e2m1_rne(q):
+    """Nearest E2M1 value code (4-bit, sign in bit 3) of float64 q with |q| <= 6, ties to even.
+
+    The E2M1 grid is spaced 0.5 on [0, 2), 1 on [2, 4) and 2 on [4, 6]; numpy's round is
+    half-to-even, and the even multiple is always the code with the even mantissa."""
+    a = np.abs(q)
+    step = np.where(a < 2.0, 0.5, np.where(a < 4.0, 1.0, 2.0))
+    v = np.round(a / step) * step
+    grid = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    code = np.searchsorted(grid, v).astype(np.uint8)
+    assert np.array_equal(grid[code], v)
+    return np.where(np.signbit(q), code | 0x8, code).astype(np.uint8)
+
+
 def mx_quantize(x, sf_vec_size, fmt):
-    """MX-quantise float32 x (L, rows, K): returns (codes uint8 (L,rows,K), scale bytes uint8 (L,rows,Kb))."""
+    """MX-quantise float32 x (L, rows, K): returns (codes uint8 (L,rows,K), scale bytes uint8 (L,rows,Kb)).
+
+    E2M1 codes come packed, (L, rows, K/2) bytes."""
     import torch
     x = np.ascontiguousarray(x, dtype=np.float32)
     l, rows, k = x.shape
@@ -98,6 +115,10 @@ def mx_quantize(x, sf_vec_size, fmt):
     q = np.ldexp(x.astype(np.float64), -per_k)
     fmax = FMAX[fmt]
     q = np.clip(q, -fmax, fmax).astype(np.float32)
+    if fmt == FMT_E2M1:
+        assert k % 2 == 0, "packed FP4 rows need an even K"
+        n = _e2m1_rne(q.astype(np.float64))
+        return (n[..., 0::2] | (n[..., 1::2] << 4)).astype(np.uint8), (e + 127).astype(np.uint8)
     codes = torch.from_numpy(q).to(_torch_fp8(fmt)).view(torch.uint8).numpy()
     return codes, (e + 127).astype(np.uint8)
 
