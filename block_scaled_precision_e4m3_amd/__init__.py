@@ -26,6 +26,7 @@ LIB_PATH = os.path.join(_PKG_DIR, "libmxgemm.so")
 
 MXG_FMT_E4M3 = 0
 MXG_FMT_E5M2 = 1
+MXG_FMT_E2M1 = 2
 MXG_FLAG_AMAX_ACCUMULATE = 1
 MXG_FLAG_FP8_MFMA = 2
 MXG_FLAG_TILE_128 = 4
@@ -323,7 +324,7 @@ __all__ = [
     "mxgemm_amax", "mxgemm_amax_ex", "mxgemm_amax_reset", "mxgemm_check_support", "mxgemm_sf_bytes",
     "mxgemm_launch_config", "mxgemm_strerror", "gemm_amax", "LIB_PATH", "EXPORTED",
     "mxgemm_mx_quantize", "mx_quantize", "mxgemm_sf_rowwise_to_atoms", "sf_from_rowwise", "Plan",
-    "MXG_FMT_E4M3", "MXG_FMT_E5M2", "MXG_FLAG_AMAX_ACCUMULATE", "MXG_FLAG_FP8_MFMA", "MXG_FLAG_TILE_128",
+    "MXG_FMT_E4M3", "MXG_FMT_E5M2", "MXG_FMT_E2M1", "MXG_FLAG_AMAX_ACCUMULATE", "MXG_FLAG_FP8_MFMA", "MXG_FLAG_TILE_128",
     "MXG_FLAG_TILE_256", "MXG_FLAG_C_BF16", "MXG_FLAG_C_F16", "MxgemmError", "MxgemmValueError",
     "MxgemmRuntimeError",
 ]

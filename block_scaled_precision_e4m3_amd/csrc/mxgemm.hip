@@ -36,8 +36,11 @@ bool fits_i32(int64_t v) { return v >= 0 && v <= 0x7FFFFFFFLL; }
 int check_sizes(int64_t M, int64_t N, int64_t K, int64_t L, int sf, int a_fmt, int b_fmt) {
   if (M < 0 || N < 0 || K < 0 || L < 0) return MXG_ERR_SHAPE;
   if (sf != 16 && sf != 32) return MXG_ERR_SFVEC;
-  if ((a_fmt != MXG_FMT_E4M3 && a_fmt != MXG_FMT_E5M2) || (b_fmt != MXG_FMT_E4M3 && b_fmt != MXG_FMT_E5M2))
-    return MXG_ERR_FMT;
+  const auto known = [](int f) { return f == MXG_FMT_E4M3 || f == MXG_FMT_E5M2 || f == MXG_FMT_E2M1; };
+  if (!known(a_fmt) || !known(b_fmt)) return MXG_ERR_FMT;
+  const bool fp4 = a_fmt == MXG_FMT_E2M1;
+  if (fp4 != (b_fmt == MXG_FMT_E2M1)) return MXG_ERR_FMT;  // packed FP4 on both operands or neither
+  if (fp4 && sf != 32) return MXG_ERR_SFVEC;                // FP4: one E8M0 scale per 32 elements
   // kernel indices are 32-bit per dimension, byte offsets 64-bit
   if (!fits_i32(M) || !fits_i32(N) || !fits_i32(K) || !fits_i32(L)) return MXG_ERR_SHAPE;
   const int64_t lim = INT64_MAX / 8;
@@ -50,6 +53,7 @@ int check_sizes(int64_t M, int64_t N, int64_t K, int64_t L, int sf, int a_fmt, i
   // tile and tile-step counts are 32-bit in the kernels
   if (L * cdiv(M, 128) * cdiv(N, 128) * (cdiv(K, 128) + 1) > 0x7FFFFFFFLL) return MXG_ERR_SHAPE;
   if (K % 16 != 0) return MXG_ERR_ALIGN;
+  if (fp4 && K % 32 != 0) return MXG_ERR_ALIGN;             // packed rows of 16-byte multiples
   if (N % 4 != 0) return MXG_ERR_ALIGN;
   return MXG_OK;
 }
@@ -121,7 +125,11 @@ hipError_t launch_mode(const mxg::Params& p, int sf, int fa, int fb, int64_t gri
     else                                                                                               \
       hipLaunchKernelGGL((mxg::mxgemm_amax_kernel<SF, FA, FB, MODE, CT>), g, b, 0, s, p);              \
   } while (0)
-  if (sf == 32) {
+  if (fa == MXG_FMT_E2M1) {
+    // packed FP4: 256x256 kernel, bf16 datapath, sf = 32 (validated on the host)
+    if constexpr (KIND == 1 && MODE == mxg::kModeBf16) MXG_LAUNCH(32, 2, 2);
+    else return hipErrorInvalidValue;
+  } else if (sf == 32) {
     if (fa == 0 && fb == 0) MXG_LAUNCH(32, 0, 0);
     else if (fa == 0 && fb == 1) MXG_LAUNCH(32, 0, 1);
     else if (fa == 1 && fb == 0) MXG_LAUNCH(32, 1, 0);
@@ -190,13 +198,15 @@ int prepare(Prepared* pr, int64_t M, int64_t N, int64_t K, int64_t L, int sf_vec
 void configure(Prepared* pr, int cus) {
   mxg::Params& p = pr->p;
   const int64_t M = p.M, N = p.N, K = p.K, L = p.L;
+  const bool fp4 = pr->fa == MXG_FMT_E2M1;
   Config cfg = choose(M, N, K, L, cus);
   if (pr->flags & MXG_FLAG_TILE_128) cfg = kSmall;
   if ((pr->flags & MXG_FLAG_TILE_256) && K > 0) cfg = kBig;
+  if (fp4 && K > 0) cfg = kBig;  // packed FP4 runs on the 256x256 kernel only
   pr->kind = cfg.kind;
   p.tilesM = (int)cdiv(M, cfg.tile_m);
   p.tilesN = (int)cdiv(N, cfg.tile_n);
-  p.ksteps = (int)cdiv(K, 128);
+  p.ksteps = (int)cdiv(K, fp4 ? 256 : 128);  // 128 bytes of every row per step
   p.num_tiles = (int)(L * p.tilesM * p.tilesN);
   pr->grid = grid_for(p.num_tiles, cus, cfg.per_cu);
   p.xcd_remap = (pr->grid % 8 == 0) ? 1 : 0;
@@ -214,6 +224,8 @@ int prepare(Prepared* pr, int64_t M, int64_t N, int64_t K, int64_t L, int sf_vec
   if (tile_flags & (tile_flags - 1)) return MXG_ERR_FLAGS;  // more than one tile flag
   if (c_flags & (c_flags - 1)) return MXG_ERR_FLAGS;        // both 16-bit C types
   if (c_flags && (flags & MXG_FLAG_FP8_MFMA)) return MXG_ERR_FLAGS;  // 16-bit C: bf16 datapath only
+  if (a_fmt == MXG_FMT_E2M1 && (flags & MXG_FLAG_FP8_MFMA)) return MXG_ERR_FLAGS;  // FP4: bf16 datapath
+  if (a_fmt == MXG_FMT_E2M1 && K > 0 && (flags & MXG_FLAG_TILE_128)) return MXG_ERR_FLAGS;  // FP4: 256x256
   memset(pr, 0, sizeof(*pr));
   pr->magic = kPlanMagic;
   pr->flags = flags;
@@ -231,6 +243,7 @@ int prepare(Prepared* pr, int64_t M, int64_t N, int64_t K, int64_t L, int sf_vec
   p.N = (int)N;
   p.K = (int)K;
   p.L = (int)L;
+  p.Kbytes = (int)(a_fmt == MXG_FMT_E2M1 ? K / 2 : K);
   p.Kb = (int)cdiv(K, sf_vec_size);
   p.Kg = (int)cdiv(K, 4 * sf_vec_size);
   p.MNbA = (int)cdiv(M, 128);
@@ -268,7 +281,11 @@ int launch_prepared(const Prepared& pr, const void* A, const void* B, const uint
   p.SFB = SFB;
   p.C = C;
   p.amax_bits = reinterpret_cast<unsigned*>(Amax);
-  const int sf = pr.sf, fa = pr.fa, fb = pr.fb;
+  const int sf = pr.sf;
+  // K == 0 never reads A or B, so a packed-FP4 problem then runs the 128x128
+  // kernel instantiated for an 8-bit format
+  const bool fp4_empty = pr.fa == MXG_FMT_E2M1 && pr.kind == 0;
+  const int fa = fp4_empty ? MXG_FMT_E4M3 : pr.fa, fb = fp4_empty ? MXG_FMT_E4M3 : pr.fb;
   const int64_t grid = pr.grid;
   hipError_t e;
   if (pr.kind == 1) {
@@ -441,7 +458,7 @@ const char* mxgemm_strerror(int status) {
     case MXG_ERR_SHAPE: return "invalid size (negative, or offsets overflow)";
     case MXG_ERR_ALIGN: return "misaligned buffer (16 bytes), K not a multiple of 16, or N not a multiple of 4";
     case MXG_ERR_SFVEC: return "sf_vec_size must be 16 or 32";
-    case MXG_ERR_FMT: return "element format must be MXG_FMT_E4M3 or MXG_FMT_E5M2";
+    case MXG_ERR_FMT: return "element format must be MXG_FMT_E4M3 or MXG_FMT_E5M2 (or MXG_FMT_E2M1 for both A and B)";
     case MXG_ERR_DEVICE: return "current device is not gfx950, or a buffer is not memory of the current device";
     case MXG_ERR_LAUNCH: return "HIP kernel launch failed";
     case MXG_ERR_FLAGS: return "unknown flag bit";

@@ -43,9 +43,10 @@ constexpr int kWN = kBN / 2;     // wave tile columns
 // into instruction issue; done early enough to land before the barrier)
 constexpr int kDmaSlices = 3;
 
-template <int SF>
+template <int SF, bool FP4>
 struct Layout {
-  static constexpr int NSF = SF == 32 ? 1 : 2;       // atoms per 128-row group per step
+  static constexpr int KE = FP4 ? 256 : 128;         // K elements per step (128 bytes per row)
+  static constexpr int NSF = KE / (4 * SF);          // atoms per 128-row group per step
   static constexpr int kSF = 2 * NSF * 512;          // atom bytes per operand per stage
   static constexpr int kOffB = kBM * kBK;            // A tile: 256 rows x 128 bytes
   static constexpr int kOffSFA = kOffB + kBN * kBK;  // B tile: 256 rows x 128 bytes
@@ -76,7 +77,11 @@ __device__ __forceinline__ unsigned sf_tail(unsigned d, int g, int Kb) {
 
 template <int SF, int FA, int FB, int MODE, int CT>
 __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) {
-  using Y = Layout<SF>;
+  // FA = FB = 2: packed FP4 (E2M1), bf16 datapath, sf = 32 (the host enforces it)
+  constexpr bool kFp4 = FA == 2;
+  static_assert(!kFp4 || (FB == 2 && SF == 32 && MODE == kModeBf16), "FP4: both operands, sf = 32, bf16 path");
+  using Y = Layout<SF, kFp4>;
+  static_assert(Y::NSF == 1 || Y::NSF == 2, "one or two scale atoms per 128-row group per step");
   constexpr int kEs = kCBytes<CT>;  // bytes per C element
   constexpr int NSF = Y::NSF;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * Y::kStage + Y::kEpiBytes];
@@ -115,7 +120,7 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
     g.a_off = (128 * wm + g.r) * kBK;
     g.b_off = Y::kOffB + (kWN * wn + g.r) * kBK;
     const int dma_row = ln >> 3;
-    g.row_k = (unsigned)(wave * 8 + dma_row) * (unsigned)p.K;
+    g.row_k = (unsigned)(wave * 8 + dma_row) * (unsigned)p.Kbytes;
     g.kchunk = (unsigned)(((ln & 7) ^ dma_row ^ (wave & 1)) << 4);
     g.sf_lane = 16u * (unsigned)(ln & 31);
     g.sf_rg = NSF == 1 ? (ln >> 5) : (wave >> 1);
@@ -151,10 +156,10 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   };
   auto dma_setup = [&](const Geo& g, const Tile& T, int kt, bool live, unsigned stage) {
     Dma d;
-    d.ra = make_rsrc(p.A + ((int64_t)T.l * p.M + T.m0) * p.K, live ? (unsigned)T.mvalid * (unsigned)p.K : 0u);
-    d.rb = make_rsrc(p.B + ((int64_t)T.l * p.N + T.n0) * p.K, live ? (unsigned)T.nvalid * (unsigned)p.K : 0u);
+    d.ra = make_rsrc(p.A + ((int64_t)T.l * p.M + T.m0) * p.Kbytes, live ? (unsigned)T.mvalid * (unsigned)p.Kbytes : 0u);
+    d.rb = make_rsrc(p.B + ((int64_t)T.l * p.N + T.n0) * p.Kbytes, live ? (unsigned)T.nvalid * (unsigned)p.Kbytes : 0u);
     const unsigned kk = (unsigned)(kt * kBK) + g.kchunk;
-    d.voff = kk < (unsigned)p.K ? g.row_k + kk : kOob;
+    d.voff = kk < (unsigned)p.Kbytes ? g.row_k + kk : kOob;
     const int mn0 = sf_is_b ? T.n0 : T.m0;
     const int mnb = sf_is_b ? p.MNbB : p.MNbA;
     const int g0 = mn0 >> 7;
@@ -167,7 +172,7 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   };
   // A/B DMA instruction q of this wave: q < 8 -> A group wave + 4q, else B
   // group wave + 4(q - 8)
-  const unsigned grp_stride = 32u * (unsigned)p.K;
+  const unsigned grp_stride = 32u * (unsigned)p.Kbytes;
   auto dma_ab = [&](const Dma& d, int q) {
     const int qq = q < 8 ? q : q - 8;
     const unsigned voff = d.voff + (unsigned)qq * grp_stride;
@@ -370,13 +375,14 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   };
 
   // --- bf16 datapath: steps pipelined across step boundaries -----------------
-  // Global step s reads ring stage s & 1.  The next step's scale dwords and
-  // first 32-K chunk are read, and its first MFMA slice converted, while the
-  // current step's last slice runs, so a step issues MFMAs from its first
-  // cycle.  A wave reads a stage for the last time in slice 4 of the stage's
-  // step (chunk 3) and has used that data by the end of slice 6.  One
-  // barrier per step, B' (after slice 6, right after the slice's MFMAs are
-  // queued, so its wait overlaps them).  Past B':
+  // Global step s reads ring stage s & 1; a step is S slices of 16 K (S = 8
+  // for the 8-bit formats, 16 for FP4), four 32-byte chunks per row.  The next
+  // step's scale dwords and first chunk are read, and its first MFMA slice
+  // converted, while the current step's last slice runs, so a step issues
+  // MFMAs from its first cycle.  A wave reads a stage for the last time in the
+  // first slice of chunk 3 and has used that data by the end of slice S-2.
+  // One barrier per step, B' (after slice S-2, right after the slice's MFMAs
+  // are queued, so its wait overlaps them).  Past B':
   //   * every wave's DMA of step s+1 has landed (each wave first waits for
   //     its own), so stage (s+1) & 1 may be read;
   //   * every wave is done with stage s & 1, so DMA into it may start: the
@@ -408,25 +414,37 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
 #pragma unroll
     for (int i = 0; i < kTN; ++i) rb[c & 1][i] = lds16(st + g.b_off + (((2 * c + g.h) ^ g.xr) << 4) + 4096 * i);
   };
-  // chunk c's scale: sf=32 -> block c (byte c); sf=16 -> block 2c+h, byte
-  // 2(c&1)+h of atom c>>1
+  // chunk c's scale: one atom per step (8-bit, sf=32) -> block c (byte c);
+  // two atoms (8-bit with sf=16, or FP4 with sf=32, whose 16-byte chunk holds
+  // 32 elements) -> block 2c+h, byte 2(c&1)+h of atom c>>1
   auto scales = [&](const Geo& g, int c) __attribute__((always_inline)) {
-    const int j = SF == 32 ? 0 : (c >> 1);
-    const unsigned k = SF == 32 ? (unsigned)c : (unsigned)(2 * (c & 1) + g.h);
+    const int j = NSF == 1 ? 0 : (c >> 1);
+    const unsigned k = NSF == 1 ? (unsigned)c : (unsigned)(2 * (c & 1) + g.h);
 #pragma unroll
     for (int i = 0; i < kTM; ++i) fa[i] = e8m0_byte_operand(sa[j][i], k);
 #pragma unroll
     for (int i = 0; i < kTN; ++i) fb[i] = e8m0_byte_operand(sb[j][i], k);
   };
-  // slice n = chunk n/2, bytes 0..7 (even n) or 8..15 (odd n) of each fragment
+  // 8-bit: slice n = chunk n/2, bytes 0..7 (even n) or 8..15 (odd n) of each
+  // fragment.  FP4: slice n = chunk n/4, dword n%4 (eight elements) of each
+  // fragment.  Either way A and B take the same K elements in the same order.
+  auto pick = [](const uint4& v, int t) { return t == 0 ? v.x : t == 1 ? v.y : t == 2 ? v.z : v.w; };
   auto convert = [&](int n) __attribute__((always_inline)) {
-    const int c = n >> 1, t = n & 1;
+    if constexpr (kFp4) {
+      const int c = n >> 2, t = n & 3;
 #pragma unroll
-    for (int i = 0; i < kTM; ++i)
-      ab[n & 1][i] = cvt8<FA>(t ? ra[c & 1][i].z : ra[c & 1][i].x, t ? ra[c & 1][i].w : ra[c & 1][i].y, fa[i]);
+      for (int i = 0; i < kTM; ++i) ab[n & 1][i] = cvt8_fp4(pick(ra[c & 1][i], t), fa[i]);
 #pragma unroll
-    for (int i = 0; i < kTN; ++i)
-      bb[n & 1][i] = cvt8<FB>(t ? rb[c & 1][i].z : rb[c & 1][i].x, t ? rb[c & 1][i].w : rb[c & 1][i].y, fb[i]);
+      for (int i = 0; i < kTN; ++i) bb[n & 1][i] = cvt8_fp4(pick(rb[c & 1][i], t), fb[i]);
+    } else {
+      const int c = n >> 1, t = n & 1;
+#pragma unroll
+      for (int i = 0; i < kTM; ++i)
+        ab[n & 1][i] = cvt8<FA>(t ? ra[c & 1][i].z : ra[c & 1][i].x, t ? ra[c & 1][i].w : ra[c & 1][i].y, fa[i]);
+#pragma unroll
+      for (int i = 0; i < kTN; ++i)
+        bb[n & 1][i] = cvt8<FB>(t ? rb[c & 1][i].z : rb[c & 1][i].x, t ? rb[c & 1][i].w : rb[c & 1][i].y, fb[i]);
+    }
   };
   // step 0's inputs (after its DMA, issued above, has landed everywhere)
   auto prime = [&]() __attribute__((always_inline)) {
@@ -447,12 +465,15 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
     const Geo g = geo(lane_opaque());
     const uint8_t* stn = lds + ((s & 1) ^ 1) * Y::kStage;
     const uint8_t* st = lds + (s & 1) * Y::kStage;
+    // slices of 16 K per step: 8 (8-bit) or 16 (FP4); kSpc per 32-byte chunk
+    constexpr int kSlices = kFp4 ? 16 : 8;
+    constexpr int kSpc = kSlices / 4;
     Dma d;
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      // chunk c+1 is read during slice 2c, a slice before its first
-      // conversion; chunk 0 of the next step after B'
-      if ((n & 1) == 0 && (n >> 1) < 3) load_raw(g, st, (n >> 1) + 1);
+    for (int n = 0; n < kSlices; ++n) {
+      // chunk c+1 is read during chunk c's first slice, a slice before its
+      // first conversion; chunk 0 of the next step after B'
+      if (n % kSpc == 0 && n / kSpc < 3) load_raw(g, st, n / kSpc + 1);
       // the DMA of step s+1, spread over slices 1 .. kDmaSlices
       if (n == 1) {
         d = dma_setup(g, nt, nkt, has_next, lds0 + (unsigned)(((s & 1) ^ 1) * Y::kStage));
@@ -464,8 +485,8 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
         for (int q = 0; q < kPer; ++q)
           if ((n - 1) * kPer + q < Y::kDma) dma_ab(d, (n - 1) * kPer + q);
       }
-      if (n < 7) {
-        if (((n + 1) & 1) == 0) scales(g, (n + 1) >> 1);
+      if (n < kSlices - 1) {
+        if ((n + 1) % kSpc == 0) scales(g, (n + 1) / kSpc);
         convert(n + 1);
       } else {
         // the next step's first slice (its inputs were read after B')
@@ -487,7 +508,7 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
         if (k < kTM + kTN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (n == 6) {
+      if (n == kSlices - 2) {
         // this wave's DMA of step s+1 (issued at the previous B') has landed
         wait_vm<0>();
         barrier();  // B'

@@ -35,6 +35,7 @@ struct Params {
   float* C;
   unsigned* amax_bits;
   int M, N, K, L;
+  int Kbytes;  // bytes of one A / B row: K, or K/2 for packed FP4 (E2M1)
   int Kb;      // ceil(K / sf): K-blocks
   int Kg;      // ceil(K / (4 sf)): atoms along K
   int MNbA;    // ceil(M / 128)
@@ -207,6 +208,19 @@ __device__ __forceinline__ void store_c4(const v4f& v, __amdgpu_buffer_rsrc_t rc
                                           0);
   else
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, __builtin_convertvector(v, v4h)), rc, voff, soff, 0);
+}
+
+// Eight packed E2M1 elements (one dword, element 2i in the low nibble of byte
+// i) to bf16 with the scale folded in: v_cvt_scalef32_pk_bf16_fp4 takes byte
+// `sel` and puts its low nibble in the first bf16 of the pair (checked on
+// MI355X for all 256 bytes and every byte select, scales 2^0, 2^-3, 2^5).
+__device__ __forceinline__ v8bf cvt8_fp4(unsigned w, float scale) {
+  v4u u;
+  u[0] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
+  u[1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
+  u[2] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
+  u[3] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
+  return __builtin_bit_cast(v8bf, u);
 }
 
 // Clears the Amax bits (queued before a GEMM that does not accumulate).

@@ -62,7 +62,14 @@ extern "C" {
 /* element formats of A and B */
 enum {
   MXG_FMT_E4M3 = 0, /* float8_e4m3fn: bias 7, no inf, NaN = 0x7F/0xFF, max 448 */
-  MXG_FMT_E5M2 = 1  /* float8_e5m2:   bias 15, inf = 0x7C/0xFC, max 57344      */
+  MXG_FMT_E5M2 = 1, /* float8_e5m2:   bias 15, inf = 0x7C/0xFC, max 57344      */
+  MXG_FMT_E2M1 = 2  /* float4_e2m1fn_x2: packed FP4, two elements per byte,
+                       element 2k in the low nibble; bias 1, no inf/NaN, max 6.
+                       A is then (L, M, K/2) bytes and B (L, N, K/2).  Both
+                       operands must be E2M1, sf_vec_size 32, K % 32 == 0,
+                       and the default (bf16) datapath; the pages list the
+                       packed container ("Parameters", A dtype) but not
+                       which nibble comes first: low first is the reading. */
 };
 
 /* status codes */
@@ -72,7 +79,7 @@ enum {
   MXG_ERR_SHAPE = -2,  /* a negative size, or a size whose offsets overflow   */
   MXG_ERR_ALIGN = -3,  /* A/B/C/Amax not 16-byte aligned, K % 16, N % 4       */
   MXG_ERR_SFVEC = -4,  /* sf_vec_size not 16 or 32                            */
-  MXG_ERR_FMT = -5,    /* element format not MXG_FMT_E4M3 / MXG_FMT_E5M2      */
+  MXG_ERR_FMT = -5,    /* element format unknown, or E2M1 on one operand only */
   MXG_ERR_DEVICE = -6, /* current device is not gfx950, or a pointer is not
                           device memory of the current device                 */
   MXG_ERR_LAUNCH = -7, /* HIP reported an error when launching                */
@@ -121,7 +128,7 @@ enum {
  *              M*N*L == 0; NaN if any C is NaN).
  *   M, N, K, L sizes, each >= 0.  K == 0 gives C == 0.
  *   sf_vec_size 16 or 32.
- *   a_fmt, b_fmt MXG_FMT_E4M3 or MXG_FMT_E5M2.
+ *   a_fmt, b_fmt MXG_FMT_E4M3, MXG_FMT_E5M2, or MXG_FMT_E2M1 for both.
  *   stream     hipStream_t (NULL = null stream).
  *
  * Requirements: A, B, C, Amax, SFA, SFB 16-byte aligned; K % 16 == 0 (16-byte
