@@ -22,6 +22,7 @@ import csv
 import glob
 import hashlib
 import json
+import math
 import os
 import re
 import sys
@@ -371,6 +372,8 @@ def main():
                     help="gemm: the GEMM + amax step (default); quantize: the MX quantisation of the "
                          "workload's float32 operands")
     ap.add_argument("--fp8-mfma", action="store_true", help="time the reduced-precision FP8 MFMA path")
+    ap.add_argument("--fp4", action="store_true",
+                    help="the workload's shape with packed FP4 (E2M1) operands and sf = 32 (same value recipe)")
     ap.add_argument("--sf-rowwise", action="store_true",
                     help="scales arrive row-wise (rows, ceil(K/sf)) bytes, as on the projection page's MXFP8 "
                          "input path; a step repacks both into the atom layout, then runs the GEMM")
@@ -405,7 +408,12 @@ def main():
     import block_scaled_precision_e4m3_amd as lib
     import workloads as W
 
-    p = W.make_workload(args.workload)
+    if args.fp4:
+        cfg = W.WORKLOADS[args.workload]
+        p = W.make_problem(cfg["M"], cfg["N"], cfg["K"], cfg["L"], 32, W.FMT_E2M1, W.FMT_E2M1, seed=args.workload,
+                           b_scale=float(1.0 / math.sqrt(cfg["K"])) if cfg["name"] == "projection" else 1.0)
+    else:
+        p = W.make_workload(args.workload)
     M, N, K, L, sf = p["M"], p["N"], p["K"], p["L"], p["sf"]
     dev = torch.device("cuda:0")
     A = torch.from_numpy(p["A"]).to(dev)
@@ -482,12 +490,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8-e4m3 codes, exact bf16 dequant, fp32 accumulate" if not args.fp8_mfma
-                 else "fp8-e4m3 scaled MFMA (reduced-precision sums), fp32 accumulate",
+        "dtype": ("fp4-e2m1 codes, exact bf16 dequant, fp32 accumulate" if args.fp4 else
+                  "fp8-e4m3 codes, exact bf16 dequant, fp32 accumulate" if not args.fp8_mfma
+                  else "fp8-e4m3 scaled MFMA (reduced-precision sums), fp32 accumulate"),
         "data": "synthetic (seeded, MX-quantised)",
         "config": {"workload": W.WORKLOADS[args.workload]["name"], "M": M, "N": N, "K": K, "L": L,
-                   "sf_vec_size": sf, "a_fmt": "e4m3" if p["a_fmt"] == 0 else "e5m2",
-                   "b_fmt": "e4m3" if p["b_fmt"] == 0 else "e5m2", "tile": f"{tile_m}x{tile_n}", "grid": grid,
+                   "sf_vec_size": sf, "a_fmt": ["e4m3", "e5m2", "e2m1"][p["a_fmt"]],
+                   "b_fmt": ["e4m3", "e5m2", "e2m1"][p["b_fmt"]], "tile": f"{tile_m}x{tile_n}", "grid": grid,
                    "path": "fp8-mfma" if args.fp8_mfma else "bf16-mfma", "c_dtype": args.c_dtype,
                    "sf_layout": "row-wise, repacked each step" if args.sf_rowwise else "atoms"},
         "pct_of_mxfp8_peak": round(100.0 * achieved / PEAK_FP8, 2),
