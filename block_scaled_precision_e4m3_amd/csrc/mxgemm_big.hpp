@@ -380,9 +380,12 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   // step's scale dwords and first chunk are read, and its first MFMA slice
   // converted, while the current step's last slice runs, so a step issues
   // MFMAs from its first cycle.  A wave reads a stage for the last time in the
-  // first slice of chunk 3 and has used that data by the end of slice S-2.
-  // One barrier per step, B' (after slice S-2, right after the slice's MFMAs
-  // are queued, so its wait overlaps them).  Past B':
+  // first slice of chunk 3, and that read has completed by the end of slice
+  // S-3 (chunk 3's first conversion happens there); by then the scales of
+  // chunk 3 are taken from the scale dwords as well.  One barrier per step,
+  // B' (after slice S-3, right after the slice's MFMAs are queued, so its
+  // wait overlaps them; the reads it releases then have two slices before
+  // their first use).  Past B':
   //   * every wave's DMA of step s+1 has landed (each wave first waits for
   //     its own), so stage (s+1) & 1 may be read;
   //   * every wave is done with stage s & 1, so DMA into it may start: the
@@ -508,7 +511,7 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
         if (k < kTM + kTN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (n == kSlices - 2) {
+      if (n == kSlices - 3) {
         // this wave's DMA of step s+1 (issued at the previous B') has landed
         wait_vm<0>();
         barrier();  // B'
