@@ -15,10 +15,10 @@
 //   one wave per SIMD keeps the matrix core fed.
 // * C stores.  A tile's C is stored at its end, transposed through LDS so
 //   that every store writes whole 128-byte lines.  Every CU ends its tiles at
-//   about the same time, so the stores drain slowly; the stage DMA is issued
-//   two steps ahead, before those stores, so that the next steps wait for
-//   their DMA only and the stores drain under their MFMAs (the vector-memory
-//   counter retires in issue order).
+//   about the same time, so the stores drain slowly; the DMA of the next
+//   tile's second step is issued before those stores, so that the next
+//   tile's first step waits for its DMA only and the stores drain under its
+//   MFMAs (the vector-memory counter retires in issue order).
 //
 // bf16 datapath, per 32-K chunk c of a step: lane (r, h) reads the 16 bytes
 // K [32c + 16h, +16) of its row for each of its A and B fragments; bytes
@@ -38,10 +38,6 @@ constexpr int kThreads = 256;
 constexpr int kBM = 256, kBN = 256, kBK = 128;
 constexpr int kTM = 4, kTN = 4;  // 32x32 MFMA blocks per wave (128 x 128)
 constexpr int kWN = kBN / 2;     // wave tile columns
-// bf16 datapath: a step's DMA of the next stage goes out over its slices
-// 1 .. kDmaSlices (spread so that the texture unit's queue does not back up
-// into instruction issue; done early enough to land before the barrier)
-constexpr int kDmaSlices = 3;
 
 template <int SF, bool FP4>
 struct Layout {
@@ -54,14 +50,17 @@ struct Layout {
   static constexpr int kStage = kOffSFB + kSF;
   static constexpr int kDma = (kBM + kBN) / 32;      // A/B DMA instructions per wave per step
   // Per-wave LDS area where the epilogue transposes one 32x32 fp32 block
-  // (rows padded to 36 floats) so its stores write whole 128-byte lines.  Its
-  // first kilobyte is where the scale DMA of a wave that loads no atoms
-  // (sf = 32: waves 2 and 3) writes its zeros: every wave issues the same
-  // instructions, so a step stays one branch-free block the scheduler can
-  // interleave.
+  // (rows padded to 36 floats) so its stores write whole 128-byte lines.
   static constexpr int kEpiRow = 36;
   static constexpr int kEpiWave = 32 * kEpiRow * 4;
   static constexpr int kEpiBytes = 4 * kEpiWave;
+  // Two kilobytes where the scale DMA of a wave that loads no atoms (sf = 32:
+  // waves 2 and 3) writes its zeros: every wave issues the same instructions,
+  // so a step stays one branch-free block the scheduler can interleave.  It
+  // is apart from the epilogue area because that DMA may still be in flight
+  // while the epilogue runs.
+  static constexpr int kOffDummy = 2 * kStage + kEpiBytes;
+  static constexpr int kLds = kOffDummy + 2048;
 };
 
 __device__ __forceinline__ uint4 lds16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
@@ -84,7 +83,8 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   static_assert(Y::NSF == 1 || Y::NSF == 2, "one or two scale atoms per 128-row group per step");
   constexpr int kEs = kCBytes<CT>;  // bytes per C element
   constexpr int NSF = Y::NSF;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * Y::kStage + Y::kEpiBytes];
+  static_assert(Y::kLds <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[Y::kLds];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -143,8 +143,8 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   // both 128-row groups (lanes 0-31 group 0, 32-63 group 1); sf=16 -> waves
   // 0,1 (A,B) load row group 0's two atoms, waves 2,3 row group 1's.  Groups
   // past the matrix read as zero.  With sf=32, waves 2 and 3 issue the same
-  // instruction on an empty resource into the wave's own kilobyte of the
-  // epilogue area (no branch in the step).
+  // instruction on an empty resource into their own kilobyte of the dummy
+  // area (no branch in the step).
   constexpr unsigned kOob = 0x80000000u;
   const bool sf_wave = NSF == 2 || wave < 2;
   const bool sf_is_b = (wave & 1) != 0;
@@ -179,9 +179,8 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
     const unsigned dst = d.dst + (q >= 8 ? (unsigned)Y::kOffB : 0u) + (unsigned)(wave + 4 * qq) * 1024u;
     dma16_at(q >= 8 ? d.rb : d.ra, voff, dst);
   };
-  // each wave's own kilobyte, which only that wave's epilogue reuses (after
-  // the wave's DMA has been waited for)
-  const unsigned sf_dummy = lds0 + 2u * (unsigned)Y::kStage + (unsigned)wave * (unsigned)Y::kEpiWave;
+  // waves 2 and 3 (the only ones that use it) each own a kilobyte
+  const unsigned sf_dummy = lds0 + (unsigned)Y::kOffDummy + (unsigned)(wave & 1) * 1024u;
   auto dma_sf = [&](const Dma& d) {
     const unsigned dst = d.dst + (sf_is_b ? (unsigned)Y::kOffSFB : (unsigned)Y::kOffSFA) +
                          (NSF == 1 ? 0u : (unsigned)(wave >> 1) * 1024u);
@@ -388,8 +387,15 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   // their first use).  Past B':
   //   * every wave's DMA of step s+1 has landed (each wave first waits for
   //     its own), so stage (s+1) & 1 may be read;
-  //   * every wave is done with stage s & 1, so DMA into it may start: the
-  //     next step queues the DMA of step s+2 over its slices 1 .. kDmaSlices.
+  //   * every wave is done with stage s & 1, so DMA into it may start.
+  // A step queues the DMA of step s+1 over its slices 1..3 (into the stage
+  // freed at the previous B'; spread so that the texture unit's queue does
+  // not back up into instruction issue).  A tile's last step also queues the
+  // DMA of the next tile's step 1 right after its B' (over slices S-2 and
+  // S-1), ahead of the tile's C stores; that tile's first step then queues no
+  // DMA, and its B' waits for all but 63 vector-memory operations (the 64
+  // stores of each lane retire after that DMA, in issue order), so the stores
+  // keep draining under its MFMAs; only the step after it waits for them.
   unsigned sa[NSF][kTM], sb[NSF][kTN];  // scale dwords of the current step
   uint4 ra[2][kTM], rb[2][kTN];         // raw 16-byte fragments, by chunk parity
   v8bf ab[2][kTM], bb[2][kTN];          // converted operands, by slice parity
@@ -449,9 +455,20 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
         bb[n & 1][i] = cvt8<FB>(t ? rb[c & 1][i].z : rb[c & 1][i].x, t ? rb[c & 1][i].w : rb[c & 1][i].y, fb[i]);
     }
   };
-  // step 0's inputs (after its DMA, issued above, has landed everywhere)
-  auto prime = [&]() __attribute__((always_inline)) {
+  // DMA target: a tile, its K step, and whether it exists
+  struct Tgt {
+    Tile t;
+    int kt;
+    bool live;
+  };
+  // steps 0 and 1 go into the two stages at once; step 0's inputs are read
+  // after both have landed everywhere
+  auto prime = [&](const Tgt& n1) __attribute__((always_inline)) {
     const Geo g = geo(lane_opaque());
+    const Dma d1 = dma_setup(g, n1.t, n1.kt, n1.live, lds0 + (unsigned)Y::kStage);
+    dma_sf(d1);
+#pragma unroll
+    for (int q = 0; q < Y::kDma; ++q) dma_ab(d1, q);
     wait_vm<0>();
     barrier();
     load_sf(g, lds, 0);
@@ -460,33 +477,45 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
     convert(0);
   };
   // One K step of tile `cur`.  FIRST: the tile's first step (its first MFMA
-  // per accumulator takes a zero C operand).  (nt, nkt, has_next): step s+1,
-  // whose DMA this step queues (nkt is also the K step of the scale tail
-  // read at B').
-  auto step_bf16 = [&](auto first, const Tile& nt, int nkt, bool has_next) __attribute__((always_inline)) {
+  // per accumulator takes a zero C operand, and its B' waits past the
+  // previous tile's C stores).  nkt: the K step of step s+1 (for the scale
+  // tail read at B').  EARLY (n2): the DMA of step s+2 goes out after B'.
+  // LATE (n1): the DMA of step s+1 goes out over slices 1..3.
+  auto step_bf16 = [&](auto first, auto late, auto early, int nkt, const Tgt& n1, const Tgt& n2)
+                       __attribute__((always_inline)) {
     constexpr bool kFirst = decltype(first)::value;
+    constexpr bool kLate = decltype(late)::value;
+    constexpr bool kEarly = decltype(early)::value;
     const Geo g = geo(lane_opaque());
     const uint8_t* stn = lds + ((s & 1) ^ 1) * Y::kStage;
     const uint8_t* st = lds + (s & 1) * Y::kStage;
     // slices of 16 K per step: 8 (8-bit) or 16 (FP4); kSpc per 32-byte chunk
     constexpr int kSlices = kFp4 ? 16 : 8;
     constexpr int kSpc = kSlices / 4;
-    Dma d;
+    constexpr int kPer2 = Y::kDma / 2;        // early DMA: per slice of S-2, S-1
+    constexpr int kPer1 = (Y::kDma + 2) / 3;  // late DMA: per slice of 1..3
+    Dma d1, d2;
 #pragma unroll
     for (int n = 0; n < kSlices; ++n) {
       // chunk c+1 is read during chunk c's first slice, a slice before its
       // first conversion; chunk 0 of the next step after B'
       if (n % kSpc == 0 && n / kSpc < 3) load_raw(g, st, n / kSpc + 1);
-      // the DMA of step s+1, spread over slices 1 .. kDmaSlices
-      if (n == 1) {
-        d = dma_setup(g, nt, nkt, has_next, lds0 + (unsigned)(((s & 1) ^ 1) * Y::kStage));
-        dma_sf(d);
-      }
-      if (n >= 1 && n <= kDmaSlices) {
-        constexpr int kPer = (Y::kDma + kDmaSlices - 1) / kDmaSlices;
+      if constexpr (kLate) {
+        if (n == 1) {
+          d1 = dma_setup(g, n1.t, n1.kt, n1.live, lds0 + (unsigned)(((s & 1) ^ 1) * Y::kStage));
+          dma_sf(d1);
+        }
+        if (n >= 1 && n <= 3) {
 #pragma unroll
-        for (int q = 0; q < kPer; ++q)
-          if ((n - 1) * kPer + q < Y::kDma) dma_ab(d, (n - 1) * kPer + q);
+          for (int q = 0; q < kPer1; ++q)
+            if ((n - 1) * kPer1 + q < Y::kDma) dma_ab(d1, (n - 1) * kPer1 + q);
+        }
+      }
+      if constexpr (kEarly) {
+        if (n >= kSlices - 2) {
+#pragma unroll
+          for (int q = 0; q < kPer2; ++q) dma_ab(d2, (n - (kSlices - 2)) * kPer2 + q);
+        }
       }
       if (n < kSlices - 1) {
         if ((n + 1) % kSpc == 0) scales(g, (n + 1) / kSpc);
@@ -512,11 +541,18 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
       }
       __builtin_amdgcn_sched_barrier(0);
       if (n == kSlices - 3) {
-        // this wave's DMA of step s+1 (issued at the previous B') has landed
-        wait_vm<0>();
+        // this wave's DMA of step s+1 has landed; on a tile's first step the
+        // previous tile's 64 C stores per lane, queued after that DMA, may
+        // still be in flight
+        if constexpr (kFirst) wait_vm<63>();
+        else wait_vm<0>();
         barrier();  // B'
         load_sf(g, stn, nkt);
         load_raw(g, stn, 0);
+        if constexpr (kEarly) {
+          d2 = dma_setup(g, n2.t, n2.kt, n2.live, lds0 + (unsigned)((s & 1) * Y::kStage));
+          dma_sf(d2);
+        }
       }
     }
     ++s;
@@ -525,18 +561,27 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   const std::true_type yes;
   const std::false_type no;
   if constexpr (MODE == kModeBf16) {
-    if (my_tiles > 0) prime();
+    if (my_tiles > 0) {
+      if (p.ksteps > 1) prime(Tgt{cur, 1, true});
+      else prime(Tgt{my_tiles > 1 ? make_tile<kBM, kBN>(p, t0 + G) : cur, 0, my_tiles > 1});
+    }
   }
   for (int i = 0; i < my_tiles; ++i) {
     const bool more = i + 1 < my_tiles;
     const Tile nxt = more ? make_tile<kBM, kBN>(p, t0 + (i + 1) * G) : cur;
     if constexpr (MODE == kModeBf16) {
+      const Tgt none = {cur, 0, false};
       if (p.ksteps == 1) {
-        step_bf16(yes, nxt, 0, more);
+        const bool more2 = i + 2 < my_tiles;
+        const Tgt n2 = {more2 ? make_tile<kBM, kBN>(p, t0 + (i + 2) * G) : cur, 0, more2};
+        step_bf16(yes, no, yes, 0, none, n2);
       } else {
-        step_bf16(yes, cur, 1, true);
-        for (int kt = 1; kt + 1 < p.ksteps; ++kt) step_bf16(no, cur, kt + 1, true);
-        step_bf16(no, nxt, 0, more);
+        // the tile's first step issues no DMA (its step 1 went out after
+        // the previous tile's last B'); middle steps the DMA of step s+1;
+        // the last step also that of the next tile's step 1, after B'
+        step_bf16(yes, no, no, 1, none, none);
+        for (int kt = 1; kt + 1 < p.ksteps; ++kt) step_bf16(no, yes, no, kt + 1, Tgt{cur, kt + 1, true}, none);
+        step_bf16(no, yes, yes, 0, Tgt{nxt, 0, more}, Tgt{nxt, 1, more});
       }
     } else {
       if (p.ksteps == 1) {

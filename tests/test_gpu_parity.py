@@ -279,3 +279,31 @@ def test_special_scale_bytes(lib, sf, tile):
     assert np.isnan(amax)
     keep = ~np.isnan(c_ref)
     check_c(c[keep], c_ref[keep], s_ref[keep], "special scale bytes")
+
+
+@pytest.mark.parametrize("M,N,K,sf", [(2048, 2048, 2048, 32),    # 128x128 tiles, one workgroup per CU
+                                      (256, 24576, 1536, 32),    # 128x128 tiles, two per CU
+                                      (1000, 772, 1040, 16),     # a few 128x128 tiles
+                                      (4000, 4100, 208, 16),     # 256x256 tiles, two K steps
+                                      (4096, 4096, 4096, 32)])   # 256x256 tiles, several per workgroup
+def test_back_to_back_calls_bitwise_equal(lib, M, N, K, sf):
+    # Calls queued back to back on one stream, with a different problem in
+    # between, must give bitwise the same C and Amax: a race inside a call
+    # (LDS read before its DMA landed) or anything a call leaves in flight
+    # shows up as a difference between repeats.
+    print(f"back-to-back {M}x{N}x{K} sf={sf} config={lib.mxgemm_launch_config(M, N, K, 1, sf)}", flush=True)
+    p = W.make_problem(M, N, K, 1, sf, E4, E4, seed=19)
+    q = W.make_problem(384, 640, 512, 1, 32, E5, E4, seed=20)
+    d, e = to_device(p), to_device(q)
+    outs = []
+    for _ in range(3):
+        run(lib, p, d)
+        run(lib, q, e)
+        c, amax = fetch(p, d)
+        outs.append((c.copy(), amax))
+    for c, amax in outs[1:]:
+        assert np.array_equal(c.view(np.uint32), outs[0][0].view(np.uint32))
+        assert float_bits(amax) == float_bits(outs[0][1])
+    rows = np.array([0, 1, M // 2, M - 1])
+    c_ref, s_ref = oracle.gemm_rows(p["A"], p["B"], p["SFA"], p["SFB"], M, N, K, 1, sf, E4, E4, 0, rows)
+    check_c(outs[0][0][0, rows], c_ref, s_ref, "back-to-back rows")
