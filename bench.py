@@ -379,6 +379,8 @@ def main():
                          "input path; a step repacks both into the atom layout, then runs the GEMM")
     ap.add_argument("--c-dtype", choices=["f32", "bf16", "f16"], default="f32",
                     help="C element type (f32, the default, is the operation's own output)")
+    ap.add_argument("--c-major", choices=["n", "m"], default="n",
+                    help="C layout: n-major (L, M, N), the default, or m-major (L, N, M) (float32 C)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-host-overhead", action="store_true",
                     help="skip the 1000 small calls that time the host side (keeps profiles to the workload)")
@@ -425,7 +427,8 @@ def main():
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
     mode_flag = (lib.MXG_FLAG_FP8_MFMA if args.fp8_mfma else 0) | \
-        {"f32": 0, "bf16": lib.MXG_FLAG_C_BF16, "f16": lib.MXG_FLAG_C_F16}[args.c_dtype]
+        {"f32": 0, "bf16": lib.MXG_FLAG_C_BF16, "f16": lib.MXG_FLAG_C_F16}[args.c_dtype] | \
+        (lib.MXG_FLAG_C_MMAJOR if args.c_major == "m" else 0)
 
     if args.sf_rowwise:
         import numpy as np
@@ -498,6 +501,7 @@ def main():
                    "sf_vec_size": sf, "a_fmt": ["e4m3", "e5m2", "e2m1"][p["a_fmt"]],
                    "b_fmt": ["e4m3", "e5m2", "e2m1"][p["b_fmt"]], "tile": f"{tile_m}x{tile_n}", "grid": grid,
                    "path": "fp8-mfma" if args.fp8_mfma else "bf16-mfma", "c_dtype": args.c_dtype,
+                   "c_major": args.c_major,
                    "sf_layout": "row-wise, repacked each step" if args.sf_rowwise else "atoms"},
         "pct_of_mxfp8_peak": round(100.0 * achieved / PEAK_FP8, 2),
         "kernel_ms": round(kernel_ms, 4),

@@ -33,6 +33,7 @@ MXG_FLAG_TILE_128 = 4
 MXG_FLAG_TILE_256 = 8
 MXG_FLAG_C_BF16 = 32
 MXG_FLAG_C_F16 = 64
+MXG_FLAG_C_MMAJOR = 128
 
 MXG_OK = 0
 MXG_ERR_NULL = -1
@@ -210,11 +211,13 @@ def _sf_phys(t, mn, k, l, sf):
 
 
 def gemm_amax(a, b, sfa, sfb, c=None, amax=None, sf_vec_size=32, stream=None, accumulate=False, fp8_mfma=False,
-              c_dtype=None):
+              c_dtype=None, c_major="n"):
     """(c, amax) = block-scaled GEMM + amax of torch FP8 tensors; see the module docstring.
 
     C is float32 by default; c_dtype (or a preallocated c) of torch.bfloat16 / torch.float16
-    stores the accumulators rounded to nearest even (amax still from the float32 values)."""
+    stores the accumulators rounded to nearest even (amax still from the float32 values).
+    c_major: "n" (C strides (N, 1, M*N), the default) or "m" (strides (1, M, M*N), float32),
+    as the pages' wrapper argument of that name."""
     import torch
     a_base, m, k, l = _as_lrk(a, "A")
     b_base, n, kb, lb = _as_lrk(b, "B")
@@ -223,13 +226,23 @@ def gemm_amax(a, b, sfa, sfb, c=None, amax=None, sf_vec_size=32, stream=None, ac
     fa, fb = _fmt_of(a), _fmt_of(b)
     sfa_p = _sf_phys(sfa, m, k, l, sf_vec_size)
     sfb_p = _sf_phys(sfb, n, k, l, sf_vec_size)
-    if c is None:
-        c = torch.empty((l, m, n), dtype=c_dtype or torch.float32, device=a.device).permute(1, 2, 0)
-    c_base = c.permute(2, 0, 1) if c.dim() == 3 else c.unsqueeze(0)
-    c_flag = {torch.float32: 0, torch.bfloat16: MXG_FLAG_C_BF16, torch.float16: MXG_FLAG_C_F16}.get(c.dtype)
-    if c_flag is None or not c_base.is_contiguous():
-        raise MxgemmValueError(MXG_ERR_ALIGN, "C must be float32, bfloat16 or float16, n-major (M, N, L) with "
-                                              "strides (N, 1, M*N)")
+    if c_major not in ("n", "m"):
+        raise MxgemmValueError(MXG_ERR_FLAGS, f"c_major must be 'n' or 'm', got {c_major!r}")
+    if c_major == "m":
+        if c is None:
+            c = torch.empty((l, n, m), dtype=c_dtype or torch.float32, device=a.device).permute(2, 1, 0)
+        c_base = c.permute(2, 1, 0) if c.dim() == 3 else c.t().unsqueeze(0)
+        c_flag = MXG_FLAG_C_MMAJOR if c.dtype == torch.float32 else None
+        if c_flag is None or not c_base.is_contiguous():
+            raise MxgemmValueError(MXG_ERR_ALIGN, "m-major C must be float32 (M, N, L) with strides (1, M, M*N)")
+    else:
+        if c is None:
+            c = torch.empty((l, m, n), dtype=c_dtype or torch.float32, device=a.device).permute(1, 2, 0)
+        c_base = c.permute(2, 0, 1) if c.dim() == 3 else c.unsqueeze(0)
+        c_flag = {torch.float32: 0, torch.bfloat16: MXG_FLAG_C_BF16, torch.float16: MXG_FLAG_C_F16}.get(c.dtype)
+        if c_flag is None or not c_base.is_contiguous():
+            raise MxgemmValueError(MXG_ERR_ALIGN, "C must be float32, bfloat16 or float16, n-major (M, N, L) with "
+                                                  "strides (N, 1, M*N)")
     if amax is None:
         amax = torch.zeros((1, 1, 1), dtype=torch.float32, device=a.device)
     flags = (MXG_FLAG_AMAX_ACCUMULATE if accumulate else 0) | (MXG_FLAG_FP8_MFMA if fp8_mfma else 0) | c_flag
@@ -325,6 +338,6 @@ __all__ = [
     "mxgemm_launch_config", "mxgemm_strerror", "gemm_amax", "LIB_PATH", "EXPORTED",
     "mxgemm_mx_quantize", "mx_quantize", "mxgemm_sf_rowwise_to_atoms", "sf_from_rowwise", "Plan",
     "MXG_FMT_E4M3", "MXG_FMT_E5M2", "MXG_FMT_E2M1", "MXG_FLAG_AMAX_ACCUMULATE", "MXG_FLAG_FP8_MFMA", "MXG_FLAG_TILE_128",
-    "MXG_FLAG_TILE_256", "MXG_FLAG_C_BF16", "MXG_FLAG_C_F16", "MxgemmError", "MxgemmValueError",
+    "MXG_FLAG_TILE_256", "MXG_FLAG_C_BF16", "MXG_FLAG_C_F16", "MXG_FLAG_C_MMAJOR", "MxgemmError", "MxgemmValueError",
     "MxgemmRuntimeError",
 ]

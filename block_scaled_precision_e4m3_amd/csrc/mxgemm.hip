@@ -203,6 +203,7 @@ void configure(Prepared* pr, int cus) {
   if (pr->flags & MXG_FLAG_TILE_128) cfg = kSmall;
   if ((pr->flags & MXG_FLAG_TILE_256) && K > 0) cfg = kBig;
   if (fp4 && K > 0) cfg = kBig;  // packed FP4 runs on the 256x256 kernel only
+  if (pr->ct == 3 && K > 0) cfg = kBig;  // so does an m-major C
   pr->kind = cfg.kind;
   p.tilesM = (int)cdiv(M, cfg.tile_m);
   p.tilesN = (int)cdiv(N, cfg.tile_n);
@@ -219,13 +220,18 @@ int prepare(Prepared* pr, int64_t M, int64_t N, int64_t K, int64_t L, int sf_vec
   const unsigned tile_flags = flags & (MXG_FLAG_TILE_128 | MXG_FLAG_TILE_256);
   const unsigned c_flags = flags & (MXG_FLAG_C_BF16 | MXG_FLAG_C_F16);
   if (flags & ~(unsigned)(MXG_FLAG_AMAX_ACCUMULATE | MXG_FLAG_FP8_MFMA | MXG_FLAG_TILE_128 | MXG_FLAG_TILE_256 |
-                          MXG_FLAG_C_BF16 | MXG_FLAG_C_F16))
+                          MXG_FLAG_C_BF16 | MXG_FLAG_C_F16 | MXG_FLAG_C_MMAJOR))
     return MXG_ERR_FLAGS;
+  const bool c_mmajor = (flags & MXG_FLAG_C_MMAJOR) != 0;
+  // m-major C: the 256x256 kernel's bf16 datapath with a float32 C
+  if (c_mmajor && (flags & (MXG_FLAG_FP8_MFMA | MXG_FLAG_C_BF16 | MXG_FLAG_C_F16))) return MXG_ERR_FLAGS;
+  if (c_mmajor && K > 0 && (flags & MXG_FLAG_TILE_128)) return MXG_ERR_FLAGS;
   if (tile_flags & (tile_flags - 1)) return MXG_ERR_FLAGS;  // more than one tile flag
   if (c_flags & (c_flags - 1)) return MXG_ERR_FLAGS;        // both 16-bit C types
   if (c_flags && (flags & MXG_FLAG_FP8_MFMA)) return MXG_ERR_FLAGS;  // 16-bit C: bf16 datapath only
   if (a_fmt == MXG_FMT_E2M1 && (flags & MXG_FLAG_FP8_MFMA)) return MXG_ERR_FLAGS;  // FP4: bf16 datapath
   if (a_fmt == MXG_FMT_E2M1 && K > 0 && (flags & MXG_FLAG_TILE_128)) return MXG_ERR_FLAGS;  // FP4: 256x256
+  if (c_mmajor && M % 4 != 0) return MXG_ERR_ALIGN;  // 16-byte runs along M
   memset(pr, 0, sizeof(*pr));
   pr->magic = kPlanMagic;
   pr->flags = flags;
@@ -234,7 +240,7 @@ int prepare(Prepared* pr, int64_t M, int64_t N, int64_t K, int64_t L, int sf_vec
   pr->fb = b_fmt;
   pr->fp8 = (flags & MXG_FLAG_FP8_MFMA) != 0;
   pr->accumulate = (flags & MXG_FLAG_AMAX_ACCUMULATE) != 0;
-  pr->ct = (flags & MXG_FLAG_C_BF16) ? 1 : (flags & MXG_FLAG_C_F16) ? 2 : 0;
+  pr->ct = (flags & MXG_FLAG_C_BF16) ? 1 : (flags & MXG_FLAG_C_F16) ? 2 : c_mmajor ? 3 : 0;
   // A, B and the scales are read only when there is a non-empty C and a non-empty K
   pr->need_c = M > 0 && N > 0 && L > 0;
   pr->need_a = pr->need_c && K > 0;
@@ -290,6 +296,7 @@ int launch_prepared(const Prepared& pr, const void* A, const void* B, const uint
   hipError_t e;
   if (pr.kind == 1) {
     if (pr.fp8) e = launch_mode<mxg::kModeFp8, 1, 0>(p, sf, fa, fb, grid, s);
+    else if (pr.ct == 3) e = launch_mode<mxg::kModeBf16, 1, 3>(p, sf, fa, fb, grid, s);
     else if (pr.ct == 1) e = launch_mode<mxg::kModeBf16, 1, 1>(p, sf, fa, fb, grid, s);
     else if (pr.ct == 2) e = launch_mode<mxg::kModeBf16, 1, 2>(p, sf, fa, fb, grid, s);
     else e = launch_mode<mxg::kModeBf16, 1, 0>(p, sf, fa, fb, grid, s);
@@ -297,6 +304,8 @@ int launch_prepared(const Prepared& pr, const void* A, const void* B, const uint
     if (pr.fp8) e = launch_mode<mxg::kModeFp8, 0, 0>(p, sf, fa, fb, grid, s);
     else if (pr.ct == 1) e = launch_mode<mxg::kModeBf16, 0, 1>(p, sf, fa, fb, grid, s);
     else if (pr.ct == 2) e = launch_mode<mxg::kModeBf16, 0, 2>(p, sf, fa, fb, grid, s);
+    // float32 C; an m-major C gets here only with K == 0, where C is all zeros
+    // and the layouts hold the same bytes
     else e = launch_mode<mxg::kModeBf16, 0, 0>(p, sf, fa, fb, grid, s);
   }
   return e == hipSuccess ? MXG_OK : MXG_ERR_LAUNCH;

@@ -79,6 +79,7 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   // FA = FB = 2: packed FP4 (E2M1), bf16 datapath, sf = 32 (the host enforces it)
   constexpr bool kFp4 = FA == 2;
   static_assert(!kFp4 || (FB == 2 && SF == 32 && MODE == kModeBf16), "FP4: both operands, sf = 32, bf16 path");
+  static_assert(!kCMajorM<CT> || MODE == kModeBf16, "m-major C: bf16 path");
   using Y = Layout<SF, kFp4>;
   static_assert(Y::NSF == 1 || Y::NSF == 2, "one or two scale atoms per 128-row group per step");
   constexpr int kEs = kCBytes<CT>;  // bytes per C element
@@ -192,23 +193,30 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   unsigned lmax = 0u;
 
   // --- C stores -----------------------------------------------------------------
-  // Lane (r, h) of block (i, j) holds C row 128*wm + 32i + r and, for q =
-  // 0..3, the 4 columns kWN*wn + 32j + 8q + 4h + (0..3).  Rows past the tile's
-  // valid rows land past the resource (num_records = valid rows * N * 4);
-  // columns past N get an offset past it as well.  Every store folds its
-  // values into the lane's amax.
+  // n-major C: lane (r, h) of block (i, j) holds C row m = 128*wm + 32i + r
+  // and, for q = 0..3, the 4 columns n = kWN*wn + 32j + 8q + 4h + (0..3).
+  // m-major C (CT = 3, the MFMA operands swapped): the lane holds row
+  // n = kWN*wn + 32j + r of the (L, N, M) layout and the 4 columns
+  // m = 128*wm + 32i + 8q + 4h + (0..3).  Either way a "row" runs along the
+  // layout's outer dimension and a "column" along its contiguous one.  Rows
+  // past the tile's valid rows land past the resource (num_records = valid
+  // rows * row length * element size); columns past the matrix get an offset
+  // past it as well.  Every store folds its values into the lane's amax.
+  constexpr bool kMM = kCMajorM<CT>;
   struct StoreCtx {
     __amdgpu_buffer_rsrc_t rc;
     unsigned c_bytes;
-    int mvalid, nvalid, n0;
+    int rvalid, cvalid, c0, stride;  // valid rows, valid columns, first column, row length
   };
   auto store_ctx = [&](const Tile& T) {
     StoreCtx x;
-    x.c_bytes = (unsigned)T.mvalid * (unsigned)p.N * (unsigned)kEs;
-    x.rc = make_rsrc(reinterpret_cast<uint8_t*>(p.C) + ((int64_t)T.l * p.M + T.m0) * p.N * kEs, x.c_bytes);
-    x.mvalid = T.mvalid;
-    x.nvalid = T.nvalid;
-    x.n0 = T.n0;
+    x.stride = kMM ? p.M : p.N;
+    x.rvalid = kMM ? T.nvalid : T.mvalid;
+    x.cvalid = kMM ? T.mvalid : T.nvalid;
+    x.c0 = kMM ? T.m0 : T.n0;
+    const int64_t row0 = kMM ? (int64_t)T.l * p.N + T.n0 : (int64_t)T.l * p.M + T.m0;
+    x.c_bytes = (unsigned)x.rvalid * (unsigned)x.stride * (unsigned)kEs;
+    x.rc = make_rsrc(reinterpret_cast<uint8_t*>(p.C) + row0 * x.stride * kEs, x.c_bytes);
     return x;
   };
   // Every block of `acc` at tile end.  A block goes through the
@@ -226,8 +234,10 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
     const int wr_off = ((ln & 31) * Y::kEpiRow + 4 * (ln >> 5)) * 4;        // + 32 q bytes
     const int rd_row = ln >> 3, rd_col = 4 * (ln & 7);
     const int rd_off = (rd_row * Y::kEpiRow + rd_col) * 4;                  // + 8 k rows
-    const int col_base = kWN * wn + rd_col;                                  // tile column of the lane's run
-    const unsigned vrow0 = ((unsigned)(128 * wm + rd_row) * (unsigned)p.N + (unsigned)(x.n0 + col_base)) * (unsigned)kEs;
+    const int row_base = kMM ? kWN * wn : 128 * wm;                          // the wave's first tile row
+    const int col_base = (kMM ? 128 * wm : kWN * wn) + rd_col;               // tile column of the lane's run
+    const unsigned vrow0 =
+        ((unsigned)(row_base + rd_row) * (unsigned)x.stride + (unsigned)(x.c0 + col_base)) * (unsigned)kEs;
     auto put = [&](int i, int j) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -244,13 +254,14 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
       for (int k = 0; k < 4; ++k) out[k] = *reinterpret_cast<const v4f*>(epi + rd_off + k * 8 * Y::kEpiRow * 4);
     };
     auto emit = [&](const v4f (&v)[4], int i, int j) {
-      const bool cok = col_base + 32 * j < x.nvalid;
+      const int rb = kMM ? j : i, cb = kMM ? i : j;  // the block's row and column block
+      const bool cok = col_base + 32 * cb < x.cvalid;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const int row = 128 * wm + 32 * i + 8 * k + rd_row;
-        const bool ok = cok & (row < x.mvalid);
+        const int row = row_base + 32 * rb + 8 * k + rd_row;
+        const bool ok = cok & (row < x.rvalid);
         const unsigned off =
-            vrow0 + (unsigned)(32 * i + 8 * k) * (unsigned)p.N * (unsigned)kEs + (unsigned)(32 * j * kEs);
+            vrow0 + (unsigned)(32 * rb + 8 * k) * (unsigned)x.stride * (unsigned)kEs + (unsigned)(32 * cb * kEs);
         store_c4<CT>(v[k], x.rc, ok ? (int)off : (int)x.c_bytes, 0);
         const unsigned m4 = max(max(__float_as_uint(v[k][0]) & 0x7FFFFFFFu, __float_as_uint(v[k][1]) & 0x7FFFFFFFu),
                                 max(__float_as_uint(v[k][2]) & 0x7FFFFFFFu, __float_as_uint(v[k][3]) & 0x7FFFFFFFu));
@@ -529,8 +540,10 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
       for (int i = 0; i < kTM; ++i)
 #pragma unroll
         for (int jj = 0; jj < kTN; ++jj)
-          acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bb[n & 1][jj], ab[n & 1][i],
-                                                               (kFirst && n == 0) ? zero16 : acc[i][jj], 0, 0, 0);
+          acc[i][jj] = kMM ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab[n & 1][i], bb[n & 1][jj],
+                                                                     (kFirst && n == 0) ? zero16 : acc[i][jj], 0, 0, 0)
+                           : __builtin_amdgcn_mfma_f32_32x32x16_bf16(bb[n & 1][jj], ab[n & 1][i],
+                                                                     (kFirst && n == 0) ? zero16 : acc[i][jj], 0, 0, 0);
       // interleave: each MFMA followed by up to 3 VALU ops; the chunk's
       // fragment reads go out one after each of the first MFMAs
 #pragma unroll

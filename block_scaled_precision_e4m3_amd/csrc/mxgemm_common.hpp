@@ -190,18 +190,21 @@ __device__ __forceinline__ v8bf cvt8(unsigned w0, unsigned w1, float scale) {
   return __builtin_bit_cast(v8bf, u);
 }
 
-// C element type, a kernel template parameter CT: 0 float32, 1 bfloat16,
-// 2 float16.  The accumulators are float32 either way; a 16-bit C receives
-// them rounded to nearest even (v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32), and
-// the amax is taken over the float32 values.
+// C element type and layout, a kernel template parameter CT: 0 float32,
+// 1 bfloat16, 2 float16, all n-major (L, M, N); 3 float32 m-major (L, N, M)
+// (256x256 kernel only).  The accumulators are float32 either way; a 16-bit C
+// receives them rounded to nearest even (v_cvt_pk_bf16_f32 /
+// v_cvt_pk_f16_f32), and the amax is taken over the float32 values.
 template <int CT>
-constexpr int kCBytes = CT == 0 ? 4 : 2;
+constexpr int kCBytes = (CT == 0 || CT == 3) ? 4 : 2;
+template <int CT>
+constexpr bool kCMajorM = CT == 3;
 
 // Four consecutive outputs of one C row, given in float32, stored as C's
 // element type at byte offset voff + soff of resource rc.
 template <int CT>
 __device__ __forceinline__ void store_c4(const v4f& v, __amdgpu_buffer_rsrc_t rc, int voff, int soff) {
-  if constexpr (CT == 0)
+  if constexpr (CT == 0 || CT == 3)
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), rc, voff, soff, 0);
   else if constexpr (CT == 1)
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, __builtin_convertvector(v, v4bf)), rc, voff, soff,

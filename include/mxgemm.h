@@ -114,7 +114,15 @@ enum {
      the signature and must still be 16-byte aligned.  Not with
      MXG_FLAG_FP8_MFMA; setting both C flags is an error. */
   MXG_FLAG_C_BF16 = 32u,
-  MXG_FLAG_C_F16 = 64u
+  MXG_FLAG_C_F16 = 64u,
+  /* m-major C ("GEMM + Amax (SM100)", section "Parameters": C of shape
+     (M, N, L) with strides (1, M, M*N), the wrapper's c_major="m"): C then
+     holds (L, N, M) float32 elements, M contiguous.  The contiguous dimension
+     must be 16-byte aligned, so M % 4 == 0 as well (MXG_ERR_ALIGN otherwise).
+     Runs on the 256x256 kernel (the default datapath, float32 C only):
+     not with MXG_FLAG_FP8_MFMA, MXG_FLAG_C_BF16 / _F16 or, when K > 0,
+     MXG_FLAG_TILE_128 (MXG_ERR_FLAGS). */
+  MXG_FLAG_C_MMAJOR = 128u
 };
 
 /*
@@ -148,8 +156,9 @@ int mxgemm_amax(const void* A, const void* B, const uint8_t* SFA, const uint8_t*
  * max-reduces into the existing Amax (queues the GEMM kernel only);
  * MXG_FLAG_FP8_MFMA selects the reduced-precision FP8 matrix path;
  * MXG_FLAG_TILE_128 / _256 force a tile configuration; MXG_FLAG_C_BF16 /
- * _F16 store a 16-bit C.  Returns MXG_ERR_FLAGS for unknown bits, more than
- * one tile flag, both C flags, or a C flag with MXG_FLAG_FP8_MFMA.
+ * _F16 store a 16-bit C; MXG_FLAG_C_MMAJOR stores C m-major.  Returns
+ * MXG_ERR_FLAGS for unknown bits, more than one tile flag, both C flags, a C
+ * flag with MXG_FLAG_FP8_MFMA, or MXG_FLAG_C_MMAJOR with a flag it excludes.
  *
  * Exactness of the default path: every dequantised element is exact when
  * its scale byte lies in 3..246 (E4M3) or 10..239 (E5M2), i.e. when the

@@ -90,7 +90,14 @@ def test_errors_before_device_work(lib):
     assert f(*(args[:5] + [None]), *dims, 32, 0, 0, 0, None) == lib.MXG_ERR_NULL
     assert f(*([good + 8] + args[1:]), *dims, 32, 0, 0, 0, None) == lib.MXG_ERR_ALIGN
     assert f(*(args[:4] + [good + 4] + args[5:]), *dims, 32, 0, 0, 0, None) == lib.MXG_ERR_ALIGN
-    assert f(*args, *dims, 32, 0, 0, 128, None) == lib.MXG_ERR_FLAGS    # unknown bit
+    assert f(*args, *dims, 32, 0, 0, 256, None) == lib.MXG_ERR_FLAGS    # unknown bit
+    # m-major C: the bf16 datapath, float32 C, 256x256 tiles, M % 4 == 0
+    mm = lib.MXG_FLAG_C_MMAJOR
+    assert f(*args, *dims, 32, 0, 0, mm | lib.MXG_FLAG_FP8_MFMA, None) == lib.MXG_ERR_FLAGS
+    assert f(*args, *dims, 32, 0, 0, mm | lib.MXG_FLAG_C_BF16, None) == lib.MXG_ERR_FLAGS
+    assert f(*args, *dims, 32, 0, 0, mm | lib.MXG_FLAG_C_F16, None) == lib.MXG_ERR_FLAGS
+    assert f(*args, *dims, 32, 0, 0, mm | lib.MXG_FLAG_TILE_128, None) == lib.MXG_ERR_FLAGS
+    assert f(*args, 250, 256, 256, 1, 32, 0, 0, mm, None) == lib.MXG_ERR_ALIGN
     assert f(*args, *dims, 32, 0, 0, 96, None) == lib.MXG_ERR_FLAGS     # both 16-bit C types
     assert f(*args, *dims, 32, 0, 0, 34, None) == lib.MXG_ERR_FLAGS     # 16-bit C with the FP8 datapath
     assert f(*args, *dims, 32, 0, 0, 16, None) == lib.MXG_ERR_FLAGS   # unknown bit
