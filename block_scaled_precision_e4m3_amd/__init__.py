@@ -47,7 +47,7 @@ MXG_ERR_FLAGS = -8
 
 EXPORTED = ("mxgemm_amax", "mxgemm_amax_ex", "mxgemm_amax_reset", "mxgemm_check_support",
             "mxgemm_sf_bytes", "mxgemm_launch_config", "mxgemm_strerror", "mxgemm_mx_quantize",
-            "mxgemm_sf_rowwise_to_atoms", "mxgemm_plan_init", "mxgemm_plan_execute")
+            "mxgemm_sf_rowwise_to_atoms", "mxgemm_plan_init", "mxgemm_plan_execute", "mxgemm_codes_to_kmajor")
 
 
 class MxgemmError(Exception):
@@ -95,6 +95,8 @@ def _load():
     lib.mxgemm_plan_init.restype = ci
     lib.mxgemm_plan_execute.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
     lib.mxgemm_plan_execute.restype = ci
+    lib.mxgemm_codes_to_kmajor.argtypes = [vp, vp, i64, i64, i64, vp]
+    lib.mxgemm_codes_to_kmajor.restype = ci
     return lib
 
 
@@ -181,17 +183,35 @@ def _fmt_of(t):
     raise MxgemmValueError(MXG_ERR_FMT, f"A/B dtype must be float8_e4m3fn or float8_e5m2, got {t.dtype}")
 
 
-def _as_lrk(t, name):
-    """Return (storage tensor contiguous as (L, rows, K), rows, K, L) from a k-major (rows, K, L) view or 2-D."""
+def _as_lrk(t, name, stream=None):
+    """Return (storage tensor contiguous as (L, rows, K), rows, K, L) from a (rows, K, L) view or 2-D.
+
+    k-major views (strides (K, 1, rows*K)) are used as they are; m-major ones (strides
+    (1, rows, rows*K), the pages' m-major A / n-major B) are rewritten k-major into a new
+    tensor by mxgemm_codes_to_kmajor on `stream`."""
+    import torch
     if t.dim() == 2:
         t = t.unsqueeze(2)
     if t.dim() != 3:
         raise MxgemmValueError(MXG_ERR_SHAPE, f"{name} must be (rows, K) or (rows, K, L)")
     rows, k, l = t.shape
     base = t.permute(2, 0, 1)
-    if not base.is_contiguous():
-        raise MxgemmValueError(MXG_ERR_ALIGN, f"{name} must be k-major with batch outermost: strides (K, 1, rows*K)")
-    return base, rows, k, l
+    if base.is_contiguous():
+        return base, rows, k, l
+    mmajor = t.permute(2, 1, 0)
+    if mmajor.is_contiguous() and t.dtype in (torch.float8_e4m3fn, torch.float8_e5m2):
+        dst = torch.empty((l, rows, k), dtype=t.dtype, device=t.device)
+        codes_to_kmajor(mmajor, dst, rows, k, l, stream)
+        return dst, rows, k, l
+    raise MxgemmValueError(MXG_ERR_ALIGN, f"{name} must be k-major (strides (K, 1, rows*K)) or, for FP8 codes, "
+                                          f"m-major (strides (1, rows, rows*K)), batch outermost")
+
+
+def codes_to_kmajor(src, dst, MN, K, L, stream=None):
+    """C-ABI mxgemm_codes_to_kmajor: (L, K, MN) codes into (L, MN, K); raises on a nonzero status."""
+    st = _lib.mxgemm_codes_to_kmajor(_ptr(src), _ptr(dst), MN, K, L, _stream(stream))
+    if st != MXG_OK:
+        _raise(st)
 
 
 def _sf_phys(t, mn, k, l, sf):
@@ -219,8 +239,8 @@ def gemm_amax(a, b, sfa, sfb, c=None, amax=None, sf_vec_size=32, stream=None, ac
     c_major: "n" (C strides (N, 1, M*N), the default) or "m" (strides (1, M, M*N), float32),
     as the pages' wrapper argument of that name."""
     import torch
-    a_base, m, k, l = _as_lrk(a, "A")
-    b_base, n, kb, lb = _as_lrk(b, "B")
+    a_base, m, k, l = _as_lrk(a, "A", stream)
+    b_base, n, kb, lb = _as_lrk(b, "B", stream)
     if kb != k or lb != l:
         raise MxgemmValueError(MXG_ERR_SHAPE, "A and B disagree on K or L")
     fa, fb = _fmt_of(a), _fmt_of(b)
@@ -338,6 +358,6 @@ __all__ = [
     "mxgemm_launch_config", "mxgemm_strerror", "gemm_amax", "LIB_PATH", "EXPORTED",
     "mxgemm_mx_quantize", "mx_quantize", "mxgemm_sf_rowwise_to_atoms", "sf_from_rowwise", "Plan",
     "MXG_FMT_E4M3", "MXG_FMT_E5M2", "MXG_FMT_E2M1", "MXG_FLAG_AMAX_ACCUMULATE", "MXG_FLAG_FP8_MFMA", "MXG_FLAG_TILE_128",
-    "MXG_FLAG_TILE_256", "MXG_FLAG_C_BF16", "MXG_FLAG_C_F16", "MXG_FLAG_C_MMAJOR", "MxgemmError", "MxgemmValueError",
+    "MXG_FLAG_TILE_256", "MXG_FLAG_C_BF16", "MXG_FLAG_C_F16", "MXG_FLAG_C_MMAJOR", "codes_to_kmajor", "MxgemmError", "MxgemmValueError",
     "MxgemmRuntimeError",
 ]

@@ -13,6 +13,7 @@
 #include "../../include/mxgemm.h"
 #include "mx_quantize.hpp"
 #include "sf_repack.hpp"
+#include "codes_transpose.hpp"
 #include "mxgemm_big.hpp"
 #include "mxgemm_kernel.hpp"
 
@@ -451,6 +452,32 @@ int mxgemm_sf_rowwise_to_atoms(const uint8_t* rowwise, uint8_t* SF, int64_t MN, 
   p.num_atoms = (int)(L * p.MNb * p.Kg);
   const int64_t grid = std::min<int64_t>(p.num_atoms, 16LL * cus);
   hipLaunchKernelGGL(mxg::repack::rowwise_to_atoms_kernel, dim3((unsigned)grid), dim3(mxg::repack::kThreads), 0,
+                     (hipStream_t)stream, p);
+  return hipGetLastError() == hipSuccess ? MXG_OK : MXG_ERR_LAUNCH;
+}
+
+int mxgemm_codes_to_kmajor(const void* src, void* dst, int64_t MN, int64_t K, int64_t L, void* stream) {
+  if (MN < 0 || K < 0 || L < 0) return MXG_ERR_SHAPE;
+  if (!fits_i32(MN) || !fits_i32(K) || !fits_i32(L)) return MXG_ERR_SHAPE;
+  if (L * cdiv(MN, 64) * cdiv(K, 64) > 0x7FFFFFFFLL) return MXG_ERR_SHAPE;
+  if (MN % 16 != 0 || K % 16 != 0) return MXG_ERR_ALIGN;
+  if (MN == 0 || K == 0 || L == 0) return MXG_OK;
+  if (!src || !dst) return MXG_ERR_NULL;
+  if (!aligned16(src) || !aligned16(dst)) return MXG_ERR_ALIGN;
+  int dev = 0, cus = 0;
+  int st = device_check(&dev, &cus);
+  if (st != MXG_OK) return st;
+  if (!on_device(src, dev) || !on_device(dst, dev)) return MXG_ERR_DEVICE;
+  mxg::transpose::TParams p;
+  p.S = static_cast<const uint8_t*>(src);
+  p.D = static_cast<uint8_t*>(dst);
+  p.MN = (int)MN;
+  p.K = (int)K;
+  p.tiles_mn = (int)cdiv(MN, mxg::transpose::kTile);
+  p.tiles_k = (int)cdiv(K, mxg::transpose::kTile);
+  p.num_tiles = (int)(L * p.tiles_mn * p.tiles_k);
+  const int64_t grid = std::min<int64_t>(p.num_tiles, 16LL * cus);
+  hipLaunchKernelGGL(mxg::transpose::codes_to_kmajor_kernel, dim3((unsigned)grid), dim3(mxg::transpose::kThreads), 0,
                      (hipStream_t)stream, p);
   return hipGetLastError() == hipSuccess ? MXG_OK : MXG_ERR_LAUNCH;
 }

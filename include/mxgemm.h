@@ -280,6 +280,25 @@ int mxgemm_sf_rowwise_to_atoms(const uint8_t* rowwise, uint8_t* SF, int64_t MN, 
                                int sf_vec_size, void* stream);
 
 /* mxgemm_strerror -- static text for a status code. No HIP call. */
+/*
+ * mxgemm_codes_to_kmajor -- m-major (or n-major) 8-bit element codes into the
+ * k-major rows mxgemm_amax reads ("GEMM + Amax (SM100)", section
+ * "Parameters": A of shape (M, K, L) may have strides (1, M, M*K), B of shape
+ * (N, K, L) strides (1, N, N*K); packed FP4 operands must be k-major).
+ *
+ *   src : (L, K, MN) bytes, MN contiguous -- byte (mn, k, l) at
+ *         mn + MN*k + MN*K*l; 16-byte aligned.
+ *   dst : (L, MN, K) bytes, K contiguous -- the A or B argument of
+ *         mxgemm_amax; 16-byte aligned, caller-owned, not overlapping src.
+ *   MN  : M for A, N for B.
+ *
+ * Asynchronous on `stream`; the library allocates nothing.  Errors (before
+ * any work): MXG_ERR_SHAPE, MXG_ERR_ALIGN (MN % 16 or K % 16 -- the 16-byte
+ * alignment of both contiguous dimensions -- or a pointer), MXG_ERR_NULL,
+ * MXG_ERR_DEVICE.  MN, K or L == 0 queues nothing and returns MXG_OK.
+ */
+int mxgemm_codes_to_kmajor(const void* src, void* dst, int64_t MN, int64_t K, int64_t L, void* stream);
+
 const char* mxgemm_strerror(int status);
 
 #ifdef __cplusplus

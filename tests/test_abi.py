@@ -106,6 +106,15 @@ def test_errors_before_device_work(lib):
     assert f(*args, 256, 256, 256, 1, 32, 0, 9, 0, None) == lib.MXG_ERR_FMT
     assert f(*args, 256, 256, 100, 1, 32, 0, 0, 0, None) == lib.MXG_ERR_ALIGN
     assert f(*args, 256, -5, 256, 1, 32, 0, 0, 0, None) == lib.MXG_ERR_SHAPE
+    t = c.mxgemm_codes_to_kmajor
+    t.argtypes = [vp, vp, i64, i64, i64, vp]
+    t.restype = ci
+    assert t(good, good, 72, 48, 1, None) == lib.MXG_ERR_ALIGN    # MN % 16
+    assert t(good, good, 80, 40, 1, None) == lib.MXG_ERR_ALIGN    # K % 16
+    assert t(good + 8, good, 80, 48, 1, None) == lib.MXG_ERR_ALIGN
+    assert t(None, good, 80, 48, 1, None) == lib.MXG_ERR_NULL
+    assert t(good, good, -16, 48, 1, None) == lib.MXG_ERR_SHAPE
+    assert t(None, None, 0, 48, 1, None) == lib.MXG_OK              # nothing to do
     r = c.mxgemm_amax_reset
     r.argtypes = [vp, vp]
     r.restype = ci

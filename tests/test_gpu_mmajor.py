@@ -111,3 +111,50 @@ def test_mmajor_projection_workload_rows(lib):
                                     rows)
     check_c(c[0, rows], c_ref, s_ref, "projection, m-major rows")
     assert amax == float(np.max(np.abs(c)))
+
+
+# --- m-major A / n-major B: codes rewritten k-major by mxgemm_codes_to_kmajor --------
+
+@pytest.mark.parametrize("MN,K,L", [(64, 64, 1), (80, 48, 3), (4096, 1536, 1), (1040, 208, 2), (16, 16, 1)])
+def test_codes_to_kmajor_bit_exact(lib, MN, K, L):
+    print(f"codes_to_kmajor {MN}x{K}x{L}", flush=True)
+    rng = np.random.default_rng(MN + K + L)
+    src = rng.integers(0, 256, size=(L, K, MN), dtype=np.uint8)
+    dev = torch.device("cuda:0")
+    s = torch.from_numpy(src).to(dev)
+    guard = 4096
+    d = torch.full((L * MN * K + guard,), 0xA5, dtype=torch.uint8, device=dev)
+    lib.codes_to_kmajor(s, d, MN, K, L)
+    torch.cuda.synchronize()
+    out = d.cpu().numpy()
+    assert np.all(out[L * MN * K:] == 0xA5), "write past the destination"
+    assert np.array_equal(out[:L * MN * K].reshape(L, MN, K), src.transpose(0, 2, 1))
+
+
+@pytest.mark.parametrize("a_major,b_major", [("m", "k"), ("k", "n"), ("m", "n")])
+def test_mmajor_operands_through_wrapper(lib, a_major, b_major):
+    M, N, K, L, sf = 320, 272, 384, 2, 32
+    p = W.make_problem(M, N, K, L, sf, E4, E5, seed=23)
+    dev = torch.device("cuda:0")
+
+    def view(codes, dtype, major):
+        # codes (L, rows, K) -> the pages' (rows, K, L) view: k-major as stored, or m/n-major
+        t = torch.from_numpy(np.ascontiguousarray(codes)).to(dev).view(dtype)
+        if major == "k":
+            return t.permute(1, 2, 0)
+        mm = t.permute(0, 2, 1).contiguous()           # (L, K, rows), rows contiguous
+        return mm.permute(2, 1, 0)                     # (rows, K, L) with strides (1, rows, rows*K)
+
+    a = view(p["A"], torch.float8_e4m3fn, a_major)
+    b = view(p["B"], torch.float8_e5m2, b_major)
+    if a_major == "m":
+        assert a.stride() == (1, M, M * K)
+    sfa, sfb = torch.from_numpy(p["SFA"]).to(dev), torch.from_numpy(p["SFB"]).to(dev)
+    c, amax = lib.gemm_amax(a, b, sfa, sfb, sf_vec_size=sf)
+    ck, amaxk = lib.gemm_amax(view(p["A"], torch.float8_e4m3fn, "k"), view(p["B"], torch.float8_e5m2, "k"),
+                              sfa, sfb, sf_vec_size=sf)
+    torch.cuda.synchronize()
+    assert torch.equal(c, ck) and torch.equal(amax, amaxk)
+    c_ref, s_ref, amax_ref = oracle.gemm_amax(p["A"], p["B"], p["SFA"], p["SFB"], M, N, K, L, sf, E4, E5)
+    check_c(c.permute(2, 0, 1).cpu().numpy(), c_ref, s_ref, f"A {a_major}-major, B {b_major}-major")
+    check_amax(amax.item(), amax_ref)
