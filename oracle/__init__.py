@@ -22,6 +22,8 @@ in float64, where every decoded product is exact.  Modules:
 * ``mx_quantize`` -- MX block quantisation of float32 data into codes and
                    E8M0 scales in the atom layout (the step that produces
                    the GEMM's inputs).
+* ``proj_rope`` -- the projection page's per-head RoPE and dual-direction
+                   MXFP8 quantisation of the GEMM output.
 
 Every function has a pin in ``tests/test_oracle_*.py``; see each module's
 header for which pin covers it.
@@ -33,6 +35,7 @@ from .sf_atom import sf_physical_shape, sf_logical_shape, sf_logical_view, expan
 from .gemm_amax import (dequantize, gemm_amax, gemm_amax_loops, gemm_rows, gemm_entries,
                         amax_of)
 from .mx_quantize import mx_quantize, block_max, block_exponent, encode_rne, place_scales, pack_e2m1
+from .proj_rope import rope, proj_rope_mxfp8
 
 __all__ = [
     "decode", "decode_e4m3", "decode_e5m2", "decode_e8m0", "decode_e2m1", "unpack_e2m1", "element_codes",
@@ -40,4 +43,5 @@ __all__ = [
     "sf_physical_shape", "sf_logical_shape", "sf_logical_view", "expand_scales",
     "dequantize", "gemm_amax", "gemm_amax_loops", "gemm_rows", "gemm_entries", "amax_of",
     "mx_quantize", "block_max", "block_exponent", "encode_rne", "place_scales", "pack_e2m1",
+    "rope", "proj_rope_mxfp8",
 ]
