@@ -47,7 +47,8 @@ MXG_ERR_FLAGS = -8
 
 EXPORTED = ("mxgemm_amax", "mxgemm_amax_ex", "mxgemm_amax_reset", "mxgemm_check_support",
             "mxgemm_sf_bytes", "mxgemm_launch_config", "mxgemm_strerror", "mxgemm_mx_quantize",
-            "mxgemm_sf_rowwise_to_atoms", "mxgemm_plan_init", "mxgemm_plan_execute", "mxgemm_codes_to_kmajor")
+            "mxgemm_sf_rowwise_to_atoms", "mxgemm_plan_init", "mxgemm_plan_execute", "mxgemm_codes_to_kmajor",
+            "mxgemm_proj_rope_mxfp8")
 
 
 class MxgemmError(Exception):
@@ -97,6 +98,8 @@ def _load():
     lib.mxgemm_plan_execute.restype = ci
     lib.mxgemm_codes_to_kmajor.argtypes = [vp, vp, i64, i64, i64, vp]
     lib.mxgemm_codes_to_kmajor.restype = ci
+    lib.mxgemm_proj_rope_mxfp8.argtypes = [vp] * 7 + [i64] * 4 + [vp]
+    lib.mxgemm_proj_rope_mxfp8.restype = ci
     return lib
 
 
@@ -205,6 +208,32 @@ def _as_lrk(t, name, stream=None):
         return dst, rows, k, l
     raise MxgemmValueError(MXG_ERR_ALIGN, f"{name} must be k-major (strides (K, 1, rows*K)) or, for FP8 codes, "
                                           f"m-major (strides (1, rows, rows*K)), batch outermost")
+
+
+def proj_rope_mxfp8(y, cos, sin, num_heads, head_dim=192, qk_rope=64, stream=None, out=None):
+    """C-ABI mxgemm_proj_rope_mxfp8 on torch tensors: y (tokens, num_heads * head_dim) float32, cos / sin
+    (tokens, qk_rope) bfloat16.  Returns (out_fp8_row, out_scales_row, out_fp8_col, out_scales_col) as the
+    projection page's wrapper does: codes (tokens, H, D) float8_e4m3fn, scales uint8 (tokens, H, D/32) and
+    (tokens/32, H, D); `out` may hold those four tensors preallocated."""
+    import torch
+    tokens = y.shape[0]
+    if out is None:
+        dev = y.device
+        out = (torch.empty((tokens, num_heads, head_dim), dtype=torch.float8_e4m3fn, device=dev),
+               torch.empty((tokens, num_heads, head_dim // 32), dtype=torch.uint8, device=dev),
+               torch.empty((tokens, num_heads, head_dim), dtype=torch.float8_e4m3fn, device=dev),
+               torch.empty((tokens // 32, num_heads, head_dim), dtype=torch.uint8, device=dev))
+    for t, name in ((y, "y"), (cos, "cos"), (sin, "sin")) + tuple(zip(out, ("row", "row scales", "col",
+                                                                         "col scales"))):
+        if not t.is_contiguous():
+            raise MxgemmValueError(MXG_ERR_ALIGN, f"{name} must be contiguous")
+    if y.dtype != torch.float32 or cos.dtype != torch.bfloat16 or sin.dtype != torch.bfloat16:
+        raise MxgemmValueError(MXG_ERR_FMT, "y must be float32, cos and sin bfloat16")
+    st = _lib.mxgemm_proj_rope_mxfp8(_ptr(y), _ptr(cos), _ptr(sin), _ptr(out[0]), _ptr(out[1]), _ptr(out[2]),
+                                     _ptr(out[3]), tokens, num_heads, head_dim, qk_rope, _stream(stream))
+    if st != MXG_OK:
+        _raise(st)
+    return out
 
 
 def codes_to_kmajor(src, dst, MN, K, L, stream=None):
@@ -358,6 +387,7 @@ __all__ = [
     "mxgemm_launch_config", "mxgemm_strerror", "gemm_amax", "LIB_PATH", "EXPORTED",
     "mxgemm_mx_quantize", "mx_quantize", "mxgemm_sf_rowwise_to_atoms", "sf_from_rowwise", "Plan",
     "MXG_FMT_E4M3", "MXG_FMT_E5M2", "MXG_FMT_E2M1", "MXG_FLAG_AMAX_ACCUMULATE", "MXG_FLAG_FP8_MFMA", "MXG_FLAG_TILE_128",
-    "MXG_FLAG_TILE_256", "MXG_FLAG_C_BF16", "MXG_FLAG_C_F16", "MXG_FLAG_C_MMAJOR", "codes_to_kmajor", "MxgemmError", "MxgemmValueError",
+    "MXG_FLAG_TILE_256", "MXG_FLAG_C_BF16", "MXG_FLAG_C_F16", "MXG_FLAG_C_MMAJOR", "codes_to_kmajor",
+    "proj_rope_mxfp8", "MxgemmError", "MxgemmValueError",
     "MxgemmRuntimeError",
 ]

@@ -14,6 +14,7 @@
 #include "mx_quantize.hpp"
 #include "sf_repack.hpp"
 #include "codes_transpose.hpp"
+#include "proj_rope.hpp"
 #include "mxgemm_big.hpp"
 #include "mxgemm_kernel.hpp"
 
@@ -478,6 +479,45 @@ int mxgemm_codes_to_kmajor(const void* src, void* dst, int64_t MN, int64_t K, in
   p.num_tiles = (int)(L * p.tiles_mn * p.tiles_k);
   const int64_t grid = std::min<int64_t>(p.num_tiles, 16LL * cus);
   hipLaunchKernelGGL(mxg::transpose::codes_to_kmajor_kernel, dim3((unsigned)grid), dim3(mxg::transpose::kThreads), 0,
+                     (hipStream_t)stream, p);
+  return hipGetLastError() == hipSuccess ? MXG_OK : MXG_ERR_LAUNCH;
+}
+
+int mxgemm_proj_rope_mxfp8(const float* Y, const uint16_t* cos_bf16, const uint16_t* sin_bf16, uint8_t* row_codes,
+                           uint8_t* row_scales, uint8_t* col_codes, uint8_t* col_scales, int64_t tokens,
+                           int64_t num_heads, int64_t head_dim, int64_t qk_rope, void* stream) {
+  if (tokens < 0 || num_heads < 0 || head_dim <= 0 || qk_rope < 0) return MXG_ERR_SHAPE;
+  if (head_dim % 32 != 0 || head_dim > mxg::rope::kMaxD || qk_rope % 2 != 0 || qk_rope > head_dim)
+    return MXG_ERR_SHAPE;
+  if (!fits_i32(tokens) || !fits_i32(num_heads) || !fits_i32(num_heads * head_dim) ||
+      tokens * num_heads > (INT64_MAX / 8) / head_dim)
+    return MXG_ERR_SHAPE;
+  if (tokens % 32 != 0) return MXG_ERR_ALIGN;  // column blocks of 32 tokens
+  if ((tokens / 32) * num_heads > 0x7FFFFFFFLL) return MXG_ERR_SHAPE;
+  if (tokens == 0 || num_heads == 0) return MXG_OK;
+  if (!Y || !row_codes || !row_scales || !col_codes || !col_scales || (qk_rope > 0 && (!cos_bf16 || !sin_bf16)))
+    return MXG_ERR_NULL;
+  if (!aligned16(Y) || !aligned16(row_codes) || !aligned16(col_codes)) return MXG_ERR_ALIGN;
+  int dev = 0, cus = 0;
+  int st = device_check(&dev, &cus);
+  if (st != MXG_OK) return st;
+  if (!on_device(Y, dev) || !on_device(row_codes, dev) || !on_device(row_scales, dev) || !on_device(col_codes, dev) ||
+      !on_device(col_scales, dev) || (qk_rope > 0 && (!on_device(cos_bf16, dev) || !on_device(sin_bf16, dev))))
+    return MXG_ERR_DEVICE;
+  mxg::rope::RParams p;
+  p.Y = Y;
+  p.cs = cos_bf16;
+  p.sn = sin_bf16;
+  p.row_codes = row_codes;
+  p.row_scales = row_scales;
+  p.col_codes = col_codes;
+  p.col_scales = col_scales;
+  p.H = (int)num_heads;
+  p.D = (int)head_dim;
+  p.QR = (int)qk_rope;
+  p.num_tiles = (int)((tokens / 32) * num_heads);
+  const int64_t grid = std::min<int64_t>(p.num_tiles, 32LL * cus);
+  hipLaunchKernelGGL(mxg::rope::proj_rope_mxfp8_kernel, dim3((unsigned)grid), dim3(mxg::rope::kThreads), 0,
                      (hipStream_t)stream, p);
   return hipGetLastError() == hipSuccess ? MXG_OK : MXG_ERR_LAUNCH;
 }

@@ -299,6 +299,41 @@ int mxgemm_sf_rowwise_to_atoms(const uint8_t* rowwise, uint8_t* SF, int64_t MN, 
  */
 int mxgemm_codes_to_kmajor(const void* src, void* dst, int64_t MN, int64_t K, int64_t L, void* stream);
 
+/*
+ * mxgemm_proj_rope_mxfp8 -- the projection's per-head RoPE and dual-direction
+ * MXFP8 quantisation ("GEMM + RoPE + MXFP8 Projection (SM100)", sections
+ * "Overview", "Shapes" and "Equations"), applied to the float32 output Y of
+ * mxgemm_amax (M = tokens, N = num_heads * head_dim).
+ *
+ *   Y          : (tokens, num_heads * head_dim) float32, 16-byte aligned.
+ *   cos_bf16,
+ *   sin_bf16   : (tokens, qk_rope) bfloat16 bit patterns.
+ *   row_codes  : (tokens, num_heads, head_dim) E4M3 codes, blocks of 32 along
+ *                head_dim; row_scales: (tokens, num_heads, head_dim / 32)
+ *                E8M0 bytes.
+ *   col_codes  : (tokens, num_heads, head_dim) E4M3 codes, blocks of 32 along
+ *                tokens; col_scales: (tokens / 32, num_heads, head_dim) E8M0.
+ *
+ * RoPE acts on the last qk_rope features of each head, interleaved in and
+ * halves out: with (a_i, b_i) = (y[2i], y[2i+1]) of that part and
+ * R = qk_rope / 2, out[i] = a_i cos[i] - b_i sin[i] and
+ * out[R+i] = b_i cos[R+i] + a_i sin[R+i], in float32 with each product and
+ * the sum rounded on its own.  Block scale 2^e with e the smallest integer
+ * giving 448 * 2^e >= the block's largest magnitude (0 for an all-zero
+ * block), codes rounded to nearest, ties to even (the rule of
+ * mxgemm_mx_quantize).
+ *
+ * Asynchronous on `stream`; all buffers caller-owned device memory, outputs
+ * not overlapping the inputs.  Errors (before any work): MXG_ERR_SHAPE
+ * (head_dim not a multiple of 32 or above 256, qk_rope odd or above
+ * head_dim, sizes too large), MXG_ERR_ALIGN (tokens % 32, or Y / the code
+ * buffers not 16-byte aligned), MXG_ERR_NULL, MXG_ERR_DEVICE.  tokens or
+ * num_heads == 0 queues nothing and returns MXG_OK.
+ */
+int mxgemm_proj_rope_mxfp8(const float* Y, const uint16_t* cos_bf16, const uint16_t* sin_bf16, uint8_t* row_codes,
+                           uint8_t* row_scales, uint8_t* col_codes, uint8_t* col_scales, int64_t tokens,
+                           int64_t num_heads, int64_t head_dim, int64_t qk_rope, void* stream);
+
 const char* mxgemm_strerror(int status);
 
 #ifdef __cplusplus
