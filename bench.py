@@ -362,15 +362,121 @@ def bench_quantize(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_proj(args):
+    """One JSON line for the projection pipeline of the projection page at the projection workload's
+    shape: a step repacks both operands' row-wise E8M0 scales into atoms, runs the GEMM + amax into
+    float32 Y, then the per-head RoPE and dual-direction MXFP8 quantisation of Y."""
+    import numpy as np
+    import torch
+
+    import block_scaled_precision_e4m3_amd as lib
+    import workloads as W
+    heads, d, qr = 128, 192, 64
+    p = W.make_workload(5)
+    tokens, n, k, sf = p["M"], p["N"], p["K"], p["sf"]
+    assert n == heads * d
+    kb = W.cdiv(k, sf)
+
+    def rowwise(phys, mn):
+        # the (mn, kb) byte of the physical (1, MNb, Kg, 32, 4, 4) atom buffer
+        v = phys.reshape(-1, W.cdiv(k, 4 * sf), 32, 4, 4)
+        m, b = np.arange(mn)[:, None], np.arange(kb)[None, :]
+        return np.ascontiguousarray(v[m // 128, b // 4, m % 32, (m // 32) % 4, b % 4])
+
+    dev = torch.device("cuda:0")
+    A, B = torch.from_numpy(p["A"][0]).to(dev), torch.from_numpy(p["B"][0]).to(dev)
+    xs = torch.from_numpy(rowwise(p["SFA"], tokens)).to(dev)
+    ws = torch.from_numpy(rowwise(p["SFB"], n)).to(dev)
+    sfa = torch.empty(W.sf_bytes(tokens, k, 1, sf), dtype=torch.uint8, device=dev)
+    sfb = torch.empty(W.sf_bytes(n, k, 1, sf), dtype=torch.uint8, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    theta = torch.rand((tokens, qr // 2), generator=gen, device=dev) * 6.283185307179586
+    cs = torch.cos(theta).repeat(1, 2).to(torch.bfloat16).contiguous()
+    sn = torch.sin(theta).repeat(1, 2).to(torch.bfloat16).contiguous()
+    Y = torch.empty((tokens, n), dtype=torch.float32, device=dev)
+    amax = torch.zeros(4, dtype=torch.float32, device=dev)
+    outs = (torch.empty((tokens, heads, d), dtype=torch.float8_e4m3fn, device=dev),
+            torch.empty((tokens, heads, d // 32), dtype=torch.uint8, device=dev),
+            torch.empty((tokens, heads, d), dtype=torch.float8_e4m3fn, device=dev),
+            torch.empty((tokens // 32, heads, d), dtype=torch.uint8, device=dev))
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+
+    def step(e=None):
+        if e:
+            e[0].record(stream)
+        lib.mxgemm_sf_rowwise_to_atoms(xs, sfa, tokens, k, 1, sf, sh)
+        lib.mxgemm_sf_rowwise_to_atoms(ws, sfb, n, k, 1, sf, sh)
+        if e:
+            e[1].record(stream)
+        lib.mxgemm_amax(A, B, sfa, sfb, Y, amax, tokens, n, k, 1, sf, lib.MXG_FMT_E4M3, lib.MXG_FMT_E4M3, sh)
+        if e:
+            e[2].record(stream)
+        lib.proj_rope_mxfp8(Y, cs, sn, heads, d, qr, stream=stream, out=outs)
+        if e:
+            e[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    part = [sum(e[j].elapsed_time(e[j + 1]) for e in ev) / args.steps for j in range(3)]
+    ms_per_step = wall * 1e3 / args.steps
+    flops = W.flops(tokens, n, k, 1)
+    rope_bytes = 4 * tokens * n + 2 * 2 * tokens * qr + 2 * tokens * n + 2 * (tokens * n // 32)
+    rope_gbs = rope_bytes / (part[2] * 1e-3) / 1e9
+    out = {
+        "metric": "projection GEMM + RoPE + dual-direction MXFP8 TFLOP/s (GEMM flops over the whole step)",
+        "value": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8-e4m3 codes in, fp32 Y, e4m3 codes + e8m0 scales out",
+        "data": "synthetic (seeded, MX-quantised; random rotary angles)",
+        "config": {"workload": "projection pipeline", "tokens": tokens, "num_heads": heads, "head_dim": d,
+                   "qk_rope": qr, "q_lora": k, "sf_vec_size": sf},
+        "repack_ms": round(part[0], 4), "gemm_ms": round(part[1], 4), "rope_quant_ms": round(part[2], 4),
+        "roofline": {"kernel": "proj_rope_mxfp8", "bound": "hbm", "achieved": round(rope_gbs, 1),
+                     "peak": HBM_GBS, "unit": "GB/s", "frac": round(rope_gbs / HBM_GBS, 4), "traffic": None,
+                     "algorithmic_bytes": rope_bytes},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        yh = Y.cpu().numpy()
+        ch, shh = cs.float().cpu().numpy(), sn.float().cpu().numpy()
+        t_total, done = 0.0, 0
+        while t_total < 10.0:
+            t1 = time.perf_counter()
+            r0 = 256 * ((done // 256) % (tokens // 256))
+            oracle.proj_rope_mxfp8(yh[r0:r0 + 256], ch[r0:r0 + 256], shh[r0:r0 + 256], heads, d, qr)
+            t_total += time.perf_counter() - t1
+            done += 256
+        try:
+            cores = len(os.sched_getaffinity(0))
+        except AttributeError:
+            cores = os.cpu_count()
+        out["cpu_baseline"] = {
+            "value": rope_bytes * done / tokens / t_total / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"oracle.proj_rope_mxfp8 (RoPE + both quantisation directions) on {done} tokens in blocks of "
+                      f"256, {t_total:.1f} s; value counts the RoPE kernel's algorithmic bytes per token"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=5)
-    ap.add_argument("--op", choices=["gemm", "quantize"], default="gemm",
+    ap.add_argument("--op", choices=["gemm", "quantize", "proj"], default="gemm",
                     help="gemm: the GEMM + amax step (default); quantize: the MX quantisation of the "
-                         "workload's float32 operands")
+                         "workload's float32 operands; proj: the projection pipeline (row-wise scales -> GEMM -> "
+                         "RoPE + dual-direction MXFP8) at the projection workload's shape")
     ap.add_argument("--fp8-mfma", action="store_true", help="time the reduced-precision FP8 MFMA path")
     ap.add_argument("--fp4", action="store_true",
                     help="the workload's shape with packed FP4 (E2M1) operands and sf = 32 (same value recipe)")
@@ -403,6 +509,9 @@ def main():
 
     if args.op == "quantize":
         bench_quantize(args)
+        return
+    if args.op == "proj":
+        bench_proj(args)
         return
 
     import torch

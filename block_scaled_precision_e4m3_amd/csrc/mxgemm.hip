@@ -516,7 +516,10 @@ int mxgemm_proj_rope_mxfp8(const float* Y, const uint16_t* cos_bf16, const uint1
   p.D = (int)head_dim;
   p.QR = (int)qk_rope;
   p.num_tiles = (int)((tokens / 32) * num_heads);
-  const int64_t grid = std::min<int64_t>(p.num_tiles, 32LL * cus);
+  // runs of 4 heads (4 * head_dim bytes of a token's codes, whole lines for a
+  // head_dim of 32 * odd) where that still gives 16 workgroups per CU
+  p.per_wg = p.num_tiles >= 64LL * cus ? 4 : 1;
+  const int64_t grid = cdiv(p.num_tiles, p.per_wg);
   hipLaunchKernelGGL(mxg::rope::proj_rope_mxfp8_kernel, dim3((unsigned)grid), dim3(mxg::rope::kThreads), 0,
                      (hipStream_t)stream, p);
   return hipGetLastError() == hipSuccess ? MXG_OK : MXG_ERR_LAUNCH;

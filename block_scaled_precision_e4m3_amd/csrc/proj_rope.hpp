@@ -17,11 +17,14 @@
 //
 // One workgroup of 256 threads per (32-token block, head).  The 32 x D tile
 // is read with 16-byte loads (each token's D floats are contiguous) and
-// parked in LDS at a pitch of D + 1 floats, so that a column read by 32
-// lanes hits 32 banks.  RoPE runs in place after a barrier.  Row blocks:
-// one thread per (token, block) quantises 32 consecutive values and stores
-// 32 codes.  Column blocks: one thread per feature quantises its 32 tokens
-// into an LDS byte tile, which then leaves as whole rows.
+// parked in LDS at a pitch of D + 4 floats (rows stay 16-byte aligned, and a
+// column read by 64 lanes hits 64 banks).  RoPE runs in place after a
+// barrier.  Then one thread per feature finds its column block's exponent,
+// and finally thread (token r, features 4c..4c+3) makes both codes of its 4
+// values: the row block's maximum comes from the 8 threads of the block
+// (consecutive lanes, xor shuffles), the column exponents from LDS; each
+// direction's 4 codes leave as one dword store, consecutive threads writing
+// consecutive dwords of a token's row.
 #pragma once
 
 #include "mx_quantize.hpp"
@@ -42,43 +45,31 @@ struct RParams {
   uint8_t* col_scales;      // (tokens / 32, H, D)
   int H, D, QR;
   int num_tiles;            // tokens / 32 * H
+  int per_wg;               // consecutive tiles per workgroup
 };
 
 __device__ __forceinline__ float bf16_bits_to_float(uint16_t b) { return __uint_as_float((unsigned)b << 16); }
 
-// 32 floats at stride `step` (in floats) from LDS -> block exponent and 32 codes
-__device__ __forceinline__ int quantize32(const float* src, int step, unsigned (&w)[8]) {
-  float bm = 0.f;
-#pragma unroll
-  for (int j = 0; j < 32; ++j) bm = fmaxf(bm, fabsf(src[j * step]));
-  const int e = quant::block_exponent<0>(bm);
-#pragma unroll
-  for (int q = 0; q < 8; ++q)
-    w[q] = quant::codes4<0>(ldexpf(src[(4 * q) * step], -e), ldexpf(src[(4 * q + 1) * step], -e),
-                            ldexpf(src[(4 * q + 2) * step], -e), ldexpf(src[(4 * q + 3) * step], -e));
-  return e;
-}
-
 __global__ __launch_bounds__(kThreads) void proj_rope_mxfp8_kernel(RParams p) {
-  __shared__ float z[32 * (kMaxD + 1)];
-  __shared__ __attribute__((aligned(16))) uint8_t qc[32 * kMaxD];
+  __shared__ __attribute__((aligned(16))) float z[32 * (kMaxD + 4)];
+  __shared__ int ecol[kMaxD];
   const int t = threadIdx.x;
-  const int D = p.D, P = p.D + 1, HD = p.H * p.D;
+  const int D = p.D, P = p.D + 4, HD = p.H * p.D;
   const int nope = p.D - p.QR, R = p.QR / 2, nb = p.D / 32;
-  for (int a = blockIdx.x; a < p.num_tiles; a += gridDim.x) {
+  const int q4 = D / 4;  // float4 groups per token (a multiple of 8: D % 32 == 0)
+  // a contiguous run of tiles per workgroup: consecutive heads of one token
+  // block, so that a workgroup writes whole 128-byte lines of the code rows
+  // (a head's row is D bytes) instead of sharing them with workgroups on
+  // other XCDs
+  const int a0 = blockIdx.x * p.per_wg, a1 = min(a0 + p.per_wg, p.num_tiles);
+  for (int a = a0; a < a1; ++a) {
     const int h = a % p.H, tb = a / p.H;
     const int64_t row0 = (int64_t)tb * 32;
     __syncthreads();  // the previous tile's LDS reads are done
-    // load: 32 rows of D floats (D / 4 float4 per row)
-    const int q4 = D / 4;
     for (int f = t; f < 32 * q4; f += kThreads) {
       const int r = f / q4, c = f - r * q4;
       const float4 v = *reinterpret_cast<const float4*>(p.Y + (row0 + r) * HD + (int64_t)h * D + 4 * c);
-      float* dst = z + r * P + 4 * c;
-      dst[0] = v.x;
-      dst[1] = v.y;
-      dst[2] = v.z;
-      dst[3] = v.w;
+      *reinterpret_cast<float4*>(z + r * P + 4 * c) = v;
     }
     __syncthreads();
     // RoPE: pair i of row r, results held in registers until every pair has
@@ -110,32 +101,33 @@ __global__ __launch_bounds__(kThreads) void proj_rope_mxfp8_kernel(RParams p) {
       }
     }
     __syncthreads();
-    // row blocks: thread (r, blk)
-    for (int f = t; f < 32 * nb; f += kThreads) {
-      const int r = f / nb, blk = f - r * nb;
-      unsigned w[8];
-      const int e = quantize32(z + r * P + 32 * blk, 1, w);
-      const int64_t o = ((row0 + r) * p.H + h) * (int64_t)D + 32 * blk;
-      *reinterpret_cast<uint4*>(p.row_codes + o) = uint4{w[0], w[1], w[2], w[3]};
-      *reinterpret_cast<uint4*>(p.row_codes + o + 16) = uint4{w[4], w[5], w[6], w[7]};
-      p.row_scales[((row0 + r) * p.H + h) * nb + blk] = (uint8_t)(e + 127);
-    }
-    // column blocks: thread d quantises its 32 tokens into the LDS byte tile
+    // column blocks: the exponent of feature d over the 32 tokens
     for (int d = t; d < D; d += kThreads) {
-      unsigned w[8];
-      const int e = quantize32(z + d, P, w);
-#pragma unroll
-      for (int q = 0; q < 8; ++q)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) qc[(4 * q + j) * D + d] = (uint8_t)(w[q] >> (8 * j));
+      float bm = 0.f;
+#pragma unroll 8
+      for (int r = 0; r < 32; ++r) bm = fmaxf(bm, fabsf(z[r * P + d]));
+      const int e = quant::block_exponent<0>(bm);
+      ecol[d] = e;
       p.col_scales[((int64_t)tb * p.H + h) * D + d] = (uint8_t)(e + 127);
     }
     __syncthreads();
-    const int d4 = D / 4;
-    for (int f = t; f < 32 * d4; f += kThreads) {
-      const int r = f / d4, c = f - r * d4;
-      *reinterpret_cast<unsigned*>(p.col_codes + ((row0 + r) * p.H + h) * (int64_t)D + 4 * c) =
-          *reinterpret_cast<const unsigned*>(qc + r * D + 4 * c);
+    // both directions' codes: thread (r, c) holds features 4c..4c+3 of token
+    // r; the 8 threads of a row block are consecutive lanes (q4 and the
+    // thread count are multiples of 8, so every lane takes part each pass)
+    for (int f = t; f < 32 * q4; f += kThreads) {
+      const int r = f / q4, c = f - r * q4;
+      const float4 v = *reinterpret_cast<const float4*>(z + r * P + 4 * c);
+      float bm = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+#pragma unroll
+      for (int sh = 1; sh < 8; sh <<= 1) bm = fmaxf(bm, __shfl_xor(bm, sh));
+      const int e = quant::block_exponent<0>(bm);
+      const int64_t o = ((row0 + r) * p.H + h) * (int64_t)D + 4 * c;
+      *reinterpret_cast<unsigned*>(p.row_codes + o) =
+          quant::codes4<0>(ldexpf(v.x, -e), ldexpf(v.y, -e), ldexpf(v.z, -e), ldexpf(v.w, -e));
+      if ((c & 7) == 0) p.row_scales[((row0 + r) * p.H + h) * nb + (c >> 3)] = (uint8_t)(e + 127);
+      *reinterpret_cast<unsigned*>(p.col_codes + o) =
+          quant::codes4<0>(ldexpf(v.x, -ecol[4 * c]), ldexpf(v.y, -ecol[4 * c + 1]), ldexpf(v.z, -ecol[4 * c + 2]),
+                           ldexpf(v.w, -ecol[4 * c + 3]));
     }
   }
 }
