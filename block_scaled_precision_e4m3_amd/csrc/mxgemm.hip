@@ -487,7 +487,8 @@ int mxgemm_proj_rope_mxfp8(const float* Y, const uint16_t* cos_bf16, const uint1
                            uint8_t* row_scales, uint8_t* col_codes, uint8_t* col_scales, int64_t tokens,
                            int64_t num_heads, int64_t head_dim, int64_t qk_rope, void* stream) {
   if (tokens < 0 || num_heads < 0 || head_dim <= 0 || qk_rope < 0) return MXG_ERR_SHAPE;
-  if (head_dim % 32 != 0 || head_dim > mxg::rope::kMaxD || qk_rope % 2 != 0 || qk_rope > head_dim)
+  if (head_dim % 32 != 0 || head_dim > mxg::rope::kMaxD || qk_rope % 2 != 0 || qk_rope > head_dim ||
+      qk_rope > mxg::rope::kMaxQR)
     return MXG_ERR_SHAPE;
   if (!fits_i32(tokens) || !fits_i32(num_heads) || !fits_i32(num_heads * head_dim) ||
       tokens * num_heads > (INT64_MAX / 8) / head_dim)
@@ -497,7 +498,9 @@ int mxgemm_proj_rope_mxfp8(const float* Y, const uint16_t* cos_bf16, const uint1
   if (tokens == 0 || num_heads == 0) return MXG_OK;
   if (!Y || !row_codes || !row_scales || !col_codes || !col_scales || (qk_rope > 0 && (!cos_bf16 || !sin_bf16)))
     return MXG_ERR_NULL;
-  if (!aligned16(Y) || !aligned16(row_codes) || !aligned16(col_codes)) return MXG_ERR_ALIGN;
+  if (!aligned16(Y) || !aligned16(row_codes) || !aligned16(col_codes) ||
+      (qk_rope > 0 && (!aligned16(cos_bf16) || !aligned16(sin_bf16))))
+    return MXG_ERR_ALIGN;
   int dev = 0, cus = 0;
   int st = device_check(&dev, &cus);
   if (st != MXG_OK) return st;

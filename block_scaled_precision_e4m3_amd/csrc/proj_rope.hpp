@@ -15,12 +15,15 @@
 //   quantiser (mx_quantize.hpp): e the smallest integer with 448 * 2^e >= the
 //   block's largest magnitude, codes rounded to nearest, ties to even.
 //
-// One workgroup of 256 threads per (32-token block, head).  The 32 x D tile
-// is read with 16-byte loads (each token's D floats are contiguous) and
-// parked in LDS at a pitch of D + 4 floats (rows stay 16-byte aligned, and a
-// column read by 64 lanes hits 64 banks).  RoPE runs in place after a
-// barrier.  Then one thread per feature finds its column block's exponent,
-// and finally thread (token r, features 4c..4c+3) makes both codes of its 4
+// One workgroup of 512 threads per (32-token block, head), in runs of
+// consecutive heads.  The 32 x D tile is read with 16-byte loads (each
+// token's D floats are contiguous) and parked in LDS at a pitch of D + 4
+// floats (rows stay 16-byte aligned, and a column read by 64 lanes hits 64
+// banks); the rotary features are de-interleaved on the way in (a_i to
+// position i of the rotary part, b_i to R + i), so that each thread then
+// rotates its own pairs in place.  The tokens' cos / sin rows come in with
+// 16-byte loads too.  Then one thread per feature finds its column block's
+// exponent, and finally thread (token r, features 4c..4c+3) makes both codes of its 4
 // values: the row block's maximum comes from the 8 threads of the block
 // (consecutive lanes, xor shuffles), the column exponents from LDS; each
 // direction's 4 codes leave as one dword store, consecutive threads writing
@@ -32,8 +35,9 @@
 namespace mxg {
 namespace rope {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;  // 8 waves: LDS allows 3 workgroups per CU
 constexpr int kMaxD = 256;
+constexpr int kMaxQR = 128;
 
 struct RParams {
   const float* Y;           // (tokens, H * D)
@@ -53,6 +57,7 @@ __device__ __forceinline__ float bf16_bits_to_float(uint16_t b) { return __uint_
 __global__ __launch_bounds__(kThreads) void proj_rope_mxfp8_kernel(RParams p) {
   __shared__ __attribute__((aligned(16))) float z[32 * (kMaxD + 4)];
   __shared__ int ecol[kMaxD];
+  __shared__ __attribute__((aligned(16))) uint16_t csl[32 * kMaxQR], snl[32 * kMaxQR];
   const int t = threadIdx.x;
   const int D = p.D, P = p.D + 4, HD = p.H * p.D;
   const int nope = p.D - p.QR, R = p.QR / 2, nb = p.D / 32;
@@ -66,39 +71,37 @@ __global__ __launch_bounds__(kThreads) void proj_rope_mxfp8_kernel(RParams p) {
     const int h = a % p.H, tb = a / p.H;
     const int64_t row0 = (int64_t)tb * 32;
     __syncthreads();  // the previous tile's LDS reads are done
+    // the tile into LDS, rotary features de-interleaved on the way: feature
+    // nope + 2i (a_i) to position nope + i, nope + 2i + 1 (b_i) to nope + R + i
     for (int f = t; f < 32 * q4; f += kThreads) {
       const int r = f / q4, c = f - r * q4;
       const float4 v = *reinterpret_cast<const float4*>(p.Y + (row0 + r) * HD + (int64_t)h * D + 4 * c);
-      *reinterpret_cast<float4*>(z + r * P + 4 * c) = v;
-    }
-    __syncthreads();
-    // RoPE: pair i of row r, results held in registers until every pair has
-    // been read (a fixed trip count keeps them out of scratch)
-    constexpr int kPairsPerThread = 32 * (kMaxD / 2) / kThreads;
-    float o1[kPairsPerThread], o2[kPairsPerThread];
+      if (4 * c + 3 < nope) {
+        *reinterpret_cast<float4*>(z + r * P + 4 * c) = v;
+      } else {
+        const float e4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int k = 0; k < kPairsPerThread; ++k) {
-      const int f = t + k * kThreads;
-      if (f < 32 * R) {
-        const int r = f / R, i = f - r * R;
-        const float av = z[r * P + nope + 2 * i], bv = z[r * P + nope + 2 * i + 1];
-        const uint16_t* cr = p.cs + (row0 + r) * p.QR;
-        const uint16_t* sr = p.sn + (row0 + r) * p.QR;
-        const float c1 = bf16_bits_to_float(cr[i]), s1 = bf16_bits_to_float(sr[i]);
-        const float c2 = bf16_bits_to_float(cr[R + i]), s2 = bf16_bits_to_float(sr[R + i]);
-        o1[k] = __fsub_rn(__fmul_rn(av, c1), __fmul_rn(bv, s1));
-        o2[k] = __fadd_rn(__fmul_rn(bv, c2), __fmul_rn(av, s2));
+        for (int j = 0; j < 4; ++j) {
+          const int d = 4 * c + j, k = d - nope;
+          z[r * P + (k < 0 ? d : nope + (k & 1) * R + (k >> 1))] = e4[j];
+        }
       }
     }
+    // the 32 tokens' cos / sin rows: 32 * QR * 2 contiguous bytes per table
+    for (int f = t; f < 4 * p.QR; f += kThreads) {
+      reinterpret_cast<uint4*>(csl)[f] = reinterpret_cast<const uint4*>(p.cs + row0 * p.QR)[f];
+      reinterpret_cast<uint4*>(snl)[f] = reinterpret_cast<const uint4*>(p.sn + row0 * p.QR)[f];
+    }
     __syncthreads();
-#pragma unroll
-    for (int k = 0; k < kPairsPerThread; ++k) {
-      const int f = t + k * kThreads;
-      if (f < 32 * R) {
-        const int r = f / R, i = f - r * R;
-        z[r * P + nope + i] = o1[k];
-        z[r * P + nope + R + i] = o2[k];
-      }
+    // RoPE: each thread rotates its own pairs (i, R + i) in place
+    for (int f = t; f < 32 * R; f += kThreads) {
+      const int r = f / R, i = f - r * R;
+      float* zr = z + r * P + nope;
+      const float av = zr[i], bv = zr[R + i];
+      const float c1 = bf16_bits_to_float(csl[r * p.QR + i]), s1 = bf16_bits_to_float(snl[r * p.QR + i]);
+      const float c2 = bf16_bits_to_float(csl[r * p.QR + R + i]), s2 = bf16_bits_to_float(snl[r * p.QR + R + i]);
+      zr[i] = __fsub_rn(__fmul_rn(av, c1), __fmul_rn(bv, s1));
+      zr[R + i] = __fadd_rn(__fmul_rn(bv, c2), __fmul_rn(av, s2));
     }
     __syncthreads();
     // column blocks: the exponent of feature d over the 32 tokens
@@ -113,7 +116,8 @@ __global__ __launch_bounds__(kThreads) void proj_rope_mxfp8_kernel(RParams p) {
     __syncthreads();
     // both directions' codes: thread (r, c) holds features 4c..4c+3 of token
     // r; the 8 threads of a row block are consecutive lanes (q4 and the
-    // thread count are multiples of 8, so every lane takes part each pass)
+    // thread count are multiples of 8, so the 8 lanes of a group take part in
+    // a pass together or not at all)
     for (int f = t; f < 32 * q4; f += kThreads) {
       const int r = f / q4, c = f - r * q4;
       const float4 v = *reinterpret_cast<const float4*>(z + r * P + 4 * c);

@@ -307,7 +307,7 @@ int mxgemm_codes_to_kmajor(const void* src, void* dst, int64_t MN, int64_t K, in
  *
  *   Y          : (tokens, num_heads * head_dim) float32, 16-byte aligned.
  *   cos_bf16,
- *   sin_bf16   : (tokens, qk_rope) bfloat16 bit patterns.
+ *   sin_bf16   : (tokens, qk_rope) bfloat16 bit patterns, 16-byte aligned.
  *   row_codes  : (tokens, num_heads, head_dim) E4M3 codes, blocks of 32 along
  *                head_dim; row_scales: (tokens, num_heads, head_dim / 32)
  *                E8M0 bytes.
@@ -326,8 +326,9 @@ int mxgemm_codes_to_kmajor(const void* src, void* dst, int64_t MN, int64_t K, in
  * Asynchronous on `stream`; all buffers caller-owned device memory, outputs
  * not overlapping the inputs.  Errors (before any work): MXG_ERR_SHAPE
  * (head_dim not a multiple of 32 or above 256, qk_rope odd or above
- * head_dim, sizes too large), MXG_ERR_ALIGN (tokens % 32, or Y / the code
- * buffers not 16-byte aligned), MXG_ERR_NULL, MXG_ERR_DEVICE.  tokens or
+ * head_dim or 128, sizes too large), MXG_ERR_ALIGN (tokens % 32, or Y, the
+ * code buffers, cos or sin not 16-byte aligned), MXG_ERR_NULL,
+ * MXG_ERR_DEVICE.  tokens or
  * num_heads == 0 queues nothing and returns MXG_OK.
  */
 int mxgemm_proj_rope_mxfp8(const float* Y, const uint16_t* cos_bf16, const uint16_t* sin_bf16, uint8_t* row_codes,

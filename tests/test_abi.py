@@ -115,6 +115,18 @@ def test_errors_before_device_work(lib):
     assert t(None, good, 80, 48, 1, None) == lib.MXG_ERR_NULL
     assert t(good, good, -16, 48, 1, None) == lib.MXG_ERR_SHAPE
     assert t(None, None, 0, 48, 1, None) == lib.MXG_OK              # nothing to do
+    pr = c.mxgemm_proj_rope_mxfp8
+    pr.argtypes = [vp] * 7 + [i64] * 4 + [vp]
+    pr.restype = ci
+    buf7 = [good] * 7
+    assert pr(*buf7, 64, 3, 200, 64, None) == lib.MXG_ERR_SHAPE      # head_dim % 32
+    assert pr(*buf7, 64, 3, 288, 64, None) == lib.MXG_ERR_SHAPE      # head_dim above 256
+    assert pr(*buf7, 64, 3, 192, 63, None) == lib.MXG_ERR_SHAPE      # odd rotary width
+    assert pr(*buf7, 64, 3, 192, 160, None) == lib.MXG_ERR_SHAPE     # rotary width above 128
+    assert pr(*buf7, 48, 3, 192, 64, None) == lib.MXG_ERR_ALIGN      # tokens % 32
+    assert pr(*([good, good + 2] + buf7[2:]), 64, 3, 192, 64, None) == lib.MXG_ERR_ALIGN   # cos
+    assert pr(*([None] + buf7[1:]), 64, 3, 192, 64, None) == lib.MXG_ERR_NULL
+    assert pr(*([None] * 7), 0, 3, 192, 64, None) == lib.MXG_OK        # nothing to do
     r = c.mxgemm_amax_reset
     r.argtypes = [vp, vp]
     r.restype = ci
