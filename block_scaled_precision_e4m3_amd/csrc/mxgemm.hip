@@ -523,8 +523,8 @@ int mxgemm_proj_rope_mxfp8(const float* Y, const uint16_t* cos_bf16, const uint1
   // head_dim of 32 * odd) where that still gives 16 workgroups per CU
   p.per_wg = p.num_tiles >= 64LL * cus ? 4 : 1;
   const int64_t grid = cdiv(p.num_tiles, p.per_wg);
-  hipLaunchKernelGGL(mxg::rope::proj_rope_mxfp8_kernel, dim3((unsigned)grid), dim3(mxg::rope::kThreads), 0,
-                     (hipStream_t)stream, p);
+  hipLaunchKernelGGL(mxg::rope::proj_rope_mxfp8_kernel, dim3((unsigned)grid), dim3(mxg::rope::kThreads),
+                     (unsigned)mxg::rope::lds_bytes(p.D, p.QR), (hipStream_t)stream, p);
   return hipGetLastError() == hipSuccess ? MXG_OK : MXG_ERR_LAUNCH;
 }
 

@@ -35,7 +35,7 @@
 namespace mxg {
 namespace rope {
 
-constexpr int kThreads = 512;  // 8 waves: LDS allows 3 workgroups per CU
+constexpr int kThreads = 512;  // 8 waves per workgroup
 constexpr int kMaxD = 256;
 constexpr int kMaxQR = 128;
 
@@ -52,12 +52,21 @@ struct RParams {
   int per_wg;               // consecutive tiles per workgroup
 };
 
+// bytes of dynamic LDS for head size D and rotary width QR (34 KB for 192 / 64:
+// four workgroups per CU)
+inline size_t lds_bytes(int D, int QR) { return (size_t)32 * (D + 4) * 4 + (size_t)D * 4 + (size_t)64 * QR * 2; }
+
 __device__ __forceinline__ float bf16_bits_to_float(uint16_t b) { return __uint_as_float((unsigned)b << 16); }
 
 __global__ __launch_bounds__(kThreads) void proj_rope_mxfp8_kernel(RParams p) {
-  __shared__ __attribute__((aligned(16))) float z[32 * (kMaxD + 4)];
-  __shared__ int ecol[kMaxD];
-  __shared__ __attribute__((aligned(16))) uint16_t csl[32 * kMaxQR], snl[32 * kMaxQR];
+  // dynamic LDS, lds_bytes(D, QR): the tile (32 x (D + 4) floats), the column
+  // exponents (D ints), the cos and sin rows (32 x QR bf16 each); every part
+  // starts 16-byte aligned (D % 32 == 0, QR even)
+  extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
+  float* z = reinterpret_cast<float*>(dyn);
+  int* ecol = reinterpret_cast<int*>(z + 32 * (p.D + 4));
+  uint16_t* csl = reinterpret_cast<uint16_t*>(ecol + p.D);
+  uint16_t* snl = csl + 32 * p.QR;
   const int t = threadIdx.x;
   const int D = p.D, P = p.D + 4, HD = p.H * p.D;
   const int nope = p.D - p.QR, R = p.QR / 2, nb = p.D / 32;
