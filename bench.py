@@ -56,6 +56,8 @@ def kernel_source_hash():
 def profile_name(workload_name, fp8_mfma, op="gemm"):
     if op == "quantize":
         return f"mx_quantize_kernel__{workload_name}_operands.txt"
+    if op == "proj":
+        return f"proj_rope_mxfp8_kernel__{workload_name}_pipeline.txt"
     return f"mxgemm_amax_kernel_{'fp8' if fp8_mfma else 'bf16'}__{workload_name}.txt"
 
 
@@ -103,6 +105,20 @@ def _is_quantize(name):
     return "mx_quantize_kernel" in name
 
 
+def _is_proj_rope(name):
+    return "proj_rope_mxfp8_kernel" in name
+
+
+# the projection pipeline's shape: the projection workload's GEMM, 128 heads x 192, 64 rotary features
+PROJ_HEADS, PROJ_HEAD_DIM, PROJ_QK_ROPE = 128, 192, 64
+
+
+def proj_rope_bytes(tokens, n, qr):
+    """Algorithmic bytes of the RoPE + dual MXFP8 kernel: float32 Y read, bf16 cos and sin read, both
+    directions' codes and scale bytes written."""
+    return 4 * tokens * n + 2 * 2 * tokens * qr + 2 * tokens * n + 2 * (tokens * n // 32)
+
+
 def quantize_operands_shape(workload):
     """The stacked float32 operands of a GEMM workload, quantised as one (L, M + N, K) tensor.
 
@@ -140,6 +156,11 @@ def rocprof_summary(d, workload, fp8_mfma, commands, op="gemm"):
         out = [f"# rocprofv3 summary: the MX quantisation kernel, the float32 operands of workload {cfg['name']} "
                f"stacked as one ({ql}, {qmn}, {qk}) tensor (A's {M} rows, then B's {N}), sf={qsf}, E4M3", ""]
         is_target = _is_quantize
+    elif op == "proj":
+        out = [f"# rocprofv3 summary: the RoPE + dual-direction MXFP8 kernel of the projection pipeline, "
+               f"workload {cfg['name']} (tokens={M}, {PROJ_HEADS} heads x {PROJ_HEAD_DIM}, "
+               f"{PROJ_QK_ROPE} rotary features)", ""]
+        is_target = _is_proj_rope
     else:
         out = [f"# rocprofv3 summary: the GEMM + amax kernel ({'fp8 MFMA' if fp8_mfma else 'bf16 MFMA'} path), "
                f"workload {cfg['name']} (M={M} N={N} K={K} L={L} sf={sf})", ""]
@@ -161,7 +182,11 @@ def rocprof_summary(d, workload, fp8_mfma, commands, op="gemm"):
             gemm_name, gemm_total = name, float(r["TotalDurationNs"])
             avg_us = float(r["AverageNs"]) / 1e3
     out.append("")
-    if avg_us and op == "quantize":
+    if avg_us and op == "proj":
+        out.append(f"kernel: {gemm_name}")
+        out.append(f"avg_duration_us: {avg_us:.2f}")
+        out.append(f"algorithmic_GBps_at_avg_duration: {proj_rope_bytes(M, N, PROJ_QK_ROPE) / (avg_us * 1e-6) / 1e9:.1f}")
+    elif avg_us and op == "quantize":
         out.append(f"kernel: {gemm_name}")
         out.append(f"avg_duration_us: {avg_us:.2f}")
         out.append(f"algorithmic_GBps_at_avg_duration: "
@@ -182,7 +207,8 @@ def rocprof_summary(d, workload, fp8_mfma, commands, op="gemm"):
         w_fac = COPY_PROBE_BYTES / (1024.0 * sum(cw) / len(cw))
         fb = sum(gf) / len(gf) * 1024.0 * f_fac
         wb = sum(gw) / len(gw) * 1024.0 * w_fac
-        ab = quantize_bytes(qmn, qk, ql, qsf) if op == "quantize" else W.algorithmic_bytes(M, N, K, L, sf)
+        ab = (quantize_bytes(qmn, qk, ql, qsf) if op == "quantize" else
+              proj_rope_bytes(M, N, PROJ_QK_ROPE) if op == "proj" else W.algorithmic_bytes(M, N, K, L, sf))
         out += ["",
                 "HBM traffic (--pmc FETCH_SIZE, then --pmc WRITE_SIZE; KiB per dispatch):",
                 f"  kernel FETCH_SIZE per dispatch (KiB, mean of {len(gf)}): {sum(gf) / len(gf):.0f}",
@@ -371,7 +397,7 @@ def bench_proj(args):
 
     import block_scaled_precision_e4m3_amd as lib
     import workloads as W
-    heads, d, qr = 128, 192, 64
+    heads, d, qr = PROJ_HEADS, PROJ_HEAD_DIM, PROJ_QK_ROPE
     p = W.make_workload(5)
     tokens, n, k, sf = p["M"], p["N"], p["K"], p["sf"]
     assert n == heads * d
@@ -429,7 +455,7 @@ def bench_proj(args):
     part = [sum(e[j].elapsed_time(e[j + 1]) for e in ev) / args.steps for j in range(3)]
     ms_per_step = wall * 1e3 / args.steps
     flops = W.flops(tokens, n, k, 1)
-    rope_bytes = 4 * tokens * n + 2 * 2 * tokens * qr + 2 * tokens * n + 2 * (tokens * n // 32)
+    rope_bytes = proj_rope_bytes(tokens, n, qr)
     rope_gbs = rope_bytes / (part[2] * 1e-3) / 1e9
     out = {
         "metric": "projection GEMM + RoPE + dual-direction MXFP8 TFLOP/s (GEMM flops over the whole step)",
@@ -442,9 +468,12 @@ def bench_proj(args):
                    "qk_rope": qr, "q_lora": k, "sf_vec_size": sf},
         "repack_ms": round(part[0], 4), "gemm_ms": round(part[1], 4), "rope_quant_ms": round(part[2], 4),
         "roofline": {"kernel": "proj_rope_mxfp8", "bound": "hbm", "achieved": round(rope_gbs, 1),
-                     "peak": HBM_GBS, "unit": "GB/s", "frac": round(rope_gbs / HBM_GBS, 4), "traffic": None,
+                     "peak": HBM_GBS, "unit": "GB/s", "frac": round(rope_gbs / HBM_GBS, 4),
+                     "traffic": read_traffic(W.WORKLOADS[5]["name"], False, "proj"),
                      "algorithmic_bytes": rope_bytes},
     }
+    if args.copy_probe:
+        copy_probe()
     if not args.no_cpu_baseline:
         import oracle
         yh = Y.cpu().numpy()
