@@ -258,7 +258,8 @@ def cpu_baseline(p, target_s=12.0):
         "cores": cores,
         "kind": "oracle",
         "sample": (f"oracle.gemm_rows (fp64 decode + SF-atom expansion + C and sum|a||b| GEMMs via numpy BLAS) "
-                   f"on {done_rows} sampled rows of batch 0 ({done_rows}x{p['N']}x{p['K']}), {t_total:.1f} s; "
+                   f"on batch 0 rows drawn in doubling sets of distinct rows (64, 128, ... up to M; a row can recur "
+                   f"between sets), {done_rows} rows x {p['N']} x {p['K']} in all, {t_total:.1f} s; "
                    f"value counts the 2*rows*N*K flops of C only"),
     }
 
