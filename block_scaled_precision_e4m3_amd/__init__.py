@@ -205,6 +205,8 @@ def _as_lrk(t, name, stream=None):
     if mmajor.is_contiguous() and t.dtype in (torch.float8_e4m3fn, torch.float8_e5m2):
         dst = torch.empty((l, rows, k), dtype=t.dtype, device=t.device)
         codes_to_kmajor(mmajor, dst, rows, k, l, stream)
+        if isinstance(stream, torch.cuda.Stream):
+            dst.record_stream(stream)  # the copy is read on `stream`, not only on the current one
         return dst, rows, k, l
     raise MxgemmValueError(MXG_ERR_ALIGN, f"{name} must be k-major (strides (K, 1, rows*K)) or, for FP8 codes, "
                                           f"m-major (strides (1, rows, rows*K)), batch outermost")
