@@ -19,7 +19,7 @@ def lib():
     return lib
 
 
-@pytest.mark.parametrize("flags", [0, 4, 8, 32, 64, 2, 1])
+@pytest.mark.parametrize("flags", [0, 4, 8, 32, 64, 2, 1, 128, 128 | 1])
 def test_plan_matches_direct_call(lib, flags):
     M, N, K, L, sf = 300, 520, 256, 2, 16
     p = W.make_problem(M, N, K, L, sf, E5, E4, seed=21)
