@@ -519,12 +519,18 @@ int mxgemm_proj_rope_mxfp8(const float* Y, const uint16_t* cos_bf16, const uint1
   p.D = (int)head_dim;
   p.QR = (int)qk_rope;
   p.num_tiles = (int)((tokens / 32) * num_heads);
-  // runs of 4 heads (4 * head_dim bytes of a token's codes, whole lines for a
-  // head_dim of 32 * odd) where that still gives 16 workgroups per CU
-  p.per_wg = p.num_tiles >= 64LL * cus ? 4 : 1;
+  // runs of consecutive heads per workgroup (a run never crosses a block of
+  // 32 tokens: its length divides num_heads), as long as that still leaves
+  // 8 workgroups per CU
+  p.per_wg = 1;
+  for (int run : {16, 4})
+    if (p.H % run == 0 && p.num_tiles >= 8LL * run * cus) {
+      p.per_wg = run;
+      break;
+    }
   const int64_t grid = cdiv(p.num_tiles, p.per_wg);
   hipLaunchKernelGGL(mxg::rope::proj_rope_mxfp8_kernel, dim3((unsigned)grid), dim3(mxg::rope::kThreads),
-                     (unsigned)mxg::rope::lds_bytes(p.D, p.QR), (hipStream_t)stream, p);
+                     (unsigned)mxg::rope::lds_bytes(p.D, p.QR, p.per_wg), (hipStream_t)stream, p);
   return hipGetLastError() == hipSuccess ? MXG_OK : MXG_ERR_LAUNCH;
 }
 

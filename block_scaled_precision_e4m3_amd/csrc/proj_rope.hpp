@@ -8,7 +8,7 @@
 //       out[i]     = a_i * cos[i]     - b_i * sin[i]
 //       out[R + i] = b_i * cos[R + i] + a_i * sin[R + i]
 //   (bf16 cos / sin rows of the token; float32 products and sum, each
-//   rounded on its own, no fused multiply-add);
+//   rounded on its own: no fused multiply-add);
 //   MXFP8 (E4M3 codes, one E8M0 scale per 32 values) along D (row codes
 //   (tokens, H, D), scales (tokens, H, D/32)) and along tokens (column codes
 //   (tokens, H, D), scales (tokens/32, H, D)), with the scale rule of the MX
@@ -27,7 +27,9 @@
 // values: the row block's maximum comes from the 8 threads of the block
 // (consecutive lanes, xor shuffles), the column exponents from LDS; each
 // direction's 4 codes leave as one dword store, consecutive threads writing
-// consecutive dwords of a token's row.
+// consecutive dwords of a token's row.  Row scale bytes collect in LDS over
+// the workgroup's run of heads and leave at its end, a token's bytes for the
+// whole run contiguous (scattered single bytes cost about 15% of the time).
 #pragma once
 
 #include "mx_quantize.hpp"
@@ -54,7 +56,9 @@ struct RParams {
 
 // bytes of dynamic LDS for head size D and rotary width QR (34 KB for 192 / 64:
 // four workgroups per CU)
-inline size_t lds_bytes(int D, int QR) { return (size_t)32 * (D + 4) * 4 + (size_t)D * 4 + (size_t)64 * QR * 2; }
+inline size_t lds_bytes(int D, int QR, int per_wg) {
+  return (size_t)32 * (D + 4) * 4 + (size_t)D * 4 + (size_t)64 * QR * 2 + (size_t)32 * per_wg * (D / 32);
+}
 
 __device__ __forceinline__ float bf16_bits_to_float(uint16_t b) { return __uint_as_float((unsigned)b << 16); }
 
@@ -67,6 +71,7 @@ __global__ __launch_bounds__(kThreads) void proj_rope_mxfp8_kernel(RParams p) {
   int* ecol = reinterpret_cast<int*>(z + 32 * (p.D + 4));
   uint16_t* csl = reinterpret_cast<uint16_t*>(ecol + p.D);
   uint16_t* snl = csl + 32 * p.QR;
+  uint8_t* rsl = reinterpret_cast<uint8_t*>(snl + 32 * p.QR);  // the run's row scale bytes, (32, per_wg * nb)
   const int t = threadIdx.x;
   const int D = p.D, P = p.D + 4, HD = p.H * p.D;
   const int nope = p.D - p.QR, R = p.QR / 2, nb = p.D / 32;
@@ -76,6 +81,7 @@ __global__ __launch_bounds__(kThreads) void proj_rope_mxfp8_kernel(RParams p) {
   // (a head's row is D bytes) instead of sharing them with workgroups on
   // other XCDs
   const int a0 = blockIdx.x * p.per_wg, a1 = min(a0 + p.per_wg, p.num_tiles);
+  const int run_bytes = (a1 - a0) * nb;  // a token's row scale bytes over the run (per_wg divides H)
   for (int a = a0; a < a1; ++a) {
     const int h = a % p.H, tb = a / p.H;
     const int64_t row0 = (int64_t)tb * 32;
@@ -104,13 +110,21 @@ __global__ __launch_bounds__(kThreads) void proj_rope_mxfp8_kernel(RParams p) {
     __syncthreads();
     // RoPE: each thread rotates its own pairs (i, R + i) in place
     for (int f = t; f < 32 * R; f += kThreads) {
+      // each product and the sum rounded on its own: a fused multiply-add
+      // (which the compiler forms by default, also from __fmul_rn /
+      // __fsub_rn, whose own operations carry the contraction flag) rounds
+      // a*c - b*s once, and under cancellation that moves the value and can
+      // flip a code.  Plain operators here, in a scope where contraction is
+      // off.
+#pragma clang fp contract(off)
       const int r = f / R, i = f - r * R;
       float* zr = z + r * P + nope;
       const float av = zr[i], bv = zr[R + i];
       const float c1 = bf16_bits_to_float(csl[r * p.QR + i]), s1 = bf16_bits_to_float(snl[r * p.QR + i]);
       const float c2 = bf16_bits_to_float(csl[r * p.QR + R + i]), s2 = bf16_bits_to_float(snl[r * p.QR + R + i]);
-      zr[i] = __fsub_rn(__fmul_rn(av, c1), __fmul_rn(bv, s1));
-      zr[R + i] = __fadd_rn(__fmul_rn(bv, c2), __fmul_rn(av, s2));
+      const float ac = av * c1, bs = bv * s1, bc = bv * c2, as = av * s2;
+      zr[i] = ac - bs;
+      zr[R + i] = bc + as;
     }
     __syncthreads();
     // column blocks: the exponent of feature d over the 32 tokens
@@ -137,10 +151,21 @@ __global__ __launch_bounds__(kThreads) void proj_rope_mxfp8_kernel(RParams p) {
       const int64_t o = ((row0 + r) * p.H + h) * (int64_t)D + 4 * c;
       *reinterpret_cast<unsigned*>(p.row_codes + o) =
           quant::codes4<0>(ldexpf(v.x, -e), ldexpf(v.y, -e), ldexpf(v.z, -e), ldexpf(v.w, -e));
-      if ((c & 7) == 0) p.row_scales[((row0 + r) * p.H + h) * nb + (c >> 3)] = (uint8_t)(e + 127);
+      if ((c & 7) == 0) rsl[r * run_bytes + (a - a0) * nb + (c >> 3)] = (uint8_t)(e + 127);
       *reinterpret_cast<unsigned*>(p.col_codes + o) =
           quant::codes4<0>(ldexpf(v.x, -ecol[4 * c]), ldexpf(v.y, -ecol[4 * c + 1]), ldexpf(v.z, -ecol[4 * c + 2]),
                            ldexpf(v.w, -ecol[4 * c + 3]));
+    }
+  }
+  // the run's row scales: per token, run_bytes contiguous bytes (heads h0 ..)
+  // in one coalesced pass instead of a scattered byte per row block
+  if (a0 < a1) {
+    __syncthreads();
+    const int h0 = a0 % p.H;
+    const int64_t row0 = (int64_t)(a0 / p.H) * 32;
+    for (int f = t; f < 32 * run_bytes; f += kThreads) {
+      const int r = f / run_bytes, b = f - r * run_bytes;
+      p.row_scales[((row0 + r) * p.H + h0) * nb + b] = rsl[f];
     }
   }
 }

@@ -106,3 +106,26 @@ def test_projection_end_to_end(lib):
         bound = 2.0 ** -3 * np.abs(z) + np.exp2(e_full - 9.0) + 2e-5 * sb + 2.0 ** -22 * np.abs(z) + 1e-30
         worst = float(np.max(np.abs(deq - z) / bound))
         assert worst <= 1.0, f"axis {axis}: max |deq - z| / bound = {worst}"
+
+
+@pytest.mark.parametrize("tokens", [2048, 8192])   # runs of 4 and of 16 heads per workgroup on 256 CUs
+def test_rope_quantise_large_sampled_blocks(lib, tokens):
+    heads, d, qr = 128, 192, 64
+    print(f"proj rope {tokens} tokens, sampled token blocks", flush=True)
+    rng = np.random.default_rng(tokens)
+    y = rng.standard_normal((tokens, heads * d), dtype=np.float32)
+    y *= np.exp2(rng.integers(-8, 9, size=(tokens, 1))).astype(np.float32)
+    cs = torch.from_numpy(rng.uniform(-1, 1, size=(tokens, qr)).astype(np.float32)).to(torch.bfloat16)
+    sn = torch.from_numpy(rng.uniform(-1, 1, size=(tokens, qr)).astype(np.float32)).to(torch.bfloat16)
+    dev = torch.device("cuda:0")
+    out = lib.proj_rope_mxfp8(torch.from_numpy(y).to(dev), cs.to(dev), sn.to(dev), heads, d, qr)
+    torch.cuda.synchronize()
+    got = [o.view(torch.uint8).cpu().numpy() for o in out]
+    cf, sf = cs.float().numpy(), sn.float().numpy()
+    for tb in (0, 1, tokens // 64, tokens // 32 - 1):   # blocks of 32 tokens are independent
+        s = slice(32 * tb, 32 * tb + 32)
+        ref = oracle.proj_rope_mxfp8(y[s], cf[s], sf[s], heads, d, qr)
+        assert np.array_equal(got[0][s], ref[0]), f"row codes, block {tb}"
+        assert np.array_equal(got[1][s], ref[1]), f"row scales, block {tb}"
+        assert np.array_equal(got[2][s], ref[2]), f"col codes, block {tb}"
+        assert np.array_equal(got[3][tb:tb + 1], ref[3]), f"col scales, block {tb}"

@@ -70,6 +70,26 @@ def test_quantize_special_values(lib, fmt):
     check(lib, x, 16, fmt)
 
 
+@pytest.mark.parametrize("fmt", [E4, E5])
+def test_quantize_exact_ties_every_code(lib, fmt):
+    # every midpoint between neighbouring codes, subnormal ones included, both signs, in blocks
+    # whose scale is 1 (each block holds FMAX): round-to-nearest-even picks the even code
+    fmax = 448.0 if fmt == E4 else 57344.0
+    vals = oracle.decode(np.arange(256, dtype=np.uint8), fmt)
+    fin = np.unique(np.abs(vals[np.isfinite(vals)]))
+    mids = ((fin[:-1] + fin[1:]) / 2).astype(np.float32)
+    xs = np.concatenate([mids, -mids])
+    per = 31                                             # 31 values plus FMAX in each block of 32
+    nblk = -(-len(xs) // per)
+    x = np.zeros((1, 128, 32 * (-(-nblk // 128))), dtype=np.float32)
+    for b in range(nblk):
+        row, col = b % 128, 32 * (b // 128)
+        chunk = xs[b * per:(b + 1) * per]
+        x[0, row, col] = fmax
+        x[0, row, col + 1:col + 1 + len(chunk)] = chunk
+    check(lib, x, 32, fmt)
+
+
 @pytest.mark.parametrize("which", ["A", "B"])
 def test_quantize_workload_shape_sampled(lib, which):
     # the projection workload's operand shapes at full size, with its value
