@@ -80,7 +80,13 @@ __global__ __launch_bounds__(kThreads) void proj_rope_mxfp8_kernel(RParams p) {
   // block, so that a workgroup writes whole 128-byte lines of the code rows
   // (a head's row is D bytes) instead of sharing them with workgroups on
   // other XCDs
-  const int a0 = blockIdx.x * p.per_wg, a1 = min(a0 + p.per_wg, p.num_tiles);
+  // workgroups go round-robin over the 8 XCDs; with the grid a multiple of 8
+  // the runs are renumbered so that consecutive runs (the heads of one token
+  // block, which share the 128-byte lines of its row scales) run on one XCD
+  // and meet in one L2
+  const int G = (int)gridDim.x, b = (int)blockIdx.x;
+  const int w = (G & 7) == 0 ? (b & 7) * (G >> 3) + (b >> 3) : b;
+  const int a0 = w * p.per_wg, a1 = min(a0 + p.per_wg, p.num_tiles);
   const int run_bytes = (a1 - a0) * nb;  // a token's row scale bytes over the run (per_wg divides H)
   for (int a = a0; a < a1; ++a) {
     const int h = a % p.H, tb = a / p.H;
