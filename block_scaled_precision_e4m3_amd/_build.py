@@ -11,16 +11,19 @@ import sys
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
-SOURCES = [os.path.join(CSRC, "mxgemm.hip")]
-HEADERS = [os.path.join(CSRC, "mxgemm_kernel.hpp"), os.path.join(ROOT, "include", "mxgemm.h")]
+# One translation unit per group of kernel instantiations, compiled in parallel,
+# then linked into one shared library (no relocatable device code: every unit
+# carries its own kernels).
+SOURCES = [os.path.join(CSRC, f) for f in ("mxgemm.hip", "launch_big_bf16_f32.hip", "launch_big_bf16_c16.hip",
+                                           "launch_big_fp8.hip", "launch_small.hip")]
 LIB = os.path.join(PKG_DIR, "libmxgemm.so")
+OBJ_DIR = os.path.join(PKG_DIR, "_build")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     # no packed-fp32 instructions in generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result",
@@ -34,15 +37,32 @@ def hipcc():
     return exe
 
 
-def build(verbose=False, extra_flags=()):
-    """Compile libmxgemm.so (always recompiles). Returns the library path."""
+def build(verbose=False, extra_flags=(), jobs=None):
+    """Compile libmxgemm.so (always recompiles every unit). Returns the library path."""
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    cc = hipcc()
+    objs, procs = [], []
+    for src in SOURCES:
+        obj = os.path.join(OBJ_DIR, os.path.basename(src).replace(".hip", ".o"))
+        cmd = [cc, *HIPCC_FLAGS, *extra_flags, "-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        objs.append(obj)
+        procs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True))
+    errors = []
+    for src, proc in zip(SOURCES, procs):
+        out, _ = proc.communicate()
+        if proc.returncode != 0:
+            errors.append(f"{os.path.basename(src)}:\n{out}")
+    if errors:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(errors))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, *SOURCES, "-o", tmp]
+    cmd = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
+        raise RuntimeError("hipcc link failed:\n" + res.stdout + res.stderr)
     os.replace(tmp, LIB)
     return LIB
 

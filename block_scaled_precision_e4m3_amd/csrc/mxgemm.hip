@@ -15,8 +15,16 @@
 #include "sf_repack.hpp"
 #include "codes_transpose.hpp"
 #include "proj_rope.hpp"
-#include "mxgemm_big.hpp"
-#include "mxgemm_kernel.hpp"
+#include "gemm_launch.hpp"
+
+namespace mxg {
+
+// Clears the Amax bits (queued before a GEMM that does not accumulate).
+__global__ void amax_reset_kernel(unsigned* amax_bits) {
+  if (threadIdx.x == 0) *amax_bits = 0u;
+}
+
+}  // namespace mxg
 
 namespace {
 
@@ -117,35 +125,6 @@ Config choose(int64_t M, int64_t N, int64_t K, int64_t L, int cus) {
   return kSmall;
 }
 
-template <int MODE, int KIND, int CT>
-hipError_t launch_mode(const mxg::Params& p, int sf, int fa, int fb, int64_t grid, hipStream_t s) {
-  const dim3 g((unsigned)grid), b(KIND ? mxg::big::kThreads : mxg::kThreads);
-#define MXG_LAUNCH(SF, FA, FB)                                                                         \
-  do {                                                                                                 \
-    if constexpr (KIND == 1)                                                                           \
-      hipLaunchKernelGGL((mxg::big::mxgemm_amax_big_kernel<SF, FA, FB, MODE, CT>), g, b, 0, s, p);     \
-    else                                                                                               \
-      hipLaunchKernelGGL((mxg::mxgemm_amax_kernel<SF, FA, FB, MODE, CT>), g, b, 0, s, p);              \
-  } while (0)
-  if (fa == MXG_FMT_E2M1) {
-    // packed FP4: 256x256 kernel, bf16 datapath, sf = 32 (validated on the host)
-    if constexpr (KIND == 1 && MODE == mxg::kModeBf16) MXG_LAUNCH(32, 2, 2);
-    else return hipErrorInvalidValue;
-  } else if (sf == 32) {
-    if (fa == 0 && fb == 0) MXG_LAUNCH(32, 0, 0);
-    else if (fa == 0 && fb == 1) MXG_LAUNCH(32, 0, 1);
-    else if (fa == 1 && fb == 0) MXG_LAUNCH(32, 1, 0);
-    else MXG_LAUNCH(32, 1, 1);
-  } else {
-    if (fa == 0 && fb == 0) MXG_LAUNCH(16, 0, 0);
-    else if (fa == 0 && fb == 1) MXG_LAUNCH(16, 0, 1);
-    else if (fa == 1 && fb == 0) MXG_LAUNCH(16, 1, 0);
-    else MXG_LAUNCH(16, 1, 1);
-  }
-#undef MXG_LAUNCH
-  return hipGetLastError();
-}
-
 int64_t grid_for(int64_t tiles, int cus, int occ) {
   int64_t g = (int64_t)cus * occ;
   if (tiles < g) g = tiles;
@@ -233,6 +212,9 @@ int prepare(Prepared* pr, int64_t M, int64_t N, int64_t K, int64_t L, int sf_vec
   if (c_flags && (flags & MXG_FLAG_FP8_MFMA)) return MXG_ERR_FLAGS;  // 16-bit C: bf16 datapath only
   if (a_fmt == MXG_FMT_E2M1 && (flags & MXG_FLAG_FP8_MFMA)) return MXG_ERR_FLAGS;  // FP4: bf16 datapath
   if (a_fmt == MXG_FMT_E2M1 && K > 0 && (flags & MXG_FLAG_TILE_128)) return MXG_ERR_FLAGS;  // FP4: 256x256
+  // m-major C: rows of C run along M, so M takes N's place in the 32-bit
+  // per-tile store offsets (256 rows * M * 4 bytes)
+  if (c_mmajor && M > (1LL << 22) - 4) return MXG_ERR_SHAPE;
   if (c_mmajor && M % 4 != 0) return MXG_ERR_ALIGN;  // 16-byte runs along M
   memset(pr, 0, sizeof(*pr));
   pr->magic = kPlanMagic;
@@ -297,18 +279,13 @@ int launch_prepared(const Prepared& pr, const void* A, const void* B, const uint
   const int64_t grid = pr.grid;
   hipError_t e;
   if (pr.kind == 1) {
-    if (pr.fp8) e = launch_mode<mxg::kModeFp8, 1, 0>(p, sf, fa, fb, grid, s);
-    else if (pr.ct == 3) e = launch_mode<mxg::kModeBf16, 1, 3>(p, sf, fa, fb, grid, s);
-    else if (pr.ct == 1) e = launch_mode<mxg::kModeBf16, 1, 1>(p, sf, fa, fb, grid, s);
-    else if (pr.ct == 2) e = launch_mode<mxg::kModeBf16, 1, 2>(p, sf, fa, fb, grid, s);
-    else e = launch_mode<mxg::kModeBf16, 1, 0>(p, sf, fa, fb, grid, s);
+    if (pr.fp8) e = mxg::launch_big_fp8(p, sf, fa, fb, grid, s);
+    else if (pr.ct == 1 || pr.ct == 2) e = mxg::launch_big_bf16_c16(p, sf, fa, fb, pr.ct, grid, s);
+    else e = mxg::launch_big_bf16_f32(p, sf, fa, fb, pr.ct, grid, s);
   } else {
-    if (pr.fp8) e = launch_mode<mxg::kModeFp8, 0, 0>(p, sf, fa, fb, grid, s);
-    else if (pr.ct == 1) e = launch_mode<mxg::kModeBf16, 0, 1>(p, sf, fa, fb, grid, s);
-    else if (pr.ct == 2) e = launch_mode<mxg::kModeBf16, 0, 2>(p, sf, fa, fb, grid, s);
-    // float32 C; an m-major C gets here only with K == 0, where C is all zeros
-    // and the layouts hold the same bytes
-    else e = launch_mode<mxg::kModeBf16, 0, 0>(p, sf, fa, fb, grid, s);
+    // float32 C for ct 0; an m-major C gets here only with K == 0, where C is
+    // all zeros and the layouts hold the same bytes
+    e = mxg::launch_small(p, pr.fp8 ? 1 : 0, sf, fa, fb, pr.ct == 3 ? 0 : pr.ct, grid, s);
   }
   return e == hipSuccess ? MXG_OK : MXG_ERR_LAUNCH;
 }

@@ -108,12 +108,23 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, un
 // inserts "s_waitcnt vmcnt(0)" before those reads, which drains the whole
 // prefetch ring every step.  Ordering is kept by explicit per-wave vmcnt
 // waits instead.
+//
+// Wait states.  A vector-memory instruction that reads an SGPR written by a
+// VALU instruction (here v_readfirstlane, which forces the buffer resource
+// and the LDS address into SGPRs) must come at least 5 wait states after it;
+// the hardware does not interlock that dependence.  The compiler's hazard
+// pass does not look inside inline assembly for it, so the 5 wait states
+// are part of the assembly itself: s_mov to m0 (1) and s_nop 3 (4), which
+// also covers the one wait state between writing m0 and the LDS DMA that
+// reads it.  With fewer, whether the load sees the new or the stale
+// resource depends on how the wave's instructions happen to be issued, so a
+// DMA can fetch rows of the wrong operand or tile now and then.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, unsigned voff, const uint8_t* lds_dst) {
   const unsigned m0 = __builtin_amdgcn_readfirstlane(
       (unsigned)(size_t)(__attribute__((address_space(3))) const uint8_t*)lds_dst);
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs),
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 3\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs),
                "s"(m0)
                : "memory", "m0");
 }
@@ -121,7 +132,7 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, unsigned voff, 
 // The same with the LDS destination given as a 32-bit LDS address (m0 value).
 __device__ __forceinline__ void dma16_at(__amdgpu_buffer_rsrc_t rs, unsigned voff, unsigned lds_addr) {
   const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_addr);
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs),
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 3\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs),
                "s"(m0)
                : "memory", "m0");
 }
@@ -139,12 +150,25 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// Workgroup barrier without a memory fence.  __syncthreads() also waits for
-// every outstanding vector-memory operation, which would drain the DMA ring
-// and the C stores; here each wave has already waited for the DMA it needs,
-// and every LDS read of a stage is consumed by an MFMA before the wave
-// reaches the next barrier.
-__device__ __forceinline__ void barrier() { __builtin_amdgcn_s_barrier(); }
+// Workgroup barrier that does not wait for vector memory.  __syncthreads()
+// also waits for every outstanding vector-memory operation, which would drain
+// the DMA ring and the C stores; here each wave has already waited for the
+// DMA it needs.  What the barrier does enforce:
+//  * every LDS read this wave issued before it has returned (lgkmcnt(0)), so
+//    a DMA that another wave queues into that stage after the barrier cannot
+//    overwrite data this wave has yet to read.  The compiler places its own
+//    lgkmcnt waits just before the first use of a read, and an MFMA or
+//    conversion that uses it may be scheduled past s_barrier (the barrier
+//    orders memory instructions only);
+//  * no memory access is moved across it by the compiler (the empty asm
+//    statements clobber memory; s_barrier alone is not a memory operation
+//    to the optimiser).
+__device__ __forceinline__ void barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left alone
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // E8M0 scale bytes as the f32 scale operand of the scaled conversions
 // v_cvt_scalef32_pk_bf16_{fp8,bf8}.  Those instructions read only the
@@ -224,11 +248,6 @@ __device__ __forceinline__ v8bf cvt8_fp4(unsigned w, float scale) {
   u[2] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
   u[3] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
   return __builtin_bit_cast(v8bf, u);
-}
-
-// Clears the Amax bits (queued before a GEMM that does not accumulate).
-__global__ void amax_reset_kernel(unsigned* amax_bits) {
-  if (threadIdx.x == 0) *amax_bits = 0u;
 }
 
 }  // namespace mxg

@@ -156,13 +156,22 @@ int mxgemm_amax(const void* A, const void* B, const uint8_t* SFA, const uint8_t*
  * max-reduces into the existing Amax (queues the GEMM kernel only);
  * MXG_FLAG_FP8_MFMA selects the reduced-precision FP8 matrix path;
  * MXG_FLAG_TILE_128 / _256 force a tile configuration; MXG_FLAG_C_BF16 /
- * _F16 store a 16-bit C; MXG_FLAG_C_MMAJOR stores C m-major.  Returns
- * MXG_ERR_FLAGS for unknown bits, more than one tile flag, both C flags, a C
- * flag with MXG_FLAG_FP8_MFMA, or MXG_FLAG_C_MMAJOR with a flag it excludes.
+ * _F16 store a 16-bit C; MXG_FLAG_C_MMAJOR stores C m-major, (L, N, M)
+ * float32 with M contiguous, which needs M % 4 == 0 (MXG_ERR_ALIGN) and
+ * M < 2^22 (MXG_ERR_SHAPE; M takes N's place in the per-tile offsets).
+ * Returns MXG_ERR_FLAGS for unknown bits, more than one tile flag, both C
+ * flags, a C flag with MXG_FLAG_FP8_MFMA, or MXG_FLAG_C_MMAJOR with a flag it
+ * excludes.
  *
- * Exactness of the default path: every dequantised element is exact when
- * its scale byte lies in 3..246 (E4M3) or 10..239 (E5M2), i.e. when the
- * value fits bf16; products are exact and sums round as fp32 additions.
+ * Accuracy of the default path.  Every dequantised element is exact when its
+ * value fits bf16: for every code when the scale byte lies in 3..246 (E4M3)
+ * or 10..239 (E5M2); outside those bytes, codes whose value still fits bf16
+ * stay exact and the others round to bf16.  Products are exact; the K sum is
+ * an fp32 accumulation, one rounded add per 16 K, so its error grows with K:
+ * at most about (K/16 + 1) * 2^-24 * S, S = sum_k |A_hat||B_hat|, reached
+ * only when all products share a sign; mixed signs grow like sqrt(K).  The
+ * bound is within 1e-5 * S for K <= 2048 whatever the data; beyond that,
+ * same-sign data can exceed it (measured ratios are in the GPU tests).
  */
 int mxgemm_amax_ex(const void* A, const void* B, const uint8_t* SFA, const uint8_t* SFB,
                    float* C, float* Amax, int64_t M, int64_t N, int64_t K, int64_t L,
@@ -279,7 +288,6 @@ int mxgemm_mx_quantize(const float* X, void* Q, uint8_t* SF, int64_t MN, int64_t
 int mxgemm_sf_rowwise_to_atoms(const uint8_t* rowwise, uint8_t* SF, int64_t MN, int64_t K, int64_t L,
                                int sf_vec_size, void* stream);
 
-/* mxgemm_strerror -- static text for a status code. No HIP call. */
 /*
  * mxgemm_codes_to_kmajor -- m-major (or n-major) 8-bit element codes into the
  * k-major rows mxgemm_amax reads ("GEMM + Amax (SM100)", section
@@ -335,6 +343,7 @@ int mxgemm_proj_rope_mxfp8(const float* Y, const uint16_t* cos_bf16, const uint1
                            uint8_t* row_scales, uint8_t* col_codes, uint8_t* col_scales, int64_t tokens,
                            int64_t num_heads, int64_t head_dim, int64_t qk_rope, void* stream);
 
+/* mxgemm_strerror -- static text for a status code. No HIP call. */
 const char* mxgemm_strerror(int status);
 
 #ifdef __cplusplus

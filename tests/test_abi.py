@@ -98,6 +98,10 @@ def test_errors_before_device_work(lib):
     assert f(*args, *dims, 32, 0, 0, mm | lib.MXG_FLAG_C_F16, None) == lib.MXG_ERR_FLAGS
     assert f(*args, *dims, 32, 0, 0, mm | lib.MXG_FLAG_TILE_128, None) == lib.MXG_ERR_FLAGS
     assert f(*args, 250, 256, 256, 1, 32, 0, 0, mm, None) == lib.MXG_ERR_ALIGN
+    # m-major C rows run along M: M is bounded like N (32-bit per-tile store offsets)
+    assert f(*args, (1 << 22) - 4, 16, 16, 1, 32, 0, 0, mm, None) != lib.MXG_ERR_SHAPE
+    assert f(*args, (1 << 22), 16, 16, 1, 32, 0, 0, mm, None) == lib.MXG_ERR_SHAPE
+    assert f(*args, (1 << 22), 16, 16, 1, 32, 0, 0, 0, None) != lib.MXG_ERR_SHAPE    # n-major C: no such bound
     assert f(*args, *dims, 32, 0, 0, 96, None) == lib.MXG_ERR_FLAGS     # both 16-bit C types
     assert f(*args, *dims, 32, 0, 0, 34, None) == lib.MXG_ERR_FLAGS     # 16-bit C with the FP8 datapath
     assert f(*args, *dims, 32, 0, 0, 16, None) == lib.MXG_ERR_FLAGS   # unknown bit
@@ -191,6 +195,7 @@ def test_plan_validation_before_device_work(lib):
     assert init(plan, 256, 256, 256, 1, 64, 0, 0, 0) == lib.MXG_ERR_SFVEC
     assert init(plan, 256, 256, 256, 1, 32, 0, 0, 96) == lib.MXG_ERR_FLAGS
     assert init(plan, -1, 256, 256, 1, 32, 0, 0, 0) == lib.MXG_ERR_SHAPE
+    assert init(plan, 1 << 22, 16, 16, 1, 32, 0, 0, lib.MXG_FLAG_C_MMAJOR) == lib.MXG_ERR_SHAPE
     # a plan that was never initialised is refused before any device call
     zero = (ctypes.c_uint64 * 32)()
     good = 0x7F0000000000

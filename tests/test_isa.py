@@ -1,0 +1,157 @@
+"""Instruction-level checks of the built library (CPU only: disassembles libmxgemm.so).
+
+The global->LDS DMA is inline assembly, and the compiler's hazard pass does not
+check inline assembly for the gfx9 rule that a vector-memory instruction may
+read an SGPR written by a VALU instruction (v_readfirstlane, v_readlane,
+v_cmp, carry-out adds) only 5 or more wait states later.  Missing wait states
+make the load use a stale buffer resource at random, so the library is checked
+here rather than trusted:
+
+* every LDS DMA is directly preceded by "s_mov_b32 m0, ..." and "s_nop 3" (the
+  5 wait states the DMA macro carries, which hold whatever came before);
+* no buffer or global memory instruction, compiler-made ones included, reads
+  an SGPR that a VALU instruction wrote fewer than 5 wait states before it
+  in straight-line code.
+
+The disassembly is of device code built in this repository from its sources.
+"""
+
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "block_scaled_precision_e4m3_amd", "libmxgemm.so")
+LLVM = "/opt/rocm/llvm/bin"
+
+
+def _tool(name):
+    path = os.path.join(LLVM, name)
+    return path if os.path.exists(path) else shutil.which(name)
+
+
+@pytest.fixture(scope="module")
+def disasm(tmp_path_factory):
+    if not os.path.exists(LIB):
+        pytest.skip("libmxgemm.so is not built")
+    objcopy, bundler, objdump = _tool("llvm-objcopy"), _tool("clang-offload-bundler"), _tool("llvm-objdump")
+    if not (objcopy and bundler and objdump):
+        pytest.skip("LLVM binary tools not found")
+    d = tmp_path_factory.mktemp("isa")
+    fatbin = str(d / "fatbin.bin")
+    subprocess.run([objcopy, "--dump-section", f".hip_fatbin={fatbin}", LIB, str(d / "host.tmp")],
+                   check=True, capture_output=True)
+    # one offload bundle per translation unit, each starting with the bundle magic
+    data = open(fatbin, "rb").read()
+    magic = b"__CLANG_OFFLOAD_BUNDLE__"
+    starts = [i for i in range(0, len(data), 8) if data.startswith(magic, i)]
+    assert starts, "no offload bundle in the library"
+    out = ""
+    for n, (a, b) in enumerate(zip(starts, starts[1:] + [len(data)])):
+        part, code = str(d / f"bundle{n}.bin"), str(d / f"gfx950_{n}.hsaco")
+        with open(part, "wb") as f:
+            f.write(data[a:b])
+        subprocess.run([bundler, "--unbundle", "--type=o", f"--input={part}",
+                        "--targets=hipv4-amdgcn-amd-amdhsa--gfx950", f"--output={code}"],
+                       check=True, capture_output=True)
+        out += subprocess.run([objdump, "-d", "--mcpu=gfx950", "--no-show-raw-insn", code],
+                              check=True, capture_output=True, text=True).stdout
+    insts = []
+    for line in out.split("\n"):
+        text = line.split("//")[0].strip()
+        if not text or text.endswith(":") or text.startswith("Disassembly") or "file format" in text:
+            continue
+        insts.append(text)
+    assert len(insts) > 10000, "unexpectedly small disassembly"
+    return insts
+
+
+def _ops(inst):
+    parts = inst.split(None, 1)
+    return parts[0], ([o.strip() for o in parts[1].split(",")] if len(parts) > 1 else [])
+
+
+def _sgprs(tok):
+    m = re.fullmatch(r"s\[(\d+):(\d+)\]", tok)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.fullmatch(r"s(\d+)", tok)
+    if m:
+        return {int(m.group(1))}
+    if tok in ("vcc", "vcc_lo", "vcc_hi"):
+        return {"vcc"}
+    return set()
+
+
+_CARRY_OUT = ("v_add_co_u32", "v_sub_co_u32", "v_subrev_co_u32", "v_addc_co_u32", "v_subb_co_u32",
+              "v_subbrev_co_u32", "v_div_scale", "v_mad_u64_u32", "v_mad_i64_i32")
+
+
+def _valu_sgpr_defs(mn, ops):
+    if not mn.startswith("v_") or not ops:
+        return set()
+    d = set()
+    if mn.startswith(("v_readfirstlane", "v_readlane", "v_cmp")):
+        d |= _sgprs(ops[0])
+    if mn.startswith(_CARRY_OUT) and len(ops) > 1:
+        d |= _sgprs(ops[1])
+    return d
+
+
+def _wait_states(mn, ops):
+    return int(ops[0], 0) + 1 if mn == "s_nop" else 1
+
+
+def test_lds_dma_carries_its_wait_states(disasm):
+    n = 0
+    for i, inst in enumerate(disasm):
+        if inst.startswith("buffer_load_dwordx4") and inst.endswith(" lds"):
+            n += 1
+            assert disasm[i - 1] == "s_nop 3", f"LDS DMA without its s_nop 3: {disasm[i - 2:i + 1]}"
+            assert disasm[i - 2].startswith("s_mov_b32 m0,"), f"LDS DMA without its m0 write: {disasm[i - 2:i + 1]}"
+    assert n > 1000, f"only {n} LDS DMA instructions found"
+
+
+def _find_hazards(insts):
+    """(VALU def, wait states, VMEM use) for every VMEM read of an SGPR a VALU wrote < 5 wait states before."""
+    bad, checked = [], 0
+    for i, inst in enumerate(insts):
+        mn, ops = _ops(inst)
+        if not mn.startswith(("buffer_", "global_", "tbuffer_")):
+            continue
+        reads = set()
+        for t in ops[1:]:
+            reads |= _sgprs(t)
+        if not reads:
+            continue
+        checked += 1
+        ws, j = 0, i - 1
+        while j >= 0 and ws < 5:
+            mn2, ops2 = _ops(insts[j])
+            if mn2 == "s_endpgm":
+                break
+            if _valu_sgpr_defs(mn2, ops2) & reads:
+                bad.append((insts[j], ws, inst))
+            ws += _wait_states(mn2, ops2)
+            j -= 1
+    return bad, checked
+
+
+def test_hazard_scan_finds_a_planted_hazard():
+    # the pattern of a DMA macro with a single wait state after v_readfirstlane
+    planted = ["v_readfirstlane_b32 s66, v7", "s_mov_b32 m0, s3", "s_nop 0",
+               "buffer_load_dwordx4 v4, s[64:67], 0 offen lds"]
+    bad, checked = _find_hazards(planted)
+    assert checked == 1 and len(bad) == 1 and bad[0][1] == 2
+    fixed = ["v_readfirstlane_b32 s66, v7", "s_mov_b32 m0, s3", "s_nop 3",
+             "buffer_load_dwordx4 v4, s[64:67], 0 offen lds"]
+    assert _find_hazards(fixed)[0] == []
+
+
+def test_no_valu_sgpr_to_vmem_hazard(disasm):
+    bad, checked = _find_hazards(disasm)
+    assert checked > 1000
+    assert not bad, f"{len(bad)} VALU-SGPR -> VMEM hazards, e.g. {bad[:3]}"
