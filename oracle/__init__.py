@@ -33,7 +33,7 @@ from .codecs import (decode, decode_e4m3, decode_e5m2, decode_e8m0, decode_e2m1,
                      bytes_per_row, FMT_E4M3, FMT_E5M2, FMT_E2M1)
 from .sf_atom import sf_physical_shape, sf_logical_shape, sf_logical_view, expand_scales
 from .gemm_amax import (dequantize, gemm_amax, gemm_amax_loops, gemm_rows, gemm_entries,
-                        amax_of)
+                        gemm_row_blocks, amax_of)
 from .mx_quantize import mx_quantize, block_max, block_exponent, encode_rne, place_scales, pack_e2m1
 from .proj_rope import rope, proj_rope_mxfp8
 
@@ -41,7 +41,7 @@ __all__ = [
     "decode", "decode_e4m3", "decode_e5m2", "decode_e8m0", "decode_e2m1", "unpack_e2m1", "element_codes",
     "bytes_per_row", "FMT_E4M3", "FMT_E5M2", "FMT_E2M1",
     "sf_physical_shape", "sf_logical_shape", "sf_logical_view", "expand_scales",
-    "dequantize", "gemm_amax", "gemm_amax_loops", "gemm_rows", "gemm_entries", "amax_of",
+    "dequantize", "gemm_amax", "gemm_amax_loops", "gemm_rows", "gemm_entries", "gemm_row_blocks", "amax_of",
     "mx_quantize", "block_max", "block_exponent", "encode_rne", "place_scales", "pack_e2m1",
     "rope", "proj_rope_mxfp8",
 ]

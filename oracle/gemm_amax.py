@@ -119,3 +119,30 @@ def gemm_entries(a, b, sfa, sfb, m, n, k, l, sf_vec_size, a_fmt, b_fmt, idx_l, i
         c = np.sum(ah * bh, axis=1)
         s = np.sum(np.abs(ah) * np.abs(bh), axis=1)
     return c, s
+
+
+def gemm_row_blocks(a, b, sfa, sfb, m, n, k, l, sf_vec_size, a_fmt, b_fmt, block_rows=1024):
+    """Every output of the full oracle, one block of rows at a time.
+
+    Yields (batch, first_row, C block, S block), blocks of shape (rows, N) in
+    float64, covering all batches and rows in order.  B is dequantised once
+    per batch; each block is the same dequantise-and-contract as gemm_amax on
+    that slice of A, so the full C and S of shapes too large to hold at once
+    can still be checked element by element.
+    """
+    a3 = element_codes(a, a_fmt, m, k, l)
+    b3 = element_codes(b, b_fmt, n, k, l)
+    sa = expand_scales(sfa, m, k, l, sf_vec_size)                        # (L, M, Kb)
+    sb = expand_scales(sfb, n, k, l, sf_vec_size)                        # (L, N, Kb)
+    for batch in range(l):
+        bh = decode(b3[batch], b_fmt) * np.repeat(sb[batch], sf_vec_size, axis=1)[:, :k]
+        bt, abt = np.ascontiguousarray(bh.T), np.ascontiguousarray(np.abs(bh).T)
+        del bh
+        for r0 in range(0, m, block_rows):
+            r1 = min(m, r0 + block_rows)
+            ah = decode(a3[batch, r0:r1], a_fmt) * np.repeat(sa[batch, r0:r1], sf_vec_size, axis=1)[:, :k]
+            with np.errstate(invalid="ignore", over="ignore"):
+                c = ah @ bt
+                s = np.abs(ah) @ abt
+            yield batch, r0, c, s
+

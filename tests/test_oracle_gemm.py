@@ -233,3 +233,37 @@ def test_sampled_forms_match_full():
     ce, se = oracle.gemm_entries(a, b, sfa, sfb, m, n, k, l, sf, E5M2, E4M3, il, im, jn)
     assert np.allclose(ce, c[il, im, jn], rtol=0, atol=1e-12 * s.max())
     assert np.allclose(se, s[il, im, jn], rtol=1e-12)
+
+
+def test_row_blocks_cover_every_output():
+    # tiny: against the plain scalar loops (no matmul); ragged blocks of 3 rows over 2 batches
+    m, n, k, l, sf = 7, 5, 64, 2, 32
+    rng = np.random.default_rng(6)
+    a = finite_codes(rng, (l, m, k), E4M3)
+    b = finite_codes(rng, (l, n, k), E5M2)
+    sfa = random_phys_sf(rng, m, k, l, sf)
+    sfb = random_phys_sf(rng, n, k, l, sf)
+    c_loop, s_loop, _ = oracle.gemm_amax_loops(a, b, sfa, sfb, m, n, k, l, sf, E4M3, E5M2)
+    seen = np.zeros((l, m), dtype=int)
+    for batch, r0, cb, sb in oracle.gemm_row_blocks(a, b, sfa, sfb, m, n, k, l, sf, E4M3, E5M2, block_rows=3):
+        r1 = r0 + cb.shape[0]
+        seen[batch, r0:r1] += 1
+        assert cb.shape == (r1 - r0, n) and sb.shape == cb.shape
+        assert np.all(np.abs(cb - c_loop[batch, r0:r1]) <= k * 2.0 ** -53 * s_loop[batch, r0:r1])
+        assert np.allclose(sb, s_loop[batch, r0:r1], rtol=k * 2.0 ** -53, atol=0)
+    assert np.all(seen == 1), "every row of every batch exactly once"
+    # medium, sf = 16, rows not a multiple of the block: against the full oracle
+    m, n, k, l, sf = 150, 90, 160, 2, 16
+    a = finite_codes(rng, (l, m, k), E5M2)
+    b = finite_codes(rng, (l, n, k), E4M3)
+    sfa = random_phys_sf(rng, m, k, l, sf)
+    sfb = random_phys_sf(rng, n, k, l, sf)
+    c, s, _ = oracle.gemm_amax(a, b, sfa, sfb, m, n, k, l, sf, E5M2, E4M3)
+    got_c = np.full_like(c, np.nan)
+    got_s = np.full_like(s, np.nan)
+    for batch, r0, cb, sb in oracle.gemm_row_blocks(a, b, sfa, sfb, m, n, k, l, sf, E5M2, E4M3, block_rows=64):
+        got_c[batch, r0:r0 + cb.shape[0]] = cb
+        got_s[batch, r0:r0 + cb.shape[0]] = sb
+    assert np.all(np.abs(got_c - c) <= 2 * k * 2.0 ** -53 * s)
+    assert np.allclose(got_s, s, rtol=2 * k * 2.0 ** -53, atol=0)
+
