@@ -514,16 +514,90 @@ def bench_proj(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_probe(args):
+    """One JSON line of hardware ceilings measured on this GPU (include/mxgemm_probe.h): the dense MFMA
+    rate and shader clock with all CUs busy (bf16 32x32x16 and scaled FP8 32x32x64), the global->LDS
+    operand path at the GEMM's per-step block counts, and HBM streaming read and write bandwidth."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import block_scaled_precision_e4m3_amd as lib
+    plib = lib._lib
+    vp, ci, u64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint64
+    plib.mxprobe_mfma.argtypes = [ci, ci, ci, vp, vp]
+    plib.mxprobe_copy_lds.argtypes = [vp, u64, ci, ci, ci, ci, ctypes.c_uint, vp, vp]
+    plib.mxprobe_hbm.argtypes = [ci, vp, u64, ci, vp, vp]
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+    cus = props.multi_processor_count
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def timed(fn, reps=3):
+        fn()
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) * 1e-3
+            best = t if best is None else min(best, t)
+        return best
+
+    out = {"metric": "MI355X ceilings measured by probes", "n_gpus": 1, "device": props.name, "cus": cus}
+    spans = torch.zeros(2 * cus, dtype=torch.int64, device=dev)
+    for kind, name, fl in ((0, "bf16_32x32x16", 32768), (1, "fp8_scaled_32x32x64", 131072)):
+        iters = 20000 if kind == 0 else 10000
+        t = timed(lambda: plib.mxprobe_mfma(kind, cus, iters, spans.data_ptr(), sh))
+        sp = spans.view(cus, 2).cpu().numpy().astype(np.float64)
+        clk = float(np.mean(sp[:, 0] / sp[:, 1])) * 100e6
+        flops = 4.0 * cus * iters * 8 * fl
+        out[f"mfma_{name}"] = {"tflops": round(flops / t / 1e12, 1), "sclk_ghz": round(clk / 1e9, 3),
+                               "tflops_per_ghz": round(flops / t / 1e12 / (clk / 1e9), 1),
+                               "what": f"{cus} workgroups x 4 waves x {iters} x 8 independent MFMAs"}
+    region = 2 << 20
+    src = torch.randint(0, 255, (32 << 20,), dtype=torch.uint8, device=dev)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    steps = 2000
+    for per_step, vgpr, stride in ((16, 0, 0), (16, 1, 0), (8, 0, 0), (16, 0, 1536), (16, 0, 2048), (16, 0, 4096),
+                                   (16, 0, 2176), (8, 0, 2048)):
+        reg = region if stride == 0 else max(region, 64 * 8 * stride)
+        t = timed(lambda: plib.mxprobe_copy_lds(src.data_ptr(), reg, cus, steps, per_step, vgpr, stride,
+                                                 sink.data_ptr(), sh))
+        nbytes = float(cus) * steps * 4 * per_step * 1024
+        key = f"l2_to_{'vgpr' if vgpr else 'lds'}_{per_step}KB_per_wave_step" + (f"_rows_at_{stride}" if stride else "")
+        out[key] = {"GBps": round(nbytes / t / 1e9, 1), "per_cu_bytes_per_ns": round(nbytes / t / 1e9 / cus, 2),
+                    "us_per_step": round(t / steps * 1e6, 3),
+                    "what": f"{cus} workgroups x 4 waves, {per_step} x 1 KB per wave per step "
+                            f"({'contiguous' if not stride else f'8 rows x 128 B, {stride} B apart'}) from a "
+                            f"{reg >> 20} MB region, wait + barrier per step, {steps} steps"}
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    for write in (1, 0):
+        t = timed(lambda: plib.mxprobe_hbm(write, buf.data_ptr(), nbytes, 8 * cus, sink.data_ptr(), sh))
+        out["hbm_write" if write else "hbm_read"] = {"GBps": round(nbytes / t / 1e9, 1),
+                                                     "frac_of_8TBps": round(nbytes / t / 8e12, 3),
+                                                     "what": f"{nbytes >> 30} GiB, 16-byte accesses, "
+                                                             f"{8 * cus} workgroups x 256 threads"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=5)
-    ap.add_argument("--op", choices=["gemm", "quantize", "proj"], default="gemm",
+    ap.add_argument("--op", choices=["gemm", "quantize", "proj", "probe"], default="gemm",
                     help="gemm: the GEMM + amax step (default); quantize: the MX quantisation of the "
                          "workload's float32 operands; proj: the projection pipeline (row-wise scales -> GEMM -> "
-                         "RoPE + dual-direction MXFP8) at the projection workload's shape")
+                         "RoPE + dual-direction MXFP8) at the projection workload's shape; probe: hardware "
+                         "ceilings (MFMA rate and clock, global->LDS path, HBM bandwidth)")
     ap.add_argument("--fp8-mfma", action="store_true", help="time the reduced-precision FP8 MFMA path")
     ap.add_argument("--fp4", action="store_true",
                     help="the workload's shape with packed FP4 (E2M1) operands and sf = 32 (same value recipe)")
@@ -559,6 +633,9 @@ def main():
         return
     if args.op == "proj":
         bench_proj(args)
+        return
+    if args.op == "probe":
+        bench_probe(args)
         return
 
     import torch

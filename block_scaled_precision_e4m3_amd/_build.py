@@ -14,8 +14,9 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 # One translation unit per group of kernel instantiations, compiled in parallel,
 # then linked into one shared library (no relocatable device code: every unit
 # carries its own kernels).
-SOURCES = [os.path.join(CSRC, f) for f in ("mxgemm.hip", "launch_big_bf16_f32.hip", "launch_big_bf16_c16.hip",
-                                           "launch_big_fp8.hip", "launch_small.hip")]
+SOURCES = [os.path.join(CSRC, f) for f in ("mxgemm.hip", "launch_t256_bf16_f32.hip", "launch_t256_bf16_c16.hip",
+                                           "launch_t128_bf16_f32.hip", "launch_t128_bf16_c16.hip",
+                                           "launch_fp8.hip", "probes.hip")]
 LIB = os.path.join(PKG_DIR, "libmxgemm.so")
 OBJ_DIR = os.path.join(PKG_DIR, "_build")
 

@@ -10,14 +10,15 @@
 
 namespace mxg {
 
-// 256x256 kernel, bf16 datapath, float32 C (ct 0: n-major, 3: m-major)
-hipError_t launch_big_bf16_f32(const Params& p, int sf, int fa, int fb, int ct, int64_t grid, hipStream_t s);
-// 256x256 kernel, bf16 datapath, 16-bit C (ct 1: bfloat16, 2: float16)
-hipError_t launch_big_bf16_c16(const Params& p, int sf, int fa, int fb, int ct, int64_t grid, hipStream_t s);
-// 256x256 kernel, scaled-FP8 datapath, float32 C
-hipError_t launch_big_fp8(const Params& p, int sf, int fa, int fb, int64_t grid, hipStream_t s);
-// 128x128 kernel, either datapath (fp8 != 0: scaled FP8), ct 0 / 1 / 2
-hipError_t launch_small(const Params& p, int fp8, int sf, int fa, int fb, int ct, int64_t grid, hipStream_t s);
+// Tile kernel (mxgemm_big.hpp), bf16 datapath, float32 C (ct 0: n-major, 3:
+// m-major), 256x256 or 128x128 tiles
+hipError_t launch_bf16_f32_t256(const Params& p, int sf, int fa, int fb, int ct, int64_t grid, hipStream_t s);
+hipError_t launch_bf16_f32_t128(const Params& p, int sf, int fa, int fb, int ct, int64_t grid, hipStream_t s);
+// the same with a 16-bit C (ct 1: bfloat16, 2: float16)
+hipError_t launch_bf16_c16_t256(const Params& p, int sf, int fa, int fb, int ct, int64_t grid, hipStream_t s);
+hipError_t launch_bf16_c16_t128(const Params& p, int sf, int fa, int fb, int ct, int64_t grid, hipStream_t s);
+// scaled-FP8 datapath, float32 C; bt = 256 or 128
+hipError_t launch_fp8(const Params& p, int sf, int fa, int fb, int bt, int64_t grid, hipStream_t s);
 
 // The format dispatch shared by those launchers: K(SF, FA, FB) names the
 // kernel to launch with hipLaunchKernelGGL(kernel, grid, block, 0, s, p).

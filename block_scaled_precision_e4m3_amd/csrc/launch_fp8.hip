@@ -1,10 +1,10 @@
-// 256x256 kernel instantiations: scaled-FP8 datapath, float32 C.
+// Tile-kernel instantiations of the scaled-FP8 datapath (float32 C), both tile sizes.
 #include "gemm_launch.hpp"
 #include "mxgemm_big.hpp"
 
 namespace mxg {
 
-hipError_t launch_big_fp8(const Params& p, int sf, int fa, int fb, int64_t grid, hipStream_t s) {
+hipError_t launch_fp8(const Params& p, int sf, int fa, int fb, int bt, int64_t grid, hipStream_t s) {
   if (fa == 2) return hipErrorInvalidValue;  // packed FP4 runs on the bf16 datapath only
   const dim3 g((unsigned)grid), b(big::kThreads);
   return dispatch_formats(sf, fa, fb, [&](auto SFc, auto FAc, auto FBc) {
@@ -12,7 +12,10 @@ hipError_t launch_big_fp8(const Params& p, int sf, int fa, int fb, int64_t grid,
     if constexpr (FA == 2) {
       return hipErrorInvalidValue;
     } else {
-      hipLaunchKernelGGL((big::mxgemm_amax_big_kernel<SF, FA, FB, kModeFp8, 0>), g, b, 0, s, p);
+      if (bt == 256)
+        hipLaunchKernelGGL((big::mxgemm_amax_big_kernel<SF, FA, FB, kModeFp8, 0, 256>), g, b, 0, s, p);
+      else
+        hipLaunchKernelGGL((big::mxgemm_amax_big_kernel<SF, FA, FB, kModeFp8, 0, 128>), g, b, 0, s, p);
       return hipGetLastError();
     }
   });

@@ -1,0 +1,19 @@
+// 128x128-tile kernel instantiations: bf16 datapath, bfloat16 or float16 C.
+#include "gemm_launch.hpp"
+#include "mxgemm_big.hpp"
+
+namespace mxg {
+
+hipError_t launch_bf16_c16_t128(const Params& p, int sf, int fa, int fb, int ct, int64_t grid, hipStream_t s) {
+  const dim3 g((unsigned)grid), b(big::kThreads);
+  return dispatch_formats(sf, fa, fb, [&](auto SFc, auto FAc, auto FBc) {
+    constexpr int SF = decltype(SFc)::value, FA = decltype(FAc)::value, FB = decltype(FBc)::value;
+    if (ct == 1)
+      hipLaunchKernelGGL((big::mxgemm_amax_big_kernel<SF, FA, FB, kModeBf16, 1, 128>), g, b, 0, s, p);
+    else
+      hipLaunchKernelGGL((big::mxgemm_amax_big_kernel<SF, FA, FB, kModeBf16, 2, 128>), g, b, 0, s, p);
+    return hipGetLastError();
+  });
+}
+
+}  // namespace mxg

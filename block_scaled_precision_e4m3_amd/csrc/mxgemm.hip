@@ -24,11 +24,19 @@ __global__ void amax_reset_kernel(unsigned* amax_bits) {
   if (threadIdx.x == 0) *amax_bits = 0u;
 }
 
+// C of an empty sum (K == 0): `n8` 8-byte words of zeros (every C type and
+// layout is all-zero bytes), grid-strided.
+__global__ void c_zero_kernel(uint2* c, int64_t n8) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += stride) c[i] = make_uint2(0u, 0u);
+}
+
 }  // namespace mxg
 
 namespace {
 
 constexpr int kMaxDevices = 64;
+
 
 struct DeviceInfo {
   int checked = 0;   // 0 unknown, 1 gfx950, -1 other
@@ -101,28 +109,26 @@ bool on_device(const void* p, int dev) {
   return attr.device == dev;
 }
 
-// Two tile shapes.  128x128: two workgroups per CU, 4 waves of 64x64.
-// 256x256: one workgroup per CU, 4 waves of 128x128; half the L2->LDS bytes
-// per flop of 128x128.  The automatic choice takes 256x256 when its tiles
-// fill the CUs at least as evenly as 128x128 tiles fill two workgroups per CU
-// (and K > 0), otherwise 128x128.
+// Tile shapes, one workgroup of 4 waves per CU either way (mxgemm_big.hpp):
+// 256x256 (waves of 128x128) or 128x128 (waves of 64x64).  A 256x256 tile
+// moves half the L2->LDS bytes per flop and converts half the operand bytes
+// per MFMA, so it runs a tile's worth of flops faster; 128x128 tiles spread a
+// small problem over more CUs.  The choice compares the time of the rounds of
+// tiles the CUs run, a 128x128 tile costing kSmallCost of a 256x256 tile's
+// (which has four times its flops).  kind 3 is the zero fill of K == 0.
 struct Config {
-  int kind;  // 0: 128x128, 1: 256x256
+  int kind;  // 0: 128x128 tiles, 1: 256x256 tiles, 3: K == 0
   int tile_m, tile_n, per_cu;
 };
-constexpr Config kSmall = {0, 128, 128, 2}, kBig = {1, 256, 256, 1};
-
-double fill(int64_t tiles, int64_t slots) {
-  if (tiles <= 0) return 0.0;
-  const int64_t waves = cdiv(tiles, slots);
-  return (double)tiles / (double)(waves * slots);
-}
+constexpr Config kT128 = {0, 128, 128, 1}, kT256 = {1, 256, 256, 1}, kZero = {3, 128, 128, 1};
+constexpr double kSmallCost = 0.35;
 
 Config choose(int64_t M, int64_t N, int64_t K, int64_t L, int cus) {
+  if (K == 0) return kZero;
   const int64_t small = L * cdiv(M, 128) * cdiv(N, 128);
   const int64_t big = L * cdiv(M, 256) * cdiv(N, 256);
-  if (K > 0 && big >= cus && fill(big, cus) >= fill(small, 2 * (int64_t)cus) - 1e-9) return kBig;
-  return kSmall;
+  const double t_big = (double)cdiv(big, cus), t_small = kSmallCost * (double)cdiv(small, cus);
+  return t_big <= t_small ? kT256 : kT128;
 }
 
 int64_t grid_for(int64_t tiles, int cus, int occ) {
@@ -181,16 +187,19 @@ void configure(Prepared* pr, int cus) {
   const int64_t M = p.M, N = p.N, K = p.K, L = p.L;
   const bool fp4 = pr->fa == MXG_FMT_E2M1;
   Config cfg = choose(M, N, K, L, cus);
-  if (pr->flags & MXG_FLAG_TILE_128) cfg = kSmall;
-  if ((pr->flags & MXG_FLAG_TILE_256) && K > 0) cfg = kBig;
-  if (fp4 && K > 0) cfg = kBig;  // packed FP4 runs on the 256x256 kernel only
-  if (pr->ct == 3 && K > 0) cfg = kBig;  // so does an m-major C
+  if (K > 0 && (pr->flags & MXG_FLAG_TILE_128)) cfg = kT128;
+  if (K > 0 && (pr->flags & MXG_FLAG_TILE_256)) cfg = kT256;
   pr->kind = cfg.kind;
   p.tilesM = (int)cdiv(M, cfg.tile_m);
   p.tilesN = (int)cdiv(N, cfg.tile_n);
   p.ksteps = (int)cdiv(K, fp4 ? 256 : 128);  // 128 bytes of every row per step
   p.num_tiles = (int)(L * p.tilesM * p.tilesN);
   pr->grid = grid_for(p.num_tiles, cus, cfg.per_cu);
+  if (cfg.kind == 3) {
+    // zero fill: 8-byte words of C, 256 threads per workgroup, up to 4 workgroups per CU
+    const int64_t words = L * M * N * (pr->ct == 1 || pr->ct == 2 ? 2 : 4) / 8;
+    pr->grid = std::max<int64_t>(1, std::min<int64_t>(cdiv(words, 256), 4LL * cus));
+  }
   p.xcd_remap = (pr->grid % 8 == 0) ? 1 : 0;
 }
 
@@ -204,14 +213,12 @@ int prepare(Prepared* pr, int64_t M, int64_t N, int64_t K, int64_t L, int sf_vec
                           MXG_FLAG_C_BF16 | MXG_FLAG_C_F16 | MXG_FLAG_C_MMAJOR))
     return MXG_ERR_FLAGS;
   const bool c_mmajor = (flags & MXG_FLAG_C_MMAJOR) != 0;
-  // m-major C: the 256x256 kernel's bf16 datapath with a float32 C
+  // m-major C: the bf16 datapath with a float32 C
   if (c_mmajor && (flags & (MXG_FLAG_FP8_MFMA | MXG_FLAG_C_BF16 | MXG_FLAG_C_F16))) return MXG_ERR_FLAGS;
-  if (c_mmajor && K > 0 && (flags & MXG_FLAG_TILE_128)) return MXG_ERR_FLAGS;
   if (tile_flags & (tile_flags - 1)) return MXG_ERR_FLAGS;  // more than one tile flag
   if (c_flags & (c_flags - 1)) return MXG_ERR_FLAGS;        // both 16-bit C types
   if (c_flags && (flags & MXG_FLAG_FP8_MFMA)) return MXG_ERR_FLAGS;  // 16-bit C: bf16 datapath only
   if (a_fmt == MXG_FMT_E2M1 && (flags & MXG_FLAG_FP8_MFMA)) return MXG_ERR_FLAGS;  // FP4: bf16 datapath
-  if (a_fmt == MXG_FMT_E2M1 && K > 0 && (flags & MXG_FLAG_TILE_128)) return MXG_ERR_FLAGS;  // FP4: 256x256
   // m-major C: rows of C run along M, so M takes N's place in the 32-bit
   // per-tile store offsets (256 rows * M * 4 bytes)
   if (c_mmajor && M > (1LL << 22) - 4) return MXG_ERR_SHAPE;
@@ -271,21 +278,21 @@ int launch_prepared(const Prepared& pr, const void* A, const void* B, const uint
   p.SFB = SFB;
   p.C = C;
   p.amax_bits = reinterpret_cast<unsigned*>(Amax);
-  const int sf = pr.sf;
-  // K == 0 never reads A or B, so a packed-FP4 problem then runs the 128x128
-  // kernel instantiated for an 8-bit format
-  const bool fp4_empty = pr.fa == MXG_FMT_E2M1 && pr.kind == 0;
-  const int fa = fp4_empty ? MXG_FMT_E4M3 : pr.fa, fb = fp4_empty ? MXG_FMT_E4M3 : pr.fb;
+  const int sf = pr.sf, fa = pr.fa, fb = pr.fb;
   const int64_t grid = pr.grid;
   hipError_t e;
-  if (pr.kind == 1) {
-    if (pr.fp8) e = mxg::launch_big_fp8(p, sf, fa, fb, grid, s);
-    else if (pr.ct == 1 || pr.ct == 2) e = mxg::launch_big_bf16_c16(p, sf, fa, fb, pr.ct, grid, s);
-    else e = mxg::launch_big_bf16_f32(p, sf, fa, fb, pr.ct, grid, s);
+  if (pr.kind == 3) {
+    const int64_t words = (int64_t)p.L * p.M * p.N * (pr.ct == 1 || pr.ct == 2 ? 2 : 4) / 8;
+    hipLaunchKernelGGL(mxg::c_zero_kernel, dim3((unsigned)grid), dim3(256), 0, s, reinterpret_cast<uint2*>(C), words);
+    e = hipGetLastError();
+  } else if (pr.fp8) {
+    e = mxg::launch_fp8(p, sf, fa, fb, pr.kind == 1 ? 256 : 128, grid, s);
+  } else if (pr.ct == 1 || pr.ct == 2) {
+    e = pr.kind == 1 ? mxg::launch_bf16_c16_t256(p, sf, fa, fb, pr.ct, grid, s)
+                     : mxg::launch_bf16_c16_t128(p, sf, fa, fb, pr.ct, grid, s);
   } else {
-    // float32 C for ct 0; an m-major C gets here only with K == 0, where C is
-    // all zeros and the layouts hold the same bytes
-    e = mxg::launch_small(p, pr.fp8 ? 1 : 0, sf, fa, fb, pr.ct == 3 ? 0 : pr.ct, grid, s);
+    e = pr.kind == 1 ? mxg::launch_bf16_f32_t256(p, sf, fa, fb, pr.ct, grid, s)
+                     : mxg::launch_bf16_f32_t128(p, sf, fa, fb, pr.ct, grid, s);
   }
   return e == hipSuccess ? MXG_OK : MXG_ERR_LAUNCH;
 }

@@ -1,24 +1,42 @@
-// One-workgroup-per-CU variant of the block-scaled FP8 GEMM + amax kernel
-// for gfx950: 256x256 C tiles.
+// Block-scaled FP8 GEMM with a fused global-amax epilogue for gfx950 (CDNA4).
 //
-// Same operation, operand layouts, scale handling and amax as the 128x128
-// kernel in mxgemm_kernel.hpp ("GEMM + Amax (SM100)", sections "Equations"
-// and "Shapes"); what changes is the shape of the work:
+// Computes, per batch l ("GEMM + Amax (SM100)", sections "Equations" and
+// "Shapes"):
+//   C[m,n] = sum_k dec(A[m,k]) 2^(SFA(m,k/sf)-127) * dec(B[n,k]) 2^(SFB(n,k/sf)-127)
+//   Amax   = max |C|
 //
-// * One workgroup per CU (the LDS ring takes 132-136 KB of the 160 KB) owns a
-//   256 x 256 tile; its 4 waves, one per SIMD, each hold a 128 x 128 block in
-//   4 x 4 MFMA accumulators (all 256 matrix-core registers).  Per 128-K step
-//   a CU moves 64 KB of A and B and the scale atoms from L2.
-// * The K loop is one straight block per step: the next chunk's fragment
-//   reads are queued ahead, and each slice's conversions run under the
+// Two datapaths share everything but the innermost step:
+//
+// * bf16 (default).  Each FP8 (or FP4) code is dequantised in registers with
+//   v_cvt_scalef32_pk_bf16_{fp8,bf8,fp4} (code * 2^(byte-127) rounded to
+//   bf16, exact whenever the value is a bf16 number) and fed to
+//   v_mfma_f32_32x32x16_bf16, whose products are exact and whose sums are
+//   fp32 additions.
+// * FP8 (opt-in).  The codes go straight into the scaled MFMA
+//   v_mfma_scale_f32_32x32x64_f8f6f4, which applies the E8M0 scales itself at
+//   twice the bf16 rate but keeps only the bits of each product down to
+//   2^-13 of the largest in its 8-element K group, so terms much smaller
+//   than their neighbours are truncated.
+//
+// Work shape: one workgroup per CU, 4 waves in 2 x 2, on square C tiles of
+// BT x BT (BT = 256: waves of 128 x 128 in 4 x 4 MFMA blocks, all 256
+// matrix-core registers; BT = 128: waves of 64 x 64).  Tiles are taken
+// persistently: workgroup w runs tiles w, w+G, ....
+//
+// * The K loop moves 128 bytes of every operand row per step through an LDS
+//   ring (2 stages for BT = 256, 4 for the bf16 datapath at BT = 128) by
+//   direct global->LDS DMA, the step's E8M0 atoms beside the tile.  Per
+//   128-K step a 256x256 tile moves 64 KB for 8.4 M multiply-adds, a
+//   128x128 tile 32 KB for 2.1 M.
+// * bf16 step: 8 MFMA slices of 16 K; each slice's conversions run under the
 //   previous slice's MFMAs (scheduling-group barriers pin the interleave), so
-//   one wave per SIMD keeps the matrix core fed.
+//   one wave per SIMD keeps the matrix core fed; one barrier per step.
 // * C stores.  A tile's C is stored at its end, transposed through LDS so
 //   that every store writes whole 128-byte lines.  Every CU ends its tiles at
 //   about the same time, so the stores drain slowly; the DMA of the next
-//   tile's second step is issued before those stores, so that the next
-//   tile's first step waits for its DMA only and the stores drain under its
-//   MFMAs (the vector-memory counter retires in issue order).
+//   steps is queued before those stores, so that the next tile's first
+//   steps wait for their DMA only and the stores drain under their MFMAs (the
+//   vector-memory counter retires in issue order).
 //
 // bf16 datapath, per 32-K chunk c of a step: lane (r, h) reads the 16 bytes
 // K [32c + 16h, +16) of its row for each of its A and B fragments; bytes
@@ -27,6 +45,13 @@
 // chunk lies in one K-block for sf=32 (block c) and for sf=16 (block 2c + h).
 // FP8 datapath, per 64-K slice S: bytes 0..15 of a lane are K [16h, +16) and
 // bytes 16..31 are K [32 + 16h, +16) of the slice, as the scaled MFMA needs.
+// MFMA output layout: lane l, element e holds D[8(e/4) + 4h + e%4][r] for
+// (src0 row, src1 col); B is src0 and A src1 (an m-major C swaps them), so
+// a lane owns one C row and 4-element runs along the contiguous dimension.
+//
+// Amax: each lane keeps max(bits(|c|)) over the outputs it stores, as an
+// unsigned integer (the order of non-negative IEEE floats, NaN above +inf),
+// reduced across the wave with xor-shuffles, then one atomic max per wave.
 #pragma once
 
 #include "mxgemm_common.hpp"
@@ -35,19 +60,28 @@ namespace mxg {
 namespace big {
 
 constexpr int kThreads = 256;
-constexpr int kBM = 256, kBN = 256, kBK = 128;
-constexpr int kTM = 4, kTN = 4;  // 32x32 MFMA blocks per wave (128 x 128)
-constexpr int kWN = kBN / 2;     // wave tile columns
+constexpr int kBK = 128;
 
-template <int SF, bool FP4>
+// Square C tiles of BT x BT (256 or 128): 2 x 2 waves, each (BT/2) x (BT/2) in
+// (BT/64) x (BT/64) blocks of 32 x 32.
+template <int SF, bool FP4, int BT, int NST>
 struct Layout {
+  static_assert(BT == 256 || BT == 128, "tile size");
+  static constexpr int kStages = NST;                // LDS ring stages
+  static constexpr int kBM = BT, kBN = BT;
   static constexpr int KE = FP4 ? 256 : 128;         // K elements per step (128 bytes per row)
   static constexpr int NSF = KE / (4 * SF);          // atoms per 128-row group per step
-  static constexpr int kSF = 2 * NSF * 512;          // atom bytes per operand per stage
-  static constexpr int kOffB = kBM * kBK;            // A tile: 256 rows x 128 bytes
-  static constexpr int kOffSFA = kOffB + kBN * kBK;  // B tile: 256 rows x 128 bytes
+  static constexpr int kGroups = BT / 128;           // 128-row atom groups per operand tile
+  // atom bytes per operand per stage: the atoms of both 128-row groups; for
+  // a 128-row tile one kilobyte, which takes the one wave's scale DMA (one
+  // group's NSF atoms, or with NSF = 1 its atom and the zeros its other half
+  // of the wave reads for a group past the tile)
+  static constexpr int kSF = BT == 256 ? 2 * NSF * 512 : 1024;
+  static constexpr int kOffB = kBM * kBK;            // A tile: BT rows x 128 bytes
+  static constexpr int kOffSFA = kOffB + kBN * kBK;  // B tile: BT rows x 128 bytes
   static constexpr int kOffSFB = kOffSFA + kSF;
   static constexpr int kStage = kOffSFB + kSF;
+  static constexpr int kDmaA = kBM / 32;             // A DMA instructions per wave per step
   static constexpr int kDma = (kBM + kBN) / 32;      // A/B DMA instructions per wave per step
   // Per-wave LDS area where the epilogue transposes one 32x32 fp32 block
   // (rows padded to 36 floats) so its stores write whole 128-byte lines.
@@ -59,7 +93,8 @@ struct Layout {
   // so a step stays one branch-free block the scheduler can interleave.  It
   // is apart from the epilogue area because that DMA may still be in flight
   // while the epilogue runs.
-  static constexpr int kOffDummy = 2 * kStage + kEpiBytes;
+  static constexpr int kOffEpi = NST * kStage;
+  static constexpr int kOffDummy = kOffEpi + kEpiBytes;
   static constexpr int kLds = kOffDummy + 2048;
 };
 
@@ -74,13 +109,20 @@ __device__ __forceinline__ unsigned sf_tail(unsigned d, int g, int Kb) {
   return (d & keep) | (0x7F7F7F7Fu & ~keep);
 }
 
-template <int SF, int FA, int FB, int MODE, int CT>
+template <int SF, int FA, int FB, int MODE, int CT, int BT>
 __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) {
   // FA = FB = 2: packed FP4 (E2M1), bf16 datapath, sf = 32 (the host enforces it)
   constexpr bool kFp4 = FA == 2;
   static_assert(!kFp4 || (FB == 2 && SF == 32 && MODE == kModeBf16), "FP4: both operands, sf = 32, bf16 path");
   static_assert(!kCMajorM<CT> || MODE == kModeBf16, "m-major C: bf16 path");
-  using Y = Layout<SF, kFp4>;
+  // LDS ring stages: a 128x128 tile's steps are short, so its bf16 datapath
+  // queues the DMA three steps ahead in four stages; a 256x256 tile's ring
+  // fills the LDS with two
+  constexpr int kStages = (BT == 128 && MODE == kModeBf16) ? 4 : 2;
+  using Y = Layout<SF, kFp4, BT, kStages>;
+  constexpr int kBM = Y::kBM, kBN = Y::kBN;
+  constexpr int kTM = BT / 64, kTN = BT / 64;  // 32x32 MFMA blocks per wave
+  constexpr int kWM = kBM / 2, kWN = kBN / 2;  // wave tile rows and columns
   static_assert(Y::NSF == 1 || Y::NSF == 2, "one or two scale atoms per 128-row group per step");
   constexpr int kEs = kCBytes<CT>;  // bytes per C element
   constexpr int NSF = Y::NSF;
@@ -118,7 +160,7 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
     g.r = ln & 31;
     g.h = ln >> 5;
     g.xr = (ln & 7) ^ ((ln >> 3) & 1);
-    g.a_off = (128 * wm + g.r) * kBK;
+    g.a_off = (kWM * wm + g.r) * kBK;
     g.b_off = Y::kOffB + (kWN * wn + g.r) * kBK;
     const int dma_row = ln >> 3;
     g.row_k = (unsigned)(wave * 8 + dma_row) * (unsigned)p.Kbytes;
@@ -141,13 +183,14 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   // (num_records = valid rows * K) and K chunks past K get an offset of 2^31
   // or more: both read as zero.  A and B rows use the same offsets, only the
   // resources differ.  SF: sf=32 -> waves 0 and 1 load the A and B atoms of
-  // both 128-row groups (lanes 0-31 group 0, 32-63 group 1); sf=16 -> waves
-  // 0,1 (A,B) load row group 0's two atoms, waves 2,3 row group 1's.  Groups
-  // past the matrix read as zero.  With sf=32, waves 2 and 3 issue the same
-  // instruction on an empty resource into their own kilobyte of the dummy
-  // area (no branch in the step).
+  // both 128-row groups (lanes 0-31 group 0, 32-63 group 1); sf=16 (or FP4)
+  // -> waves 0,1 (A,B) load row group 0's two atoms, waves 2,3 row group
+  // 1's (256-row tiles only).  Groups past the matrix or the tile read as
+  // zero.  Waves that load no atoms issue the same instruction on an empty
+  // resource into their own kilobyte of the dummy area (no branch in the
+  // step).
   constexpr unsigned kOob = 0x80000000u;
-  const bool sf_wave = NSF == 2 || wave < 2;
+  const bool sf_wave = (NSF == 2 && BT == 256) || wave < 2;
   const bool sf_is_b = (wave & 1) != 0;
   struct Dma {
     __amdgpu_buffer_rsrc_t ra, rb, rs;
@@ -164,21 +207,23 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
     const int mn0 = sf_is_b ? T.n0 : T.m0;
     const int mnb = sf_is_b ? p.MNbB : p.MNbA;
     const int g0 = mn0 >> 7;
-    const unsigned nrec = ((int)live & (int)sf_wave) ? (unsigned)min(2, mnb - g0) * (unsigned)p.Kg * 512u : 0u;
+    const unsigned nrec =
+        ((int)live & (int)sf_wave) ? (unsigned)min(Y::kGroups, mnb - g0) * (unsigned)p.Kg * 512u : 0u;
     d.rs = make_rsrc((sf_is_b ? p.SFB : p.SFA) + ((int64_t)T.l * mnb + g0) * p.Kg * 512, nrec);
     const int kg = NSF * kt + g.sf_j;
     d.sf_voff = kg < p.Kg ? (unsigned)(g.sf_rg * p.Kg + kg) * 512u + g.sf_lane : kOob;
     d.dst = stage;
     return d;
   };
-  // A/B DMA instruction q of this wave: q < 8 -> A group wave + 4q, else B
-  // group wave + 4(q - 8)
+  // A/B DMA instruction q of this wave: q < kDmaA -> A group wave + 4q, else
+  // B group wave + 4(q - kDmaA)
   const unsigned grp_stride = 32u * (unsigned)p.Kbytes;
   auto dma_ab = [&](const Dma& d, int q) {
-    const int qq = q < 8 ? q : q - 8;
+    const bool qb = q >= Y::kDmaA;
+    const int qq = qb ? q - Y::kDmaA : q;
     const unsigned voff = d.voff + (unsigned)qq * grp_stride;
-    const unsigned dst = d.dst + (q >= 8 ? (unsigned)Y::kOffB : 0u) + (unsigned)(wave + 4 * qq) * 1024u;
-    dma16_at(q >= 8 ? d.rb : d.ra, voff, dst);
+    const unsigned dst = d.dst + (qb ? (unsigned)Y::kOffB : 0u) + (unsigned)(wave + 4 * qq) * 1024u;
+    dma16_at(qb ? d.rb : d.ra, voff, dst);
   };
   // waves 2 and 3 (the only ones that use it) each own a kilobyte
   const unsigned sf_dummy = lds0 + (unsigned)Y::kOffDummy + (unsigned)(wave & 1) * 1024u;
@@ -189,6 +234,8 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   };
 
   v16f acc[kTM][kTN];  // written by each tile's first step before any read
+  constexpr int kNStores = kTM * kTN * 4;  // C store instructions per lane per tile (at least)
+  static_assert(kNStores <= 64, "vmcnt counts to 63");
   const v16f zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   unsigned lmax = 0u;
 
@@ -230,12 +277,12 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   // block b's stores go out (its reads precede those writes), with no barrier.
   auto store_all = [&](const StoreCtx& x) __attribute__((always_inline)) {
     const int ln = lane_opaque();
-    uint8_t* epi = lds + 2 * Y::kStage + wave * (32 * Y::kEpiRow * 4);
+    uint8_t* epi = lds + Y::kOffEpi + wave * (32 * Y::kEpiRow * 4);
     const int wr_off = ((ln & 31) * Y::kEpiRow + 4 * (ln >> 5)) * 4;        // + 32 q bytes
     const int rd_row = ln >> 3, rd_col = 4 * (ln & 7);
     const int rd_off = (rd_row * Y::kEpiRow + rd_col) * 4;                  // + 8 k rows
-    const int row_base = kMM ? kWN * wn : 128 * wm;                          // the wave's first tile row
-    const int col_base = (kMM ? 128 * wm : kWN * wn) + rd_col;               // tile column of the lane's run
+    const int row_base = kMM ? kWN * wn : kWM * wm;                          // the wave's first tile row
+    const int col_base = (kMM ? kWM * wm : kWN * wn) + rd_col;               // tile column of the lane's run
     const unsigned vrow0 =
         ((unsigned)(row_base + rd_row) * (unsigned)x.stride + (unsigned)(x.c0 + col_base)) * (unsigned)kEs;
     auto put = [&](int i, int j) {
@@ -307,7 +354,7 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
     // queued after it); the barrier extends that to every wave and frees the
     // other stage
     if (after_dma == 0) wait_vm<0>();
-    else wait_vm<63>();
+    else wait_vm<kNStores - 1>();
     after_dma = 0;
     barrier();
     const Geo g = geo(lane_opaque());
@@ -319,17 +366,18 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
     const bool last_k = kt + 1 == p.ksteps;
     const Dma d = dma_setup(g, nt, last_k ? 0 : kt + 1, has_next, lds0 + (unsigned)(((s & 1) ^ 1) * Y::kStage));
     dma_sf(d);
-    // SF dwords of this step: NSF atoms x (4 or kTN) fragment rows per operand.
-    // A rows 128*wm + 32i + r: atom group wm, dword i; B rows kWN*wn + 32i + r:
-    // atom group (kWN*wn)/128, dword ((kWN*wn)/32)%4 + i.
+    // SF dwords of this step: NSF atoms x kTM (kTN) fragment rows per operand.
+    // A rows kWM*wm + 32i + r: atom group (kWM*wm)/128, dword
+    // ((kWM*wm)/32)%4 + i; B rows kWN*wn + 32i + r likewise.
     unsigned sa[NSF][kTM], sb[NSF][kTN];
+    const int arg = (kWM * wm) >> 7, adw = ((kWM * wm) >> 5) & 3;
     const int brg = (kWN * wn) >> 7, bdw = ((kWN * wn) >> 5) & 3;
 #pragma unroll
     for (int j = 0; j < NSF; ++j) {
       const int ga = NSF * kt + j;
 #pragma unroll
       for (int i = 0; i < kTM; ++i)
-        sa[j][i] = sf_tail(lds4(st + Y::kOffSFA + (wm * NSF + j) * 512 + 16 * g.r + 4 * i), ga, p.Kb);
+        sa[j][i] = sf_tail(lds4(st + Y::kOffSFA + (arg * NSF + j) * 512 + 16 * g.r + 4 * (adw + i)), ga, p.Kb);
 #pragma unroll
       for (int i = 0; i < kTN; ++i)
         sb[j][i] = sf_tail(lds4(st + Y::kOffSFB + (brg * NSF + j) * 512 + 16 * g.r + 4 * (bdw + i)), ga, p.Kb);
@@ -411,17 +459,18 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   uint4 ra[2][kTM], rb[2][kTN];         // raw 16-byte fragments, by chunk parity
   v8bf ab[2][kTM], bb[2][kTN];          // converted operands, by slice parity
   float fa[kTM], fb[kTN];               // scale operands of the chunk being converted
+  const int arg = (kWM * wm) >> 7, adw = ((kWM * wm) >> 5) & 3;
   const int brg = (kWN * wn) >> 7, bdw = ((kWN * wn) >> 5) & 3;
-  // SF dwords of step kt from stage st: NSF atoms x 4 fragment rows per
-  // operand.  A rows 128*wm + 32i + r: atom group wm, dword i; B rows
-  // kWN*wn + 32i + r: atom group (kWN*wn)/128, dword ((kWN*wn)/32)%4 + i.
+  // SF dwords of step kt from stage st: NSF atoms x kTM (kTN) fragment rows
+  // per operand.  A rows kWM*wm + 32i + r: atom group (kWM*wm)/128, dword
+  // ((kWM*wm)/32)%4 + i; B rows kWN*wn + 32i + r likewise.
   auto load_sf = [&](const Geo& g, const uint8_t* st, int kt) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < NSF; ++j) {
       const int ga = NSF * kt + j;
 #pragma unroll
       for (int i = 0; i < kTM; ++i)
-        sa[j][i] = sf_tail(lds4(st + Y::kOffSFA + (wm * NSF + j) * 512 + 16 * g.r + 4 * i), ga, p.Kb);
+        sa[j][i] = sf_tail(lds4(st + Y::kOffSFA + (arg * NSF + j) * 512 + 16 * g.r + 4 * (adw + i)), ga, p.Kb);
 #pragma unroll
       for (int i = 0; i < kTN; ++i)
         sb[j][i] = sf_tail(lds4(st + Y::kOffSFB + (brg * NSF + j) * 512 + 16 * g.r + 4 * (bdw + i)), ga, p.Kb);
@@ -544,12 +593,15 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
                                                                      (kFirst && n == 0) ? zero16 : acc[i][jj], 0, 0, 0)
                            : __builtin_amdgcn_mfma_f32_32x32x16_bf16(bb[n & 1][jj], ab[n & 1][i],
                                                                      (kFirst && n == 0) ? zero16 : acc[i][jj], 0, 0, 0);
-      // interleave: each MFMA followed by up to 3 VALU ops; the chunk's
-      // fragment reads go out one after each of the first MFMAs
+      // interleave: each MFMA followed by up to kValu VALU ops (3 for 16
+      // MFMAs per slice, 6 for 4: the conversions per MFMA double when the
+      // wave tile halves); the chunk's fragment reads go out one after each
+      // of the first MFMAs
+      constexpr int kValu = BT == 256 ? 3 : 6;
 #pragma unroll
       for (int k = 0; k < kTM * kTN; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);  // VALU
         if (k < kTM + kTN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -557,7 +609,7 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
         // this wave's DMA of step s+1 has landed; on a tile's first step the
         // previous tile's 64 C stores per lane, queued after that DMA, may
         // still be in flight
-        if constexpr (kFirst) wait_vm<63>();
+        if constexpr (kFirst) wait_vm<kNStores - 1>();
         else wait_vm<0>();
         barrier();  // B'
         load_sf(g, stn, nkt);
@@ -571,8 +623,145 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
     ++s;
   };
 
+  // --- bf16 datapath on a ring of kStages > 2 stages (128x128 tiles) ---------
+  // Global step s reads stage s % kStages.  Step s queues, over its slices
+  // 1..3, the DMA of step s + kStages - 1 (the stream runs on across tiles)
+  // into stage (s - 1) % kStages, which every wave finished reading before
+  // B' of step s - 1.  B' of step s waits for this wave's DMA of step s + 1
+  // and leaves the DMAs of the kStages - 2 later steps in flight; on a tile's
+  // first kStages - 2 steps ("hold") the previous tile's C stores may stay in
+  // flight as well, since the DMA waited for went out before that tile's
+  // epilogue.  Past the end of the work the DMAs go through empty resources,
+  // so every step queues the same instructions and the counts hold.
+  constexpr int kDmaPerStep = Y::kDma + 1;
+  int di = 0, dkt = 0;  // the step whose DMA goes out next: the workgroup's tile di, K step dkt
+  Tile dtile = cur;
+  auto next_target = [&]() {
+    const Tgt t = {dtile, dkt, di < my_tiles};
+    if (++dkt == p.ksteps) {
+      dkt = 0;
+      ++di;
+      if (di < my_tiles) dtile = make_tile<kBM, kBN>(p, t0 + di * G);
+    }
+    return t;
+  };
+  auto stage_at = [&](int step) { return (unsigned)(step & (kStages - 1)) * (unsigned)Y::kStage; };
+  // steps 1 .. kStages - 2 join step 0 (queued above) before anything is read
+  auto prime_ring = [&]() __attribute__((always_inline)) {
+    const Geo g = geo(lane_opaque());
+    (void)next_target();  // step 0
+#pragma unroll
+    for (int j = 1; j + 1 < kStages; ++j) {
+      const Tgt tg = next_target();
+      const Dma d = dma_setup(g, tg.t, tg.kt, tg.live, lds0 + stage_at(j));
+      dma_sf(d);
+#pragma unroll
+      for (int q = 0; q < Y::kDma; ++q) dma_ab(d, q);
+    }
+    wait_vm<0>();
+    barrier();
+    load_sf(g, lds, 0);
+    load_raw(g, lds, 0);
+    if constexpr (!kFp4) load_raw(g, lds, 1);
+    scales(g, 0);
+    convert(0);
+  };
+  // One K step on the ring.  FIRST: the tile's first step (zero C operand on
+  // each accumulator's first MFMA); HOLD: B' lets the previous tile's stores
+  // stay in flight; nkt: the K step of step s+1 (scale tail at B'); tg: the
+  // step this one queues the DMA of.
+  auto step_ring = [&](auto first, auto hold, int nkt, const Tgt& tg) __attribute__((always_inline)) {
+    constexpr bool kFirst = decltype(first)::value;
+    constexpr bool kHold = decltype(hold)::value;
+    static_assert((kStages & (kStages - 1)) == 0 && kStages > 2, "ring of a power-of-two number of stages");
+    constexpr int kWaitSteady = (kStages - 2) * kDmaPerStep;
+    constexpr int kWait = kHold ? kWaitSteady + kNStores : kWaitSteady;
+    static_assert(kWait <= 63, "vmcnt counts to 63");
+    const Geo g = geo(lane_opaque());
+    const uint8_t* st = lds + stage_at(s);
+    const uint8_t* stn = lds + stage_at(s + 1);
+    constexpr int kSlices = kFp4 ? 16 : 8;
+    constexpr int kSpc = kSlices / 4;
+    constexpr int kPer1 = (Y::kDma + 2) / 3;  // DMA instructions per slice of 1..3
+    Dma d1;
+#pragma unroll
+    for (int n = 0; n < kSlices; ++n) {
+      // fragment reads two slices ahead of their first conversion (a slice
+      // of this tile is only 4 MFMAs): 8-bit chunks 2 and 3 in slices 1 and
+      // 3, chunk 1 of the next step in slice S-1 (after B'); FP4 chunks span
+      // four slices, so one chunk ahead is three slices
+      if constexpr (kFp4) {
+        if (n % kSpc == 0 && n / kSpc < 3) load_raw(g, st, n / kSpc + 1);
+      } else {
+        if (n == 1 || n == 3) load_raw(g, st, (n + 3) / 2);
+      }
+      if (n == 1) {
+        d1 = dma_setup(g, tg.t, tg.kt, tg.live, lds0 + stage_at(s + kStages - 1));
+        dma_sf(d1);
+      }
+      if (n >= 1 && n <= 3) {
+#pragma unroll
+        for (int q = 0; q < kPer1; ++q)
+          if ((n - 1) * kPer1 + q < Y::kDma) dma_ab(d1, (n - 1) * kPer1 + q);
+      }
+      if (n < kSlices - 1) {
+        if ((n + 1) % kSpc == 0) scales(g, (n + 1) / kSpc);
+        convert(n + 1);
+      } else {
+        scales(g, 0);
+        convert(0);
+      }
+#pragma unroll
+      for (int i = 0; i < kTM; ++i)
+#pragma unroll
+        for (int jj = 0; jj < kTN; ++jj)
+          acc[i][jj] = kMM ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab[n & 1][i], bb[n & 1][jj],
+                                                                     (kFirst && n == 0) ? zero16 : acc[i][jj], 0, 0, 0)
+                           : __builtin_amdgcn_mfma_f32_32x32x16_bf16(bb[n & 1][jj], ab[n & 1][i],
+                                                                     (kFirst && n == 0) ? zero16 : acc[i][jj], 0, 0, 0);
+      constexpr int kValu = BT == 256 ? 3 : 6;
+#pragma unroll
+      for (int k = 0; k < kTM * kTN; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);  // VALU
+        if (k < kTM + kTN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (n == kSlices - 3) {
+        wait_vm<kWait>();
+        barrier();  // B'
+        load_sf(g, stn, nkt);
+        load_raw(g, stn, 0);
+      }
+      if constexpr (!kFp4) {
+        if (n == kSlices - 2) load_raw(g, stn, 1);
+      }
+    }
+    ++s;
+  };
+
   const std::true_type yes;
   const std::false_type no;
+  if constexpr (MODE == kModeBf16 && kStages > 2) {
+    if (my_tiles > 0) prime_ring();
+    for (int i = 0; i < my_tiles; ++i) {
+      const bool more = i + 1 < my_tiles;
+      const Tile nxt = more ? make_tile<kBM, kBN>(p, t0 + (i + 1) * G) : cur;
+      const int ks = p.ksteps;
+      auto nk = [&](int kt) { return kt + 1 < ks ? kt + 1 : 0; };
+      step_ring(yes, yes, nk(0), next_target());
+      int kt = 1;
+#pragma unroll
+      for (int h = 1; h + 2 < kStages; ++h)
+        if (kt < ks) {
+          step_ring(no, yes, nk(kt), next_target());
+          ++kt;
+        }
+      for (; kt < ks; ++kt) step_ring(no, no, nk(kt), next_target());
+      store_all(store_ctx(cur));
+      cur = nxt;
+    }
+  } else {
   if constexpr (MODE == kModeBf16) {
     if (my_tiles > 0) {
       if (p.ksteps > 1) prime(Tgt{cur, 1, true});
@@ -606,8 +795,9 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
       }
     }
     store_all(store_ctx(cur));
-    after_dma = 63;  // FP8 datapath: 64 stores; waiting for 63 covers every earlier DMA
+    after_dma = 1;  // FP8 datapath: kNStores stores follow the DMA; waiting for all but one covers it
     cur = nxt;
+  }
   }
   // no DMA may still be writing this workgroup's LDS when it exits
   wait_vm<0>();

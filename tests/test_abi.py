@@ -91,12 +91,12 @@ def test_errors_before_device_work(lib):
     assert f(*([good + 8] + args[1:]), *dims, 32, 0, 0, 0, None) == lib.MXG_ERR_ALIGN
     assert f(*(args[:4] + [good + 4] + args[5:]), *dims, 32, 0, 0, 0, None) == lib.MXG_ERR_ALIGN
     assert f(*args, *dims, 32, 0, 0, 256, None) == lib.MXG_ERR_FLAGS    # unknown bit
-    # m-major C: the bf16 datapath, float32 C, 256x256 tiles, M % 4 == 0
+    # m-major C: the bf16 datapath, float32 C, M % 4 == 0 (either tile size)
     mm = lib.MXG_FLAG_C_MMAJOR
     assert f(*args, *dims, 32, 0, 0, mm | lib.MXG_FLAG_FP8_MFMA, None) == lib.MXG_ERR_FLAGS
     assert f(*args, *dims, 32, 0, 0, mm | lib.MXG_FLAG_C_BF16, None) == lib.MXG_ERR_FLAGS
     assert f(*args, *dims, 32, 0, 0, mm | lib.MXG_FLAG_C_F16, None) == lib.MXG_ERR_FLAGS
-    assert f(*args, *dims, 32, 0, 0, mm | lib.MXG_FLAG_TILE_128, None) == lib.MXG_ERR_FLAGS
+    assert f(*args, *dims, 32, 0, 0, mm | lib.MXG_FLAG_TILE_128, None) == lib.MXG_ERR_DEVICE   # valid; no GPU here
     assert f(*args, 250, 256, 256, 1, 32, 0, 0, mm, None) == lib.MXG_ERR_ALIGN
     # m-major C rows run along M: M is bounded like N (32-bit per-tile store offsets)
     assert f(*args, (1 << 22) - 4, 16, 16, 1, 32, 0, 0, mm, None) != lib.MXG_ERR_SHAPE

@@ -33,13 +33,14 @@ def run(lib, p, flags=0, c_dtype=torch.float32, guard=2048):
     return buf[:L * M * N], am
 
 
+@pytest.mark.parametrize("tile", [0, 4, 8])     # auto, 128x128, 256x256 tiles
 @pytest.mark.parametrize("shape", [(256, 256, 256, 1), (300, 520, 544, 2), (64, 100, 32, 1), (520, 260, 1536, 1),
                                    (256, 256, 0, 1)])
-def test_fp4_matches_oracle(lib, shape):
+def test_fp4_matches_oracle(lib, shape, tile):
     M, N, K, L = shape
-    print(f"fp4 {shape}", flush=True)
+    print(f"fp4 {shape} tile flag {tile}", flush=True)
     p = W.make_problem(M, N, K, L, 32, E2M1, E2M1, seed=M + N + K + 1)
-    c, am = run(lib, p)
+    c, am = run(lib, p, tile)
     cref, sref, aref = oracle.gemm_amax(p["A"], p["B"], p["SFA"], p["SFB"], M, N, K, L, 32, E2M1, E2M1)
     got = c.view(L, M, N).double().cpu().numpy()
     assert np.all(np.abs(got - cref) <= 1e-5 * sref + 1e-30)
@@ -76,5 +77,3 @@ def test_fp4_rules(lib):
     p = W.make_problem(128, 128, 128, 1, 32, E2M1, E2M1, seed=1)
     with pytest.raises(ValueError):
         run(lib, p, lib.MXG_FLAG_FP8_MFMA)
-    with pytest.raises(ValueError):
-        run(lib, p, lib.MXG_FLAG_TILE_128)

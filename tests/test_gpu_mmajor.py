@@ -52,17 +52,18 @@ SHAPES = [
 ]
 
 
+@pytest.mark.parametrize("tile", [4, 8])       # 128x128, 256x256 tiles
 @pytest.mark.parametrize("M,N,K,L,sf,fa,fb", SHAPES)
-def test_mmajor_matches_oracle_and_nmajor(lib, M, N, K, L, sf, fa, fb):
-    print(f"m-major {M}x{N}x{K}x{L} sf={sf}", flush=True)
+def test_mmajor_matches_oracle_and_nmajor(lib, M, N, K, L, sf, fa, fb, tile):
+    print(f"m-major {M}x{N}x{K}x{L} sf={sf} tile flag {tile}", flush=True)
     p = W.make_problem(M, N, K, L, sf, fa, fb, seed=M + 3 * N + K)
-    c_m, amax_m = run(lib, p, lib.MXG_FLAG_C_MMAJOR)
+    c_m, amax_m = run(lib, p, lib.MXG_FLAG_C_MMAJOR | tile)
     c_ref, s_ref, amax_ref = oracle.gemm_amax(p["A"], p["B"], p["SFA"], p["SFB"], M, N, K, L, sf, fa, fb)
     check_c(c_m, c_ref, s_ref, "m-major C")
     check_amax(amax_m, amax_ref)
     assert amax_m == float(np.max(np.abs(c_m)))
     # the n-major result of the same kernel holds the same sums
-    c_n, amax_n = run(lib, p, lib.MXG_FLAG_TILE_256)
+    c_n, amax_n = run(lib, p, tile)
     assert np.array_equal(c_m.view(np.uint32), c_n.view(np.uint32))
     assert amax_m == amax_n
 

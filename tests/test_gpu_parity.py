@@ -301,3 +301,18 @@ def test_back_to_back_calls_bitwise_equal(lib, M, N, K, sf):
     rows = np.array([0, 1, M // 2, M - 1])
     c_ref, s_ref = oracle.gemm_rows(p["A"], p["B"], p["SFA"], p["SFB"], M, N, K, 1, sf, E4, E4, 0, rows)
     check_c(outs[0][0][0, rows], c_ref, s_ref, "back-to-back rows")
+
+
+@pytest.mark.parametrize("M,N,K,L,sf,fa,fb", [(300, 520, 592, 2, 32, E4, E4), (1000, 772, 1040, 1, 16, E5, E4)])
+def test_tile_sizes_agree_bitwise(lib, M, N, K, L, sf, fa, fb):
+    # Both tile sizes run the same per-output computation (the same K order
+    # through the same MFMA slices), so their C and Amax agree bit for bit.
+    p = W.make_problem(M, N, K, L, sf, fa, fb, seed=23)
+    d = to_device(p)
+    run(lib, p, d, flags=TILES["t128"])
+    c128, a128 = fetch(p, d)
+    c128 = c128.copy()
+    run(lib, p, d, flags=TILES["t256"])
+    c256, a256 = fetch(p, d)
+    assert np.array_equal(c128.view(np.uint32), c256.view(np.uint32))
+    assert float_bits(a128) == float_bits(a256)
