@@ -10,6 +10,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mxgemm.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h"))
 
 
 @pytest.fixture(scope="module")
@@ -21,10 +22,12 @@ def lib():
     return lib
 
 
-def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(mxgemm_\w+)\s*\(", text)))
+def declared_functions(headers=(HEADER,), prefix="mxgemm_"):
+    names = set()
+    for h in headers:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names.update(re.findall(r"\b(" + prefix + r"\w+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_expected_set(lib):
@@ -32,8 +35,11 @@ def test_header_declares_expected_set(lib):
 
 
 def test_every_declared_symbol_is_exported(lib):
+    # every function of every header under include/ (the GEMM library and its probes)
     cdll = ctypes.CDLL(lib.LIB_PATH)
-    for name in declared_functions():
+    names = declared_functions(HEADERS, prefix="mx(?:gemm|probe)_")
+    assert any(n.startswith("mxprobe_") for n in names)
+    for name in names:
         assert hasattr(cdll, name), name
 
 
