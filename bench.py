@@ -119,6 +119,14 @@ def proj_rope_bytes(tokens, n, qr):
     return 4 * tokens * n + 2 * 2 * tokens * qr + 2 * tokens * n + 2 * (tokens * n // 32)
 
 
+def proj_fused_bytes(tokens, n, k, sf):
+    """Algorithmic bytes of the fused projection kernel: A and B codes and their atoms read, bf16 cos and sin
+    read (64 rotary features), both directions' codes and scale bytes written."""
+    import workloads as W
+    return (tokens * k + n * k + W.sf_bytes(tokens, k, 1, sf) + W.sf_bytes(n, k, 1, sf) + 2 * 2 * tokens * 64
+            + 2 * tokens * n + 2 * (tokens * n // 32))
+
+
 def quantize_operands_shape(workload):
     """The stacked float32 operands of a GEMM workload, quantised as one (L, M + N, K) tensor.
 
@@ -407,9 +415,11 @@ def bench_quantize(args):
 
 
 def bench_proj(args):
-    """One JSON line for the projection pipeline of the projection page at the projection workload's
-    shape: a step repacks both operands' row-wise E8M0 scales into atoms, runs the GEMM + amax into
-    float32 Y, then the per-head RoPE and dual-direction MXFP8 quantisation of Y."""
+    """One JSON line for the projection of the projection page at the projection workload's shape.  A
+    step takes the page's inputs (E4M3 codes with row-wise E8M0 scales, bf16 cos / sin) to its four
+    outputs: both operands' scales repacked into atoms, then the GEMM with the per-head RoPE and
+    dual-direction MXFP8 quantisation fused into its epilogue.  The unfused pipeline (GEMM into float32
+    Y, then the RoPE + quantisation kernel) is timed beside it, and both give the same bytes."""
     import numpy as np
     import torch
 
@@ -447,6 +457,23 @@ def bench_proj(args):
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # the fused path: the page's interface (row-wise scales) -> repacks into a workspace -> the GEMM with the
+    # RoPE + dual MXFP8 epilogue
+    wsp = torch.empty(lib._lib.mxgemm_projection_workspace_bytes(tokens, heads, d, k), dtype=torch.uint8, device=dev)
+    fouts = tuple(torch.empty_like(o) for o in outs)
+
+    def step_fused(e=None):
+        # what mxgemm_projection_mxfp8 queues (row-wise scale repacks into the workspace, then the fused
+        # kernel), called kernel by kernel here so that events can time the fused kernel alone
+        if e:
+            e[0].record(stream)
+        lib.mxgemm_sf_rowwise_to_atoms(xs, sfa, tokens, k, 1, sf, sh)
+        lib.mxgemm_sf_rowwise_to_atoms(ws, sfb, n, k, 1, sf, sh)
+        if e:
+            e[1].record(stream)
+        lib.gemm_rope_mxfp8(A, B, sfa, sfb, cs, sn, tokens, heads, d, qr, k, stream=stream, out=fouts)
+        if e:
+            e[2].record(stream)
 
     def step(e=None):
         if e:
@@ -471,12 +498,32 @@ def bench_proj(args):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     part = [sum(e[j].elapsed_time(e[j + 1]) for e in ev) / args.steps for j in range(3)]
-    ms_per_step = wall * 1e3 / args.steps
+    ms_unfused = wall * 1e3 / args.steps
+    for _ in range(args.warmup):
+        step_fused()
+    torch.cuda.synchronize()
+    fev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step_fused(fev[i])
+    torch.cuda.synchronize()
+    wall_f = time.perf_counter() - t0
+    fused_repack_ms = sum(e[0].elapsed_time(e[1]) for e in fev) / args.steps
+    fused_ms = sum(e[1].elapsed_time(e[2]) for e in fev) / args.steps
+    for a, b in zip(outs, fouts):     # the fused outputs equal the unfused pipeline's
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), "fused and unfused projections differ"
+    # and so do those of the page-interface entry point (workspace, three kernels)
+    pouts = lib.projection_mxfp8(A, B, xs, ws, cs, sn, heads, d, qr, workspace=wsp, stream=stream)
+    torch.cuda.synchronize()
+    for a, b in zip(outs, pouts):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), "projection entry point differs"
+    ms_per_step = wall_f * 1e3 / args.steps
     flops = W.flops(tokens, n, k, 1)
     rope_bytes = proj_rope_bytes(tokens, n, qr)
     rope_gbs = rope_bytes / (part[2] * 1e-3) / 1e9
     out = {
-        "metric": "projection GEMM + RoPE + dual-direction MXFP8 TFLOP/s (GEMM flops over the whole step)",
+        "metric": "projection GEMM + RoPE + dual-direction MXFP8 TFLOP/s (GEMM flops over the whole step; "
+                  "fused path)",
         "value": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -484,11 +531,21 @@ def bench_proj(args):
         "data": "synthetic (seeded, MX-quantised; random rotary angles)",
         "config": {"workload": "projection pipeline", "tokens": tokens, "num_heads": heads, "head_dim": d,
                    "qk_rope": qr, "q_lora": k, "sf_vec_size": sf},
-        "repack_ms": round(part[0], 4), "gemm_ms": round(part[1], 4), "rope_quant_ms": round(part[2], 4),
-        "roofline": {"kernel": "proj_rope_mxfp8", "bound": "hbm", "achieved": round(rope_gbs, 1),
-                     "peak": HBM_GBS, "unit": "GB/s", "frac": round(rope_gbs / HBM_GBS, 4),
-                     "traffic": read_traffic(W.WORKLOADS[5]["name"], False, "proj"),
-                     "algorithmic_bytes": rope_bytes},
+        "repack_ms": round(fused_repack_ms, 4), "fused_kernel_ms": round(fused_ms, 4),
+        "unfused": {"ms_per_step": round(ms_unfused, 4), "repack_ms": round(part[0], 4), "gemm_ms": round(part[1], 4),
+                    "rope_quant_ms": round(part[2], 4),
+                    "what": "row-wise scale repacks, the GEMM into float32 Y, then the RoPE + dual MXFP8 kernel"},
+        "roofline": {"kernel": "gemm_rope_mxfp8 (fused)", "bound": "mfma",
+                     "achieved": round(flops / (fused_ms * 1e-3) / 1e12, 2), "peak": PEAK_FP8, "unit": "TFLOP/s",
+                     "frac": round(flops / (fused_ms * 1e-3) / 1e12 / PEAK_FP8, 4),
+                     "peak_of_datapath": PEAK_BF16,
+                     "frac_of_datapath_peak": round(flops / (fused_ms * 1e-3) / 1e12 / PEAK_BF16, 4),
+                     "traffic": None,
+                     "algorithmic_bytes": proj_fused_bytes(tokens, n, k, sf)},
+        "unfused_rope_kernel_roofline": {"bound": "hbm", "achieved": round(rope_gbs, 1), "peak": HBM_GBS,
+                                         "unit": "GB/s", "frac": round(rope_gbs / HBM_GBS, 4),
+                                         "traffic": read_traffic(W.WORKLOADS[5]["name"], False, "proj"),
+                                         "algorithmic_bytes": rope_bytes},
     }
     if args.copy_probe:
         copy_probe()

@@ -48,7 +48,8 @@ MXG_ERR_FLAGS = -8
 EXPORTED = ("mxgemm_amax", "mxgemm_amax_ex", "mxgemm_amax_reset", "mxgemm_check_support",
             "mxgemm_sf_bytes", "mxgemm_launch_config", "mxgemm_strerror", "mxgemm_mx_quantize",
             "mxgemm_sf_rowwise_to_atoms", "mxgemm_plan_init", "mxgemm_plan_execute", "mxgemm_codes_to_kmajor",
-            "mxgemm_proj_rope_mxfp8")
+            "mxgemm_proj_rope_mxfp8", "mxgemm_gemm_rope_mxfp8", "mxgemm_projection_workspace_bytes",
+            "mxgemm_projection_mxfp8")
 
 
 class MxgemmError(Exception):
@@ -100,6 +101,12 @@ def _load():
     lib.mxgemm_codes_to_kmajor.restype = ci
     lib.mxgemm_proj_rope_mxfp8.argtypes = [vp] * 7 + [i64] * 4 + [vp]
     lib.mxgemm_proj_rope_mxfp8.restype = ci
+    lib.mxgemm_gemm_rope_mxfp8.argtypes = [vp] * 10 + [i64] * 5 + [ci, ci, ci, vp]
+    lib.mxgemm_gemm_rope_mxfp8.restype = ci
+    lib.mxgemm_projection_workspace_bytes.argtypes = [i64] * 4
+    lib.mxgemm_projection_workspace_bytes.restype = ctypes.c_size_t
+    lib.mxgemm_projection_mxfp8.argtypes = [vp] * 10 + [i64] * 5 + [vp, ctypes.c_size_t, vp]
+    lib.mxgemm_projection_mxfp8.restype = ci
     return lib
 
 
@@ -233,6 +240,53 @@ def proj_rope_mxfp8(y, cos, sin, num_heads, head_dim=192, qk_rope=64, stream=Non
         raise MxgemmValueError(MXG_ERR_FMT, "y must be float32, cos and sin bfloat16")
     st = _lib.mxgemm_proj_rope_mxfp8(_ptr(y), _ptr(cos), _ptr(sin), _ptr(out[0]), _ptr(out[1]), _ptr(out[2]),
                                      _ptr(out[3]), tokens, num_heads, head_dim, qk_rope, _stream(stream))
+    if st != MXG_OK:
+        _raise(st)
+    return out
+
+
+def _proj_outputs(tokens, num_heads, head_dim, dev, out):
+    import torch
+    if out is None:
+        out = (torch.empty((tokens, num_heads, head_dim), dtype=torch.float8_e4m3fn, device=dev),
+               torch.empty((tokens, num_heads, head_dim // 32), dtype=torch.uint8, device=dev),
+               torch.empty((tokens, num_heads, head_dim), dtype=torch.float8_e4m3fn, device=dev),
+               torch.empty((tokens // 32, num_heads, head_dim), dtype=torch.uint8, device=dev))
+    for t, name in zip(out, ("row", "row scales", "col", "col scales")):
+        if not t.is_contiguous():
+            raise MxgemmValueError(MXG_ERR_ALIGN, f"{name} must be contiguous")
+    return out
+
+
+def gemm_rope_mxfp8(A, B, SFA, SFB, cos, sin, tokens, num_heads, head_dim, qk_rope, K, sf_vec_size=32,
+                    a_fmt=MXG_FMT_E4M3, b_fmt=MXG_FMT_E4M3, stream=None, out=None):
+    """C-ABI mxgemm_gemm_rope_mxfp8: the projection GEMM with RoPE and dual-direction MXFP8 fused into its
+    epilogue, on k-major codes A (tokens, K) / B (num_heads * head_dim, K) and atom-layout scales.  Returns
+    (out_fp8_row, out_scales_row, out_fp8_col, out_scales_col) shaped as proj_rope_mxfp8's."""
+    out = _proj_outputs(tokens, num_heads, head_dim, A.device, out)
+    st = _lib.mxgemm_gemm_rope_mxfp8(_ptr(A), _ptr(B), _ptr(SFA), _ptr(SFB), _ptr(cos), _ptr(sin), _ptr(out[0]),
+                                     _ptr(out[1]), _ptr(out[2]), _ptr(out[3]), tokens, num_heads, head_dim, qk_rope,
+                                     K, sf_vec_size, a_fmt, b_fmt, _stream(stream))
+    if st != MXG_OK:
+        _raise(st)
+    return out
+
+
+def projection_mxfp8(x, w, x_scale, w_scale, cos, sin, num_heads, head_dim=192, qk_rope=64, workspace=None,
+                     stream=None, out=None):
+    """C-ABI mxgemm_projection_mxfp8, the projection page's MXFP8-input path: x (tokens, K) and w
+    (num_heads * head_dim, K) E4M3 codes, row-wise E8M0 scales x_scale (tokens, ceil(K/32)) and w_scale
+    (num_heads * head_dim, ceil(K/32)), bf16 cos / sin (tokens, qk_rope).  Allocates the workspace when
+    not given.  Returns the four outputs as proj_rope_mxfp8 does."""
+    import torch
+    tokens, k = x.shape
+    need = _lib.mxgemm_projection_workspace_bytes(tokens, num_heads, head_dim, k)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    out = _proj_outputs(tokens, num_heads, head_dim, x.device, out)
+    st = _lib.mxgemm_projection_mxfp8(_ptr(x), _ptr(w), _ptr(x_scale), _ptr(w_scale), _ptr(cos), _ptr(sin),
+                                      _ptr(out[0]), _ptr(out[1]), _ptr(out[2]), _ptr(out[3]), tokens, num_heads,
+                                      head_dim, qk_rope, k, _ptr(workspace), workspace.numel(), _stream(stream))
     if st != MXG_OK:
         _raise(st)
     return out
@@ -390,6 +444,6 @@ __all__ = [
     "mxgemm_mx_quantize", "mx_quantize", "mxgemm_sf_rowwise_to_atoms", "sf_from_rowwise", "Plan",
     "MXG_FMT_E4M3", "MXG_FMT_E5M2", "MXG_FMT_E2M1", "MXG_FLAG_AMAX_ACCUMULATE", "MXG_FLAG_FP8_MFMA", "MXG_FLAG_TILE_128",
     "MXG_FLAG_TILE_256", "MXG_FLAG_C_BF16", "MXG_FLAG_C_F16", "MXG_FLAG_C_MMAJOR", "codes_to_kmajor",
-    "proj_rope_mxfp8", "MxgemmError", "MxgemmValueError",
+    "proj_rope_mxfp8", "gemm_rope_mxfp8", "projection_mxfp8", "MxgemmError", "MxgemmValueError",
     "MxgemmRuntimeError",
 ]

@@ -17,6 +17,9 @@ hipError_t launch_bf16_f32_t128(const Params& p, int sf, int fa, int fb, int ct,
 // the same with a 16-bit C (ct 1: bfloat16, 2: float16)
 hipError_t launch_bf16_c16_t256(const Params& p, int sf, int fa, int fb, int ct, int64_t grid, hipStream_t s);
 hipError_t launch_bf16_c16_t128(const Params& p, int sf, int fa, int fb, int ct, int64_t grid, hipStream_t s);
+// 256x256 tiles, bf16 datapath, the projection epilogue in place of C
+// (Params' rope / code / scale fields); 8-bit formats
+hipError_t launch_proj_t256(const Params& p, int sf, int fa, int fb, int64_t grid, hipStream_t s);
 // scaled-FP8 datapath, float32 C; bt = 256 or 128
 hipError_t launch_fp8(const Params& p, int sf, int fa, int fb, int bt, int64_t grid, hipStream_t s);
 

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <initializer_list>
 #include <mutex>
 #include <stdlib.h>
 #include <string.h>
@@ -297,6 +298,111 @@ int launch_prepared(const Prepared& pr, const void* A, const void* B, const uint
   return e == hipSuccess ? MXG_OK : MXG_ERR_LAUNCH;
 }
 
+// --- the projection: GEMM with the RoPE + dual-direction MXFP8 epilogue -------
+
+// Size and format rules of the fused projection (no HIP call).
+int check_projection(int64_t tokens, int64_t H, int64_t D, int64_t QR, int64_t K, int sf, int fa, int fb) {
+  if (tokens < 0 || H < 0 || D <= 0 || QR < 0 || K <= 0) return MXG_ERR_SHAPE;
+  if (sf != 16 && sf != 32) return MXG_ERR_SFVEC;
+  if ((fa != MXG_FMT_E4M3 && fa != MXG_FMT_E5M2) || (fb != MXG_FMT_E4M3 && fb != MXG_FMT_E5M2)) return MXG_ERR_FMT;
+  if (!fits_i32(tokens) || !fits_i32(H) || !fits_i32(D) || !fits_i32(H * D)) return MXG_ERR_SHAPE;
+  const int64_t N = H * D;
+  const int st = check_sizes(tokens, N, K, 1, sf, fa, fb);
+  if (st != MXG_OK) return st;
+  // a head spans at least one 128-column wave block, blocks of 32 features
+  // never cross heads, the rotary part is a multiple of 16 features up to 64
+  if (D % 32 != 0 || D < 128 || QR % 16 != 0 || QR > 64 || N % 128 != 0) return MXG_ERR_SHAPE;
+  // no head's rotary features cross a 128-column boundary (the pattern
+  // repeats every 128 heads at most)
+  for (int64_t h = 0; QR > 0 && h < std::min<int64_t>(H, 128); ++h) {
+    const int64_t a = h * D + D - QR;
+    if (a / 128 != (a + QR - 1) / 128) return MXG_ERR_SHAPE;
+  }
+  if (tokens % 32 != 0) return MXG_ERR_ALIGN;  // column blocks of 32 tokens
+  return MXG_OK;
+}
+
+bool aligned16_all(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (!aligned16(p)) return false;
+  return true;
+}
+
+// The fused kernel on atom-layout scales; sizes already validated.
+int launch_projection(const void* A, const void* B, const uint8_t* SFA, const uint8_t* SFB, const uint16_t* cs,
+                      const uint16_t* sn, uint8_t* rc, uint8_t* rsc, uint8_t* cc, uint8_t* csc, int64_t tokens,
+                      int64_t H, int64_t D, int64_t QR, int64_t K, int sf, int fa, int fb, int cus, hipStream_t s) {
+  mxg::Params p;
+  memset(&p, 0, sizeof(p));
+  p.A = static_cast<const uint8_t*>(A);
+  p.B = static_cast<const uint8_t*>(B);
+  p.SFA = SFA;
+  p.SFB = SFB;
+  p.M = (int)tokens;
+  p.N = (int)(H * D);
+  p.K = (int)K;
+  p.L = 1;
+  p.Kbytes = (int)K;
+  p.Kb = (int)cdiv(K, sf);
+  p.Kg = (int)cdiv(K, 4 * sf);
+  p.MNbA = (int)cdiv(tokens, 128);
+  p.MNbB = (int)cdiv(H * D, 128);
+  p.tilesM = (int)cdiv(tokens, 256);
+  p.tilesN = (int)cdiv(H * D, 256);
+  p.ksteps = (int)cdiv(K, 128);
+  p.num_tiles = p.tilesM * p.tilesN;
+  const int64_t grid = grid_for(p.num_tiles, cus, 1);
+  p.xcd_remap = grid % 8 == 0 ? 1 : 0;
+  p.rope_cos = cs;
+  p.rope_sin = sn;
+  p.row_codes = rc;
+  p.row_scales = rsc;
+  p.col_codes = cc;
+  p.col_scales = csc;
+  p.head_dim = (int)D;
+  p.qk_rope = (int)QR;
+  return mxg::launch_proj_t256(p, sf, fa, fb, grid, s) == hipSuccess ? MXG_OK : MXG_ERR_LAUNCH;
+}
+
+// Row-wise E8M0 scales into atoms (the kernel of mxgemm_sf_rowwise_to_atoms);
+// sizes already validated.
+hipError_t launch_rowwise(const uint8_t* rowwise, uint8_t* SF, int64_t MN, int64_t K, int64_t L, int sf, int cus,
+                          hipStream_t s) {
+  mxg::repack::RParams p;
+  p.R = rowwise;
+  p.SF = SF;
+  p.MN = (int)MN;
+  p.Kb = (int)cdiv(K, sf);
+  p.MNb = (int)cdiv(MN, 128);
+  p.Kg = (int)cdiv(K, 4 * sf);
+  p.num_atoms = (int)(L * p.MNb * p.Kg);
+  const int64_t grid = std::min<int64_t>(p.num_atoms, 16LL * cus);
+  hipLaunchKernelGGL(mxg::repack::rowwise_to_atoms_kernel, dim3((unsigned)grid), dim3(mxg::repack::kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+// Workspace of the full projection: x's atoms, then w's, each 256-byte aligned.
+size_t projection_ws_a(int64_t tokens, int64_t K, int sf) {
+  return (size_t)((512 * cdiv(tokens, 128) * cdiv(K, 4 * sf) + 255) / 256 * 256);
+}
+size_t projection_ws_bytes(int64_t tokens, int64_t N, int64_t K, int sf) {
+  return projection_ws_a(tokens, K, sf) + (size_t)(512 * cdiv(N, 128) * cdiv(K, 4 * sf));
+}
+
+// The page's projection on row-wise scales: both repacks into `ws`, then the
+// fused kernel.  Everything validated by the caller.
+int run_projection(const void* x, const void* w, const uint8_t* xs, const uint8_t* wsc, const uint16_t* cs,
+                   const uint16_t* sn, uint8_t* rc, uint8_t* rsc, uint8_t* cc, uint8_t* csc, int64_t tokens, int64_t H,
+                   int64_t D, int64_t QR, int64_t K, uint8_t* ws, int cus, hipStream_t s) {
+  constexpr int sf = 32;
+  uint8_t* sfa = ws;
+  uint8_t* sfb = ws + projection_ws_a(tokens, K, sf);
+  if (launch_rowwise(xs, sfa, tokens, K, 1, sf, cus, s) != hipSuccess) return MXG_ERR_LAUNCH;
+  if (launch_rowwise(wsc, sfb, H * D, K, 1, sf, cus, s) != hipSuccess) return MXG_ERR_LAUNCH;
+  return launch_projection(x, w, sfa, sfb, cs, sn, rc, rsc, cc, csc, tokens, H, D, QR, K, sf, MXG_FMT_E4M3,
+                           MXG_FMT_E4M3, cus, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -427,18 +533,8 @@ int mxgemm_sf_rowwise_to_atoms(const uint8_t* rowwise, uint8_t* SF, int64_t MN, 
   int st = device_check(&dev, &cus);
   if (st != MXG_OK) return st;
   if (!on_device(rowwise, dev) || !on_device(SF, dev)) return MXG_ERR_DEVICE;
-  mxg::repack::RParams p;
-  p.R = rowwise;
-  p.SF = SF;
-  p.MN = (int)MN;
-  p.Kb = (int)cdiv(K, sf_vec_size);
-  p.MNb = (int)cdiv(MN, 128);
-  p.Kg = (int)cdiv(K, 4 * sf_vec_size);
-  p.num_atoms = (int)(L * p.MNb * p.Kg);
-  const int64_t grid = std::min<int64_t>(p.num_atoms, 16LL * cus);
-  hipLaunchKernelGGL(mxg::repack::rowwise_to_atoms_kernel, dim3((unsigned)grid), dim3(mxg::repack::kThreads), 0,
-                     (hipStream_t)stream, p);
-  return hipGetLastError() == hipSuccess ? MXG_OK : MXG_ERR_LAUNCH;
+  return launch_rowwise(rowwise, SF, MN, K, L, sf_vec_size, cus, (hipStream_t)stream) == hipSuccess ? MXG_OK
+                                                                                                 : MXG_ERR_LAUNCH;
 }
 
 int mxgemm_codes_to_kmajor(const void* src, void* dst, int64_t MN, int64_t K, int64_t L, void* stream) {
@@ -516,6 +612,63 @@ int mxgemm_proj_rope_mxfp8(const float* Y, const uint16_t* cos_bf16, const uint1
   hipLaunchKernelGGL(mxg::rope::proj_rope_mxfp8_kernel, dim3((unsigned)grid), dim3(mxg::rope::kThreads),
                      (unsigned)mxg::rope::lds_bytes(p.D, p.QR, p.per_wg), (hipStream_t)stream, p);
   return hipGetLastError() == hipSuccess ? MXG_OK : MXG_ERR_LAUNCH;
+}
+
+int mxgemm_gemm_rope_mxfp8(const void* A, const void* B, const uint8_t* SFA, const uint8_t* SFB,
+                           const uint16_t* cos_bf16, const uint16_t* sin_bf16, uint8_t* row_codes,
+                           uint8_t* row_scales, uint8_t* col_codes, uint8_t* col_scales, int64_t tokens,
+                           int64_t num_heads, int64_t head_dim, int64_t qk_rope, int64_t K, int sf_vec_size, int a_fmt,
+                           int b_fmt, void* stream) {
+  int st = check_projection(tokens, num_heads, head_dim, qk_rope, K, sf_vec_size, a_fmt, b_fmt);
+  if (st != MXG_OK) return st;
+  if (tokens == 0 || num_heads == 0) return MXG_OK;
+  if (!A || !B || !SFA || !SFB || !row_codes || !row_scales || !col_codes || !col_scales ||
+      (qk_rope > 0 && (!cos_bf16 || !sin_bf16)))
+    return MXG_ERR_NULL;
+  if (!aligned16_all({A, B, SFA, SFB, row_codes, row_scales, col_codes, col_scales}) ||
+      (qk_rope > 0 && !aligned16_all({cos_bf16, sin_bf16})))
+    return MXG_ERR_ALIGN;
+  int dev = 0, cus = 0;
+  st = device_check(&dev, &cus);
+  if (st != MXG_OK) return st;
+  for (const void* q : {A, B, (const void*)SFA, (const void*)SFB, (const void*)row_codes, (const void*)row_scales,
+                        (const void*)col_codes, (const void*)col_scales})
+    if (!on_device(q, dev)) return MXG_ERR_DEVICE;
+  if (qk_rope > 0 && (!on_device(cos_bf16, dev) || !on_device(sin_bf16, dev))) return MXG_ERR_DEVICE;
+  return launch_projection(A, B, SFA, SFB, cos_bf16, sin_bf16, row_codes, row_scales, col_codes, col_scales, tokens,
+                           num_heads, head_dim, qk_rope, K, sf_vec_size, a_fmt, b_fmt, cus, (hipStream_t)stream);
+}
+
+size_t mxgemm_projection_workspace_bytes(int64_t tokens, int64_t num_heads, int64_t head_dim, int64_t K) {
+  if (tokens < 0 || num_heads < 0 || head_dim < 0 || K < 0) return 0;
+  return projection_ws_bytes(tokens, num_heads * head_dim, K, 32);
+}
+
+int mxgemm_projection_mxfp8(const void* x, const void* w, const uint8_t* x_scale, const uint8_t* w_scale,
+                            const uint16_t* cos_bf16, const uint16_t* sin_bf16, uint8_t* row_codes,
+                            uint8_t* row_scales, uint8_t* col_codes, uint8_t* col_scales, int64_t tokens,
+                            int64_t num_heads, int64_t head_dim, int64_t qk_rope, int64_t K, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  int st = check_projection(tokens, num_heads, head_dim, qk_rope, K, 32, MXG_FMT_E4M3, MXG_FMT_E4M3);
+  if (st != MXG_OK) return st;
+  if (tokens == 0 || num_heads == 0) return MXG_OK;
+  if (!x || !w || !x_scale || !w_scale || !row_codes || !row_scales || !col_codes || !col_scales || !workspace ||
+      (qk_rope > 0 && (!cos_bf16 || !sin_bf16)))
+    return MXG_ERR_NULL;
+  if (workspace_bytes < projection_ws_bytes(tokens, num_heads * head_dim, K, 32)) return MXG_ERR_SHAPE;
+  if (!aligned16_all({x, w, row_codes, row_scales, col_codes, col_scales}) || (reinterpret_cast<uintptr_t>(workspace) & 255) ||
+      (qk_rope > 0 && !aligned16_all({cos_bf16, sin_bf16})))
+    return MXG_ERR_ALIGN;
+  int dev = 0, cus = 0;
+  st = device_check(&dev, &cus);
+  if (st != MXG_OK) return st;
+  for (const void* q : {x, w, (const void*)x_scale, (const void*)w_scale, (const void*)row_codes,
+                        (const void*)row_scales, (const void*)col_codes, (const void*)col_scales, (const void*)workspace})
+    if (!on_device(q, dev)) return MXG_ERR_DEVICE;
+  if (qk_rope > 0 && (!on_device(cos_bf16, dev) || !on_device(sin_bf16, dev))) return MXG_ERR_DEVICE;
+  return run_projection(x, w, x_scale, w_scale, cos_bf16, sin_bf16, row_codes, row_scales, col_codes, col_scales,
+                        tokens, num_heads, head_dim, qk_rope, K, static_cast<uint8_t*>(workspace), cus,
+                        (hipStream_t)stream);
 }
 
 int mxgemm_amax(const void* A, const void* B, const uint8_t* SFA, const uint8_t* SFB, float* C, float* Amax,

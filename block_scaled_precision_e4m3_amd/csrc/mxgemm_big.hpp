@@ -54,6 +54,7 @@
 // reduced across the wave with xor-shuffles, then one atomic max per wave.
 #pragma once
 
+#include "mx_quantize.hpp"
 #include "mxgemm_common.hpp"
 
 namespace mxg {
@@ -115,6 +116,7 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   constexpr bool kFp4 = FA == 2;
   static_assert(!kFp4 || (FB == 2 && SF == 32 && MODE == kModeBf16), "FP4: both operands, sf = 32, bf16 path");
   static_assert(!kCMajorM<CT> || MODE == kModeBf16, "m-major C: bf16 path");
+  static_assert(CT != 4 || (MODE == kModeBf16 && BT == 256), "projection epilogue: bf16 path, 256x256 tiles");
   // LDS ring stages: a 128x128 tile's steps are short, so its bf16 datapath
   // queues the DMA three steps ahead in four stages; a 256x256 tile's ring
   // fills the LDS with two
@@ -332,6 +334,171 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
       }
     }
   };
+  // --- projection epilogue (CT == 4) --------------------------------------------
+  // ("GEMM + RoPE + MXFP8 Projection (SM100)", sections "Overview", "Shapes"
+  // and "Equations".)  In place of storing C, the tile's float32
+  // accumulators, viewed per head of head_dim features, get RoPE on each
+  // head's trailing qk_rope features -- pairs (y[2i], y[2i+1]) in, rotated
+  // first members to position i and second members to R + i out (R =
+  // qk_rope / 2), with the token's bf16 cos / sin rows, each product and sum
+  // rounded on its own -- and then leave as E4M3 codes twice: blocks of 32
+  // features of a token (row codes, scales (M, N/32)) and blocks of 32 tokens
+  // of a feature (column codes, scales (M/32, N)); the block exponent is the
+  // smallest e with 448 * 2^e >= the block's largest magnitude and codes
+  // round to nearest even (the MX quantiser's rule).  Each wave works
+  // through its 128 x 128 block 32 tokens at a time in its quarter of the
+  // LDS stage the tile's last step freed (rows of 132 floats; the last 4 of
+  // row g hold the column exponents of columns 4g..4g+3).  The host
+  // guarantees M % 32 == 0, N % 128 == 0, head_dim % 32 == 0, qk_rope a
+  // multiple of 16 up to 64, and that no head's rotary features cross a
+  // 128-column boundary, so 32-token and 32-feature blocks and rotary
+  // segments all lie inside one wave's block.
+  auto store_proj = [&](const Tile& T, uint8_t* scratch) __attribute__((always_inline)) {
+    constexpr int P = 132;
+    float* z = reinterpret_cast<float*>(scratch) + wave * 32 * P;
+    const int ln = lane_opaque();
+    const int r = ln & 31, h = ln >> 5;
+    const int N = p.N, D = p.head_dim, QR = p.qk_rope, R = QR >> 1;
+    const int c0 = T.n0 + kWN * wn;  // the wave's first column
+    // the wave's rotary segment [seg, seg + QR), relative to c0, if any: the
+    // rotary part of the head holding column c0, or of the next head when
+    // that one ends before c0
+    int seg = (c0 / D) * D + D - QR - c0;
+    if (seg + QR <= 0) seg += D;
+    const bool rot = QR > 0 && seg < kWN;
+    // RoPE lanes: lane pair (2t, 2t+1) takes token t of the block-row, R/2
+    // pairs each; the bf16 cos / sin words of the next block-row are loaded
+    // while this one is quantised
+    const int t = ln >> 1;
+    const int pp = (ln & 1) * (R >> 1);  // this lane's first pair
+    uint2 tc1[4], tc2[4], ts1[4], ts2[4];
+    auto load_tables = [&](int i) {
+      const int64_t tok = (int64_t)T.m0 + kWM * wm + 32 * i + t;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (4 * u < (R >> 1)) {
+          const uint16_t* cs = p.rope_cos + tok * QR + pp + 4 * u;
+          const uint16_t* sn = p.rope_sin + tok * QR + pp + 4 * u;
+          tc1[u] = *reinterpret_cast<const uint2*>(cs);
+          tc2[u] = *reinterpret_cast<const uint2*>(cs + R);
+          ts1[u] = *reinterpret_cast<const uint2*>(sn);
+          ts2[u] = *reinterpret_cast<const uint2*>(sn + R);
+        }
+      }
+    };
+    if (rot && c0 < N && kWM * wm < T.mvalid) load_tables(0);
+#pragma unroll
+    for (int i = 0; i < kTM; ++i) {
+      const int row0 = kWM * wm + 32 * i;  // the block-row's first tile row
+      if (row0 >= T.mvalid || c0 >= N) continue;
+      const int64_t tok0 = (int64_t)T.m0 + row0;
+      // 1. accumulators to LDS, lane (r, h): row r, columns 32j + 8q + 4h
+#pragma unroll
+      for (int j = 0; j < kTN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          v4f v;
+          v[0] = acc[i][j][4 * q];
+          v[1] = acc[i][j][4 * q + 1];
+          v[2] = acc[i][j][4 * q + 2];
+          v[3] = acc[i][j][4 * q + 3];
+          *reinterpret_cast<v4f*>(z + r * P + 32 * j + 8 * q + 4 * h) = v;
+        }
+      // 2. RoPE; every read of the segment precedes every write (the wave's
+      // LDS operations run in order)
+      if (rot) {
+#pragma clang fp contract(off)
+        float a[16], b[16], c1[16], s1[16], c2[16], s2[16];
+        auto lo = [](unsigned w) { return __uint_as_float(w << 16); };
+        auto hi = [](unsigned w) { return __uint_as_float(w & 0xFFFF0000u); };
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (4 * u < (R >> 1)) {
+            const float* zr = z + t * P + seg + 2 * pp + 8 * u;
+            const v4f x0 = *reinterpret_cast<const v4f*>(zr);
+            const v4f x1 = *reinterpret_cast<const v4f*>(zr + 4);
+            a[4 * u] = x0[0], b[4 * u] = x0[1], a[4 * u + 1] = x0[2], b[4 * u + 1] = x0[3];
+            a[4 * u + 2] = x1[0], b[4 * u + 2] = x1[1], a[4 * u + 3] = x1[2], b[4 * u + 3] = x1[3];
+            c1[4 * u] = lo(tc1[u].x), c1[4 * u + 1] = hi(tc1[u].x), c1[4 * u + 2] = lo(tc1[u].y), c1[4 * u + 3] = hi(tc1[u].y);
+            c2[4 * u] = lo(tc2[u].x), c2[4 * u + 1] = hi(tc2[u].x), c2[4 * u + 2] = lo(tc2[u].y), c2[4 * u + 3] = hi(tc2[u].y);
+            s1[4 * u] = lo(ts1[u].x), s1[4 * u + 1] = hi(ts1[u].x), s1[4 * u + 2] = lo(ts1[u].y), s1[4 * u + 3] = hi(ts1[u].y);
+            s2[4 * u] = lo(ts2[u].x), s2[4 * u + 1] = hi(ts2[u].x), s2[4 * u + 2] = lo(ts2[u].y), s2[4 * u + 3] = hi(ts2[u].y);
+          }
+        }
+        if (i + 1 < kTM && row0 + 32 < T.mvalid) load_tables(i + 1);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (4 * u < (R >> 1)) {
+            v4f f, g;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int x = 4 * u + e;
+              const float ac = a[x] * c1[x], bs = b[x] * s1[x], bc = b[x] * c2[x], as = a[x] * s2[x];
+              f[e] = ac - bs;
+              g[e] = bc + as;
+            }
+            *reinterpret_cast<v4f*>(z + t * P + seg + pp + 4 * u) = f;
+            *reinterpret_cast<v4f*>(z + t * P + seg + R + pp + 4 * u) = g;
+          }
+        }
+      }
+      // 3. column blocks: lane (cg, h) takes columns 4cg..4cg+3 over rows
+      // 16h..16h+15; the halves meet by an xor shuffle over 32 lanes
+      {
+        v4f m = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          const v4f v = *reinterpret_cast<const v4f*>(z + (16 * h + rr) * P + 4 * r);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) m[e] = fmaxf(m[e], fabsf(v[e]));
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) m[e] = fmaxf(m[e], __shfl_xor(m[e], 32));
+        v4u ec;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ec[e] = (unsigned)quant::block_exponent<0>(m[e]);
+        if (h == 0) {
+          *reinterpret_cast<v4u*>(z + r * P + 128) = ec;
+          const unsigned sb = ((ec[0] + 127u) & 0xFFu) | (((ec[1] + 127u) & 0xFFu) << 8) |
+                              (((ec[2] + 127u) & 0xFFu) << 16) | (((ec[3] + 127u) & 0xFFu) << 24);
+          *reinterpret_cast<unsigned*>(p.col_scales + (tok0 >> 5) * N + c0 + 4 * r) = sb;
+        }
+      }
+      // 4. both directions' codes: lane takes rows (ln / 8) + 8k and column
+      // groups (ln % 8) + 8b; a row block (32 columns) is 8 consecutive
+      // lanes, whose maximum three DPP steps find (quad swaps, then the
+      // mirror of the half-row)
+      v4u ecol[4];
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) ecol[bb] = *reinterpret_cast<const v4u*>(z + ((ln & 7) + 8 * bb) * P + 128);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int rr = (ln >> 3) + 8 * k;
+        const int64_t tok = tok0 + rr;
+        unsigned rs = 0u;
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+          const int g = (ln & 7) + 8 * bb;
+          const v4f v = *reinterpret_cast<const v4f*>(z + rr * P + 4 * g);
+          const v4u ec = ecol[bb];
+          float bm = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+          bm = fmaxf(bm, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(bm), 0xB1, 0xF, 0xF, false)));
+          bm = fmaxf(bm, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(bm), 0x4E, 0xF, 0xF, false)));
+          bm = fmaxf(bm, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(bm), 0x141, 0xF, 0xF, false)));
+          const int er = quant::block_exponent<0>(bm);
+          const int64_t o = tok * N + c0 + 4 * g;
+          *reinterpret_cast<unsigned*>(p.row_codes + o) =
+              quant::codes4<0>(ldexpf(v[0], -er), ldexpf(v[1], -er), ldexpf(v[2], -er), ldexpf(v[3], -er));
+          *reinterpret_cast<unsigned*>(p.col_codes + o) =
+              quant::codes4<0>(ldexpf(v[0], -(int)ec[0]), ldexpf(v[1], -(int)ec[1]), ldexpf(v[2], -(int)ec[2]),
+                               ldexpf(v[3], -(int)ec[3]));
+          rs |= ((unsigned)(er + 127) & 0xFFu) << (8 * bb);
+        }
+        if ((ln & 7) == 0) *reinterpret_cast<unsigned*>(p.row_scales + tok * (N >> 5) + (c0 >> 5)) = rs;
+      }
+    }
+  };
+
   Tile cur = {0, 0, 0, 0, 0};
   int after_dma = 0;             // FP8 datapath: store instructions queued after the last DMA
   int s = 0;                     // global step index: selects the ring stage
@@ -523,12 +690,15 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   };
   // steps 0 and 1 go into the two stages at once; step 0's inputs are read
   // after both have landed everywhere
+  // (the projection epilogue queues step 1 from step 0 instead)
   auto prime = [&](const Tgt& n1) __attribute__((always_inline)) {
     const Geo g = geo(lane_opaque());
-    const Dma d1 = dma_setup(g, n1.t, n1.kt, n1.live, lds0 + (unsigned)Y::kStage);
-    dma_sf(d1);
+    if constexpr (CT != 4) {
+      const Dma d1 = dma_setup(g, n1.t, n1.kt, n1.live, lds0 + (unsigned)Y::kStage);
+      dma_sf(d1);
 #pragma unroll
-    for (int q = 0; q < Y::kDma; ++q) dma_ab(d1, q);
+      for (int q = 0; q < Y::kDma; ++q) dma_ab(d1, q);
+    }
     wait_vm<0>();
     barrier();
     load_sf(g, lds, 0);
@@ -609,7 +779,7 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
         // this wave's DMA of step s+1 has landed; on a tile's first step the
         // previous tile's 64 C stores per lane, queued after that DMA, may
         // still be in flight
-        if constexpr (kFirst) wait_vm<kNStores - 1>();
+        if constexpr (kFirst && !kLate) wait_vm<kNStores - 1>();
         else wait_vm<0>();
         barrier();  // B'
         load_sf(g, stn, nkt);
@@ -771,7 +941,18 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   for (int i = 0; i < my_tiles; ++i) {
     const bool more = i + 1 < my_tiles;
     const Tile nxt = more ? make_tile<kBM, kBN>(p, t0 + (i + 1) * G) : cur;
-    if constexpr (MODE == kModeBf16) {
+    if constexpr (MODE == kModeBf16 && CT == 4) {
+      // the projection epilogue uses the stage the tile's last step freed,
+      // so no DMA goes into it ahead: every step queues the next step's DMA
+      const Tgt none = {cur, 0, false};
+      if (p.ksteps == 1) {
+        step_bf16(yes, yes, no, 0, Tgt{nxt, 0, more}, none);
+      } else {
+        step_bf16(yes, yes, no, 1, Tgt{cur, 1, true}, none);
+        for (int kt = 1; kt + 1 < p.ksteps; ++kt) step_bf16(no, yes, no, kt + 1, Tgt{cur, kt + 1, true}, none);
+        step_bf16(no, yes, no, 0, Tgt{nxt, 0, more}, none);
+      }
+    } else if constexpr (MODE == kModeBf16) {
       const Tgt none = {cur, 0, false};
       if (p.ksteps == 1) {
         const bool more2 = i + 2 < my_tiles;
@@ -794,7 +975,12 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
         step(no, p.ksteps - 1, nxt, more);
       }
     }
-    store_all(store_ctx(cur));
+    if constexpr (CT == 4) {
+      store_proj(cur, lds + ((s - 1) & 1) * Y::kStage);
+      barrier();  // every wave is done with that stage before the next step's DMA enters it
+    } else {
+      store_all(store_ctx(cur));
+    }
     after_dma = 1;  // FP8 datapath: kNStores stores follow the DMA; waiting for all but one covers it
     cur = nxt;
   }

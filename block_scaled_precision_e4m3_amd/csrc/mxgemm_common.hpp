@@ -44,6 +44,15 @@ struct Params {
   int ksteps;  // ceil(K / 128)
   int num_tiles;   // L * tilesM * tilesN (the host keeps it below 2^31)
   int xcd_remap;  // 1 when gridDim.x is a multiple of 8
+  // projection epilogue only (C type 4): per-head RoPE and dual-direction
+  // MXFP8 of C in place of storing it
+  const uint16_t* rope_cos;  // (M, qk_rope) bf16 bits
+  const uint16_t* rope_sin;  // (M, qk_rope) bf16 bits
+  uint8_t* row_codes;        // (M, N) E4M3, blocks of 32 along N
+  uint8_t* row_scales;       // (M, N / 32) E8M0
+  uint8_t* col_codes;        // (M, N) E4M3, blocks of 32 along M
+  uint8_t* col_scales;       // (M / 32, N) E8M0
+  int head_dim, qk_rope;
 };
 
 // --- tile scheduling ---------------------------------------------------------
@@ -215,8 +224,9 @@ __device__ __forceinline__ v8bf cvt8(unsigned w0, unsigned w1, float scale) {
 }
 
 // C element type and layout, a kernel template parameter CT: 0 float32,
-// 1 bfloat16, 2 float16, all n-major (L, M, N); 3 float32 m-major (L, N, M)
-// (256x256 kernel only).  The accumulators are float32 either way; a 16-bit C
+// 1 bfloat16, 2 float16, all n-major (L, M, N); 3 float32 m-major (L, N, M);
+// 4: no C -- the projection epilogue (RoPE and dual-direction MXFP8 codes of
+// the float32 accumulators).  The accumulators are float32 either way; a 16-bit C
 // receives them rounded to nearest even (v_cvt_pk_bf16_f32 /
 // v_cvt_pk_f16_f32), and the amax is taken over the float32 values.
 template <int CT>

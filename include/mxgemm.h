@@ -289,6 +289,57 @@ int mxgemm_sf_rowwise_to_atoms(const uint8_t* rowwise, uint8_t* SF, int64_t MN, 
                                int sf_vec_size, void* stream);
 
 /*
+ * mxgemm_gemm_rope_mxfp8 -- the projection of "GEMM + RoPE + MXFP8
+ * Projection (SM100)" (sections "Overview", "Shapes", "Equations") in one
+ * kernel: Y = A B^T as in mxgemm_amax (L = 1; A (tokens, K) and B (N, K)
+ * codes, N = num_heads * head_dim, SF atoms as there), and in place of
+ * storing Y, per head: RoPE on the trailing qk_rope features (the rule of
+ * mxgemm_proj_rope_mxfp8 below) and E4M3 codes with E8M0 scales in both
+ * block directions, exactly what mxgemm_proj_rope_mxfp8 makes of the
+ * float32 Y that mxgemm_amax (with 256x256 tiles) computes for these
+ * operands.  No Y and no Amax is written.
+ *   cos_bf16, sin_bf16 : (tokens, qk_rope) bf16 bits.
+ *   row_codes (tokens, N) bytes, row_scales (tokens, N / 32),
+ *   col_codes (tokens, N), col_scales (tokens / 32, N): caller-owned outputs.
+ * Requirements: K > 0 and the GEMM's rules on K; tokens % 32 == 0
+ * (MXG_ERR_ALIGN); head_dim a multiple of 32, at least 128; qk_rope a
+ * multiple of 16, at most 64; N % 128 == 0; no head's rotary features
+ * crossing a multiple of 128 columns (else MXG_ERR_SHAPE); a_fmt, b_fmt
+ * E4M3 or E5M2; sf_vec_size 16 or 32; every pointer 16-byte aligned.
+ * Asynchronous on `stream`; errors before any work; tokens or num_heads == 0
+ * queues nothing.
+ */
+int mxgemm_gemm_rope_mxfp8(const void* A, const void* B, const uint8_t* SFA, const uint8_t* SFB,
+                           const uint16_t* cos_bf16, const uint16_t* sin_bf16, uint8_t* row_codes,
+                           uint8_t* row_scales, uint8_t* col_codes, uint8_t* col_scales, int64_t tokens,
+                           int64_t num_heads, int64_t head_dim, int64_t qk_rope, int64_t K, int sf_vec_size, int a_fmt,
+                           int b_fmt, void* stream);
+
+/*
+ * mxgemm_projection_workspace_bytes -- bytes of workspace that
+ * mxgemm_projection_mxfp8 needs: the atom-layout scales of x and w
+ * (mxgemm_sf_bytes of each, the first rounded up to 256).
+ */
+size_t mxgemm_projection_workspace_bytes(int64_t tokens, int64_t num_heads, int64_t head_dim, int64_t K);
+
+/*
+ * mxgemm_projection_mxfp8 -- the projection page's MXFP8-input path as the
+ * page passes it: x (tokens, K) and w (num_heads * head_dim, K) E4M3 codes
+ * with row-wise E8M0 scales x_scale (tokens, ceil(K/32)) and w_scale
+ * (num_heads * head_dim, ceil(K/32)) ("Shapes": blocks of 32 along Q_LORA).
+ * The scales are rewritten into the atom layout in `workspace` (device
+ * memory of at least mxgemm_projection_workspace_bytes, 256-byte aligned,
+ * caller-owned, overwritten), then mxgemm_gemm_rope_mxfp8 runs with
+ * sf_vec_size 32.  Rules, outputs and errors as there; a short workspace is
+ * MXG_ERR_SHAPE.  Three kernels on `stream`.
+ */
+int mxgemm_projection_mxfp8(const void* x, const void* w, const uint8_t* x_scale, const uint8_t* w_scale,
+                            const uint16_t* cos_bf16, const uint16_t* sin_bf16, uint8_t* row_codes,
+                            uint8_t* row_scales, uint8_t* col_codes, uint8_t* col_scales, int64_t tokens,
+                            int64_t num_heads, int64_t head_dim, int64_t qk_rope, int64_t K, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
  * mxgemm_codes_to_kmajor -- m-major (or n-major) 8-bit element codes into the
  * k-major rows mxgemm_amax reads ("GEMM + Amax (SM100)", section
  * "Parameters": A of shape (M, K, L) may have strides (1, M, M*K), B of shape
