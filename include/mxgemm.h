@@ -99,10 +99,11 @@ enum {
      heavy-tailed data.  The default path dequantises each element exactly
      to bf16 (scale folded in) and accumulates in fp32 on the bf16 MFMA. */
   MXG_FLAG_FP8_MFMA = 2u,
-  /* Force the tile configuration instead of the automatic choice (for tests
-     and tuning; results agree within the tolerance either way).  TILE_128:
-     128x128 tiles, two workgroups per CU.  TILE_256: 256x256 tiles, one
-     workgroup per CU; ignored when K == 0.  Setting both is an error. */
+  /* Force the tile size instead of the automatic choice (for tests and
+     tuning).  TILE_128: 128x128 tiles; TILE_256: 256x256 tiles; one
+     workgroup of 4 waves per CU either way.  Both sizes compute every
+     output the same way, so results agree bit for bit.  Ignored when K == 0.
+     Setting both is an error. */
   MXG_FLAG_TILE_128 = 4u,
   MXG_FLAG_TILE_256 = 8u,
   /* A 16-bit C ("GEMM + Amax (SM100)", section "Parameters": the C tensor
@@ -119,9 +120,8 @@ enum {
      (M, N, L) with strides (1, M, M*N), the wrapper's c_major="m"): C then
      holds (L, N, M) float32 elements, M contiguous.  The contiguous dimension
      must be 16-byte aligned, so M % 4 == 0 as well (MXG_ERR_ALIGN otherwise).
-     Runs on the 256x256 kernel (the default datapath, float32 C only):
-     not with MXG_FLAG_FP8_MFMA, MXG_FLAG_C_BF16 / _F16 or, when K > 0,
-     MXG_FLAG_TILE_128 (MXG_ERR_FLAGS). */
+     The default datapath with a float32 C only: not with MXG_FLAG_FP8_MFMA
+     or MXG_FLAG_C_BF16 / _F16 (MXG_ERR_FLAGS). */
   MXG_FLAG_C_MMAJOR = 128u
 };
 
