@@ -44,12 +44,14 @@ MXG_ERR_FMT = -5
 MXG_ERR_DEVICE = -6
 MXG_ERR_LAUNCH = -7
 MXG_ERR_FLAGS = -8
+MXG_ERR_SCRATCH = -9
+MXGEMM_NOALLOC_SCRATCH_BYTES = 8 << 20  # fixed per-device scratch of the _noalloc entry
 
 EXPORTED = ("mxgemm_amax", "mxgemm_amax_ex", "mxgemm_amax_reset", "mxgemm_check_support",
             "mxgemm_sf_bytes", "mxgemm_launch_config", "mxgemm_strerror", "mxgemm_mx_quantize",
             "mxgemm_sf_rowwise_to_atoms", "mxgemm_plan_init", "mxgemm_plan_execute", "mxgemm_codes_to_kmajor",
             "mxgemm_proj_rope_mxfp8", "mxgemm_gemm_rope_mxfp8", "mxgemm_projection_workspace_bytes",
-            "mxgemm_projection_mxfp8")
+            "mxgemm_projection_mxfp8", "mxgemm_projection_mxfp8_noalloc")
 
 
 class MxgemmError(Exception):
@@ -107,6 +109,8 @@ def _load():
     lib.mxgemm_projection_workspace_bytes.restype = ctypes.c_size_t
     lib.mxgemm_projection_mxfp8.argtypes = [vp] * 10 + [i64] * 5 + [vp, ctypes.c_size_t, vp]
     lib.mxgemm_projection_mxfp8.restype = ci
+    lib.mxgemm_projection_mxfp8_noalloc.argtypes = [vp] * 10 + [i64] * 5 + [vp]
+    lib.mxgemm_projection_mxfp8_noalloc.restype = ci
     return lib
 
 
@@ -292,6 +296,21 @@ def projection_mxfp8(x, w, x_scale, w_scale, cos, sin, num_heads, head_dim=192, 
     return out
 
 
+def projection_mxfp8_noalloc(x, w, x_scale, w_scale, cos, sin, num_heads, head_dim=192, qk_rope=64,
+                             stream=None, out=None):
+    """C-ABI mxgemm_projection_mxfp8_noalloc: projection_mxfp8 with the workspace taken from the library's
+    fixed per-device scratch array (nothing is allocated; `out` must then be given by a caller that cannot
+    allocate either).  Calls that overlap on one device race."""
+    tokens, k = x.shape
+    out = _proj_outputs(tokens, num_heads, head_dim, x.device, out)
+    st = _lib.mxgemm_projection_mxfp8_noalloc(_ptr(x), _ptr(w), _ptr(x_scale), _ptr(w_scale), _ptr(cos),
+                                              _ptr(sin), _ptr(out[0]), _ptr(out[1]), _ptr(out[2]), _ptr(out[3]),
+                                              tokens, num_heads, head_dim, qk_rope, k, _stream(stream))
+    if st != MXG_OK:
+        _raise(st)
+    return out
+
+
 def codes_to_kmajor(src, dst, MN, K, L, stream=None):
     """C-ABI mxgemm_codes_to_kmajor: (L, K, MN) codes into (L, MN, K); raises on a nonzero status."""
     st = _lib.mxgemm_codes_to_kmajor(_ptr(src), _ptr(dst), MN, K, L, _stream(stream))
@@ -444,6 +463,7 @@ __all__ = [
     "mxgemm_mx_quantize", "mx_quantize", "mxgemm_sf_rowwise_to_atoms", "sf_from_rowwise", "Plan",
     "MXG_FMT_E4M3", "MXG_FMT_E5M2", "MXG_FMT_E2M1", "MXG_FLAG_AMAX_ACCUMULATE", "MXG_FLAG_FP8_MFMA", "MXG_FLAG_TILE_128",
     "MXG_FLAG_TILE_256", "MXG_FLAG_C_BF16", "MXG_FLAG_C_F16", "MXG_FLAG_C_MMAJOR", "codes_to_kmajor",
-    "proj_rope_mxfp8", "gemm_rope_mxfp8", "projection_mxfp8", "MxgemmError", "MxgemmValueError",
+    "proj_rope_mxfp8", "gemm_rope_mxfp8", "projection_mxfp8", "projection_mxfp8_noalloc", "MxgemmError",
+    "MxgemmValueError",
     "MxgemmRuntimeError",
 ]

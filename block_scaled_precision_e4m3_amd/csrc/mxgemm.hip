@@ -20,6 +20,12 @@
 
 namespace mxg {
 
+// The workspace of mxgemm_projection_mxfp8_noalloc: one array per device,
+// reserved with the library's code object.  Host code never uses its name as
+// an address (that is a host-side stand-in); the device address comes from
+// hipGetSymbolAddress, once per device (scratch_address below).
+static __device__ __align__(256) uint8_t scratch[MXGEMM_NOALLOC_SCRATCH_BYTES];
+
 // Clears the Amax bits (queued before a GEMM that does not accumulate).
 __global__ void amax_reset_kernel(unsigned* amax_bits) {
   if (threadIdx.x == 0) *amax_bits = 0u;
@@ -97,6 +103,24 @@ int device_check(int* dev_out, int* cus) {
   *dev_out = dev;
   *cus = d.cus;
   return MXG_OK;
+}
+
+// Device address of `scratch` on device `dev` (current), looked up on the
+// first call on that device and kept; nullptr if HIP cannot give it.
+void* g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+void* scratch_address(int dev) {
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(mxg::scratch)) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
 }
 
 // Device memory of `dev` (or managed memory) is accepted; host memory is not.
@@ -671,6 +695,34 @@ int mxgemm_projection_mxfp8(const void* x, const void* w, const uint8_t* x_scale
                         (hipStream_t)stream);
 }
 
+int mxgemm_projection_mxfp8_noalloc(const void* x, const void* w, const uint8_t* x_scale, const uint8_t* w_scale,
+                                    const uint16_t* cos_bf16, const uint16_t* sin_bf16, uint8_t* row_codes,
+                                    uint8_t* row_scales, uint8_t* col_codes, uint8_t* col_scales, int64_t tokens,
+                                    int64_t num_heads, int64_t head_dim, int64_t qk_rope, int64_t K, void* stream) {
+  int st = check_projection(tokens, num_heads, head_dim, qk_rope, K, 32, MXG_FMT_E4M3, MXG_FMT_E4M3);
+  if (st != MXG_OK) return st;
+  if (projection_ws_bytes(tokens, num_heads * head_dim, K, 32) > (size_t)MXGEMM_NOALLOC_SCRATCH_BYTES)
+    return MXG_ERR_SCRATCH;
+  if (tokens == 0 || num_heads == 0) return MXG_OK;
+  if (!x || !w || !x_scale || !w_scale || !row_codes || !row_scales || !col_codes || !col_scales ||
+      (qk_rope > 0 && (!cos_bf16 || !sin_bf16)))
+    return MXG_ERR_NULL;
+  if (!aligned16_all({x, w, row_codes, row_scales, col_codes, col_scales}) ||
+      (qk_rope > 0 && !aligned16_all({cos_bf16, sin_bf16})))
+    return MXG_ERR_ALIGN;
+  int dev = 0, cus = 0;
+  st = device_check(&dev, &cus);
+  if (st != MXG_OK) return st;
+  for (const void* q : {x, w, (const void*)x_scale, (const void*)w_scale, (const void*)row_codes,
+                        (const void*)row_scales, (const void*)col_codes, (const void*)col_scales})
+    if (!on_device(q, dev)) return MXG_ERR_DEVICE;
+  if (qk_rope > 0 && (!on_device(cos_bf16, dev) || !on_device(sin_bf16, dev))) return MXG_ERR_DEVICE;
+  uint8_t* ws = static_cast<uint8_t*>(scratch_address(dev));
+  if (!ws) return MXG_ERR_DEVICE;
+  return run_projection(x, w, x_scale, w_scale, cos_bf16, sin_bf16, row_codes, row_scales, col_codes, col_scales,
+                        tokens, num_heads, head_dim, qk_rope, K, ws, cus, (hipStream_t)stream);
+}
+
 int mxgemm_amax(const void* A, const void* B, const uint8_t* SFA, const uint8_t* SFB, float* C, float* Amax,
                 int64_t M, int64_t N, int64_t K, int64_t L, int sf_vec_size, int a_fmt, int b_fmt, void* stream) {
   return mxgemm_amax_ex(A, B, SFA, SFB, C, Amax, M, N, K, L, sf_vec_size, a_fmt, b_fmt, 0u, stream);
@@ -687,6 +739,7 @@ const char* mxgemm_strerror(int status) {
     case MXG_ERR_DEVICE: return "current device is not gfx950, or a buffer is not memory of the current device";
     case MXG_ERR_LAUNCH: return "HIP kernel launch failed";
     case MXG_ERR_FLAGS: return "unknown flag bit";
+    case MXG_ERR_SCRATCH: return "the problem needs more scratch than the library's fixed scratch array holds";
     default: return "unknown status";
   }
 }

@@ -83,7 +83,9 @@ enum {
   MXG_ERR_DEVICE = -6, /* current device is not gfx950, or a pointer is not
                           device memory of the current device                 */
   MXG_ERR_LAUNCH = -7, /* HIP reported an error when launching                */
-  MXG_ERR_FLAGS = -8   /* unknown bit in `flags`                              */
+  MXG_ERR_FLAGS = -8,  /* unknown bit in `flags`                              */
+  MXG_ERR_SCRATCH = -9 /* the problem needs more scratch than the library's
+                          fixed scratch array holds (the _noalloc entry)      */
 };
 
 /* flags of mxgemm_amax_ex */
@@ -338,6 +340,26 @@ int mxgemm_projection_mxfp8(const void* x, const void* w, const uint8_t* x_scale
                             uint8_t* row_scales, uint8_t* col_codes, uint8_t* col_scales, int64_t tokens,
                             int64_t num_heads, int64_t head_dim, int64_t qk_rope, int64_t K, void* workspace,
                             size_t workspace_bytes, void* stream);
+
+/*
+ * mxgemm_projection_mxfp8_noalloc -- mxgemm_projection_mxfp8 for callers that
+ * cannot allocate device memory (code under graph capture, tight serving
+ * loops, harnesses that forbid it): the same operation, arguments and
+ * results, with the workspace taken from a fixed array inside the library
+ * (MXGEMM_NOALLOC_SCRATCH_BYTES per device, reserved when the library is
+ * loaded and held until the process ends) instead of a caller buffer.  It
+ * calls no allocator.  A problem whose workspace
+ * (mxgemm_projection_workspace_bytes) exceeds the array is rejected with
+ * MXG_ERR_SCRATCH before any work.  Every call on one device shares that
+ * device's array: calls that may overlap on one device (other streams,
+ * other threads) race and must be serialised by the caller.  The array's
+ * contents are overwritten in full by each call before they are read.
+ */
+#define MXGEMM_NOALLOC_SCRATCH_BYTES (8u << 20)
+int mxgemm_projection_mxfp8_noalloc(const void* x, const void* w, const uint8_t* x_scale, const uint8_t* w_scale,
+                                    const uint16_t* cos_bf16, const uint16_t* sin_bf16, uint8_t* row_codes,
+                                    uint8_t* row_scales, uint8_t* col_codes, uint8_t* col_scales, int64_t tokens,
+                                    int64_t num_heads, int64_t head_dim, int64_t qk_rope, int64_t K, void* stream);
 
 /*
  * mxgemm_codes_to_kmajor -- m-major (or n-major) 8-bit element codes into the

@@ -47,6 +47,8 @@ def test_status_codes_match_header(lib):
     text = open(HEADER).read()
     for name, val in re.findall(r"\b(MXG_\w+)\s*=\s*(-?\d+)", text):
         assert getattr(lib, name) == int(val), name
+    m = re.search(r"#define MXGEMM_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and lib.MXGEMM_NOALLOC_SCRATCH_BYTES == int(m.group(1)) << int(m.group(2))
 
 
 def test_check_support(lib):
@@ -207,3 +209,44 @@ def test_plan_validation_before_device_work(lib):
     good = 0x7F0000000000
     assert ex(zero, good, good, good, good, good, good, None) == lib.MXG_ERR_NULL
     assert ex(None, good, good, good, good, good, good, None) == lib.MXG_ERR_NULL
+
+
+def test_projection_errors_before_device_work(lib):
+    c = ctypes.CDLL(lib.LIB_PATH)
+    vp, i64, ci, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    wsb = c.mxgemm_projection_workspace_bytes
+    wsb.argtypes = [i64] * 4
+    wsb.restype = sz
+    ws_call = c.mxgemm_projection_mxfp8
+    ws_call.argtypes = [vp] * 10 + [i64] * 5 + [vp, sz, vp]
+    ws_call.restype = ci
+    na = c.mxgemm_projection_mxfp8_noalloc
+    na.argtypes = [vp] * 10 + [i64] * 5 + [vp]
+    na.restype = ci
+    good = 0x7F0000000000
+    ptrs = [good] * 10
+    # workspace = x's atoms (rounded up to 256 bytes) + w's atoms, 512 bytes per 128 rows x 128 K
+    assert wsb(4096, 128, 192, 1536) == 512 * 32 * 12 + 512 * 192 * 12
+    assert wsb(96, 4, 192, 160) == 512 * 1 * 2 + 512 * 6 * 2
+    assert wsb(-1, 4, 192, 160) == 0
+    # the fixed scratch of the allocation-free entry: the largest problem that fits is accepted by the
+    # size check (and reaches the pointer checks), one that does not is refused before any device call
+    cap = lib.MXGEMM_NOALLOC_SCRATCH_BYTES
+    assert wsb(4096, 128, 192, 7168) <= cap
+    assert na(*([None] * 10), 4096, 128, 192, 64, 7168, None) == lib.MXG_ERR_NULL
+    assert wsb(16384, 128, 192, 7168) > cap
+    assert na(*ptrs, 16384, 128, 192, 64, 7168, None) == lib.MXG_ERR_SCRATCH
+    assert na(*([None] * 10), 16384, 128, 192, 64, 7168, None) == lib.MXG_ERR_SCRATCH
+    # shape rules shared by both entries come first
+    for bad in ((96, 4, 100, 64, 160), (96, 4, 192, 72, 160), (100, 4, 192, 64, 160), (96, 4, 192, 64, 0)):
+        st = na(*ptrs, *bad, None)
+        assert st in (lib.MXG_ERR_SHAPE, lib.MXG_ERR_ALIGN), bad
+        assert ws_call(*ptrs, *bad, good, 1 << 20, None) == st, bad
+    # empty problems need no pointers
+    assert na(*([None] * 10), 0, 4, 192, 64, 160, None) == lib.MXG_OK
+    assert ws_call(*([None] * 10), 0, 4, 192, 64, 160, None, 0, None) == lib.MXG_OK
+    # a short or misaligned caller workspace
+    need = wsb(96, 4, 192, 160)
+    assert ws_call(*ptrs, 96, 4, 192, 64, 160, good, need - 1, None) == lib.MXG_ERR_SHAPE
+    assert ws_call(*ptrs, 96, 4, 192, 64, 160, good + 16, need, None) == lib.MXG_ERR_ALIGN
+    assert ws_call(*ptrs, 96, 4, 192, 64, 160, None, need, None) == lib.MXG_ERR_NULL
