@@ -35,6 +35,7 @@ if ROOT not in sys.path:
 # Published MI355X dense matrix peaks (TFLOP/s)
 PEAK_BF16 = 2500.0
 PEAK_FP8 = 5000.0
+SCLK_PEAK_MHZ = 2400.0  # the engine clock the published MFMA peaks are quoted at
 HBM_GBS = 8000.0
 
 CSRC = os.path.join(ROOT, "block_scaled_precision_e4m3_amd", "csrc")
@@ -57,11 +58,11 @@ def profile_name(workload_name, fp8_mfma, op="gemm"):
     if op == "quantize":
         return f"mx_quantize_kernel__{workload_name}_operands.txt"
     if op == "proj":
-        return f"proj_rope_mxfp8_kernel__{workload_name}_pipeline.txt"
-    return f"mxgemm_amax_kernel_{'fp8' if fp8_mfma else 'bf16'}__{workload_name}.txt"
+        return f"mxgemm_amax_big_kernel_projection_epilogue__{workload_name}_pipeline.txt"
+    return f"mxgemm_amax_big_kernel_{'fp8' if fp8_mfma else 'bf16'}__{workload_name}.txt"
 
 
-def read_traffic(workload_name, fp8_mfma, op="gemm"):
+def read_traffic(workload_name, fp8_mfma, op="gemm", key="traffic_bytes_per_launch"):
     """HBM bytes per launch from the committed counter summary, or None if absent or taken on other sources."""
     path = os.path.join(PROFILES, profile_name(workload_name, fp8_mfma, op))
     if not os.path.exists(path):
@@ -72,9 +73,50 @@ def read_traffic(workload_name, fp8_mfma, op="gemm"):
             m = re.match(r"^([a-z_0-9]+):\s*(\S+)\s*$", line)
             if m:
                 kv[m.group(1)] = m.group(2)
-    if kv.get("kernel_source_sha256") != kernel_source_hash() or "traffic_bytes_per_launch" not in kv:
+    if kv.get("kernel_source_sha256") != kernel_source_hash() or key not in kv:
         return None
-    return int(kv["traffic_bytes_per_launch"])
+    return int(kv[key])
+
+
+def sustained_clock(step, seconds=1.5):
+    """Median engine clock (MHz) that rocm-smi reports while `step` runs back to back for `seconds`
+    (the clock the chip holds under this load; the MFMA peaks are quoted at 2400 MHz), or None."""
+    import shutil
+    import subprocess
+    import threading
+
+    import torch
+    smi = shutil.which("rocm-smi") or "/opt/rocm/bin/rocm-smi"
+    if not os.path.exists(smi):
+        return None
+    samples, stop = [], threading.Event()
+
+    def sample():
+        while not stop.is_set():
+            r = subprocess.run([smi, "--showclocks", "--json"], capture_output=True, text=True)
+            try:
+                card = json.loads(r.stdout)
+                card = card[sorted(card)[0]]
+                for k, v in card.items():
+                    if k.startswith("sclk clock speed"):
+                        samples.append(int(re.findall(r"(\d+)Mhz", str(v))[0]))
+            except (ValueError, KeyError, IndexError):
+                pass
+            time.sleep(0.1)
+    for _ in range(20):  # reach the steady state before sampling
+        step()
+    torch.cuda.synchronize()
+    th = threading.Thread(target=sample)
+    th.start()
+    t0 = time.time()
+    while time.time() - t0 < seconds:
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    samples = samples[1:] if len(samples) > 2 else samples  # the first may precede the load
+    return sorted(samples)[len(samples) // 2] if samples else None
 
 
 def copy_probe():
@@ -98,7 +140,13 @@ def _csv_rows(pattern):
 
 
 def _is_gemm(name):
-    return "mxgemm_amax" in name and "reset" not in name
+    return "mxgemm_amax" in name and "reset" not in name and not _is_fused_proj(name)
+
+
+def _is_fused_proj(name):
+    # the tile kernel instantiated with the projection epilogue (C type 4, 256x256 tiles), by its
+    # demangled or mangled name
+    return "mxgemm_amax_big_kernel" in name and (", 4, 256>" in name or "ELi4ELi256E" in name)
 
 
 def _is_quantize(name):
@@ -165,10 +213,10 @@ def rocprof_summary(d, workload, fp8_mfma, commands, op="gemm"):
                f"stacked as one ({ql}, {qmn}, {qk}) tensor (A's {M} rows, then B's {N}), sf={qsf}, E4M3", ""]
         is_target = _is_quantize
     elif op == "proj":
-        out = [f"# rocprofv3 summary: the RoPE + dual-direction MXFP8 kernel of the projection pipeline, "
-               f"workload {cfg['name']} (tokens={M}, {PROJ_HEADS} heads x {PROJ_HEAD_DIM}, "
-               f"{PROJ_QK_ROPE} rotary features)", ""]
-        is_target = _is_proj_rope
+        out = [f"# rocprofv3 summary: the projection pipeline of workload {cfg['name']} (tokens={M}, "
+               f"{PROJ_HEADS} heads x {PROJ_HEAD_DIM}, {PROJ_QK_ROPE} rotary features, K={K}): the GEMM with the "
+               f"RoPE + dual-direction MXFP8 epilogue (fused), and the unfused pipeline's RoPE + MXFP8 kernel", ""]
+        is_target = _is_fused_proj
     else:
         out = [f"# rocprofv3 summary: the GEMM + amax kernel ({'fp8 MFMA' if fp8_mfma else 'bf16 MFMA'} path), "
                f"workload {cfg['name']} (M={M} N={N} K={K} L={L} sf={sf})", ""]
@@ -190,10 +238,21 @@ def rocprof_summary(d, workload, fp8_mfma, commands, op="gemm"):
             gemm_name, gemm_total = name, float(r["TotalDurationNs"])
             avg_us = float(r["AverageNs"]) / 1e3
     out.append("")
+    rope_name, rope_us = None, None
+    if op == "proj":
+        for r in stats:
+            if _is_proj_rope(r["Name"]):
+                rope_name, rope_us = r["Name"], float(r["AverageNs"]) / 1e3
     if avg_us and op == "proj":
-        out.append(f"kernel: {gemm_name}")
-        out.append(f"avg_duration_us: {avg_us:.2f}")
-        out.append(f"algorithmic_GBps_at_avg_duration: {proj_rope_bytes(M, N, PROJ_QK_ROPE) / (avg_us * 1e-6) / 1e9:.1f}")
+        fl = W.flops(M, N, K, L)
+        out.append(f"gemm_kernel: {gemm_name}")
+        out.append(f"gemm_avg_duration_us: {avg_us:.2f}")
+        out.append(f"gemm_tflops_at_avg_duration: {fl / (avg_us * 1e-6) / 1e12:.1f}")
+        if rope_us:
+            out.append(f"rope_kernel: {rope_name}")
+            out.append(f"rope_avg_duration_us: {rope_us:.2f}")
+            out.append(f"rope_algorithmic_GBps_at_avg_duration: "
+                       f"{proj_rope_bytes(M, N, PROJ_QK_ROPE) / (rope_us * 1e-6) / 1e9:.1f}")
     elif avg_us and op == "quantize":
         out.append(f"kernel: {gemm_name}")
         out.append(f"avg_duration_us: {avg_us:.2f}")
@@ -216,7 +275,7 @@ def rocprof_summary(d, workload, fp8_mfma, commands, op="gemm"):
         fb = sum(gf) / len(gf) * 1024.0 * f_fac
         wb = sum(gw) / len(gw) * 1024.0 * w_fac
         ab = (quantize_bytes(qmn, qk, ql, qsf) if op == "quantize" else
-              proj_rope_bytes(M, N, PROJ_QK_ROPE) if op == "proj" else W.algorithmic_bytes(M, N, K, L, sf))
+              proj_fused_bytes(M, N, K, sf) if op == "proj" else W.algorithmic_bytes(M, N, K, L, sf))
         out += ["",
                 "HBM traffic (--pmc FETCH_SIZE, then --pmc WRITE_SIZE; KiB per dispatch):",
                 f"  kernel FETCH_SIZE per dispatch (KiB, mean of {len(gf)}): {sum(gf) / len(gf):.0f}",
@@ -229,6 +288,16 @@ def rocprof_summary(d, workload, fp8_mfma, commands, op="gemm"):
                 f"traffic_bytes_per_launch: {fb + wb:.0f}",
                 f"algorithmic_bytes_per_launch: {ab}",
                 f"traffic_over_algorithmic: {(fb + wb) / ab:.3f}"]
+        if op == "proj" and rope_name:
+            rf = _per_dispatch(fetch, rope_name, "FETCH_SIZE", kernel_name_exact=True)
+            rw = _per_dispatch(write, rope_name, "WRITE_SIZE", kernel_name_exact=True)
+            if rf and rw:
+                rfb = sum(rf) / len(rf) * 1024.0 * f_fac
+                rwb = sum(rw) / len(rw) * 1024.0 * w_fac
+                rab = proj_rope_bytes(M, N, PROJ_QK_ROPE)
+                out += [f"rope_traffic_bytes_per_launch: {rfb + rwb:.0f}",
+                        f"rope_algorithmic_bytes_per_launch: {rab}",
+                        f"rope_traffic_over_algorithmic: {(rfb + rwb) / rab:.3f}"]
     out += ["", f"kernel_source_sha256: {kernel_source_hash()}"]
     bench_line = os.path.join(d, "bench.json")
     if os.path.exists(bench_line):
@@ -540,11 +609,12 @@ def bench_proj(args):
                      "frac": round(flops / (fused_ms * 1e-3) / 1e12 / PEAK_FP8, 4),
                      "peak_of_datapath": PEAK_BF16,
                      "frac_of_datapath_peak": round(flops / (fused_ms * 1e-3) / 1e12 / PEAK_BF16, 4),
-                     "traffic": None,
+                     "traffic": read_traffic(W.WORKLOADS[5]["name"], False, "proj"),
                      "algorithmic_bytes": proj_fused_bytes(tokens, n, k, sf)},
         "unfused_rope_kernel_roofline": {"bound": "hbm", "achieved": round(rope_gbs, 1), "peak": HBM_GBS,
                                          "unit": "GB/s", "frac": round(rope_gbs / HBM_GBS, 4),
-                                         "traffic": read_traffic(W.WORKLOADS[5]["name"], False, "proj"),
+                                         "traffic": read_traffic(W.WORKLOADS[5]["name"], False, "proj",
+                                                                 "rope_traffic_bytes_per_launch"),
                                          "algorithmic_bytes": rope_bytes},
     }
     if args.copy_probe:
@@ -668,6 +738,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-host-overhead", action="store_true",
                     help="skip the 1000 small calls that time the host side (keeps profiles to the workload)")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the sustained-clock reading (1.5 s of back-to-back steps under rocm-smi)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the timed steps, run the copy kernel that calibrates the HBM byte counters")
     ap.add_argument("--rocprof-summary", metavar="DIR",
@@ -807,6 +879,14 @@ def main():
     }
     if args.sf_rowwise:
         out["repack_ms"] = round(sum(a.elapsed_time(b) for a, b in rp_ev) / args.steps, 4)
+    if not args.no_clock:
+        mhz = sustained_clock(step)
+        if mhz:
+            dp = PEAK_FP8 if args.fp8_mfma else PEAK_BF16
+            out["clock"] = {"sclk_mhz_sustained": mhz, "sclk_mhz_of_peaks": SCLK_PEAK_MHZ,
+                            "datapath_peak_at_sustained_clock": round(dp * mhz / SCLK_PEAK_MHZ, 1),
+                            "frac_of_datapath_peak_at_sustained_clock": round(achieved / (dp * mhz / SCLK_PEAK_MHZ), 4),
+                            "what": "engine clock rocm-smi reports while the step runs back to back for 1.5 s"}
     if not args.no_host_overhead:
         out["host_overhead"] = host_overhead(lib, A, B, SFA, SFB, C, Amax, sh, p["a_fmt"], p["b_fmt"], sf)
     if args.copy_probe:
