@@ -28,9 +28,10 @@ hipError_t launch_fp8(const Params& p, int sf, int fa, int fb, int bt, int64_t g
 template <typename Launch>
 hipError_t dispatch_formats(int sf, int fa, int fb, Launch&& launch) {
   if (fa == 2 || fb == 2) {
-    if (fa == 2 && fb == 2 && sf == 32) return launch(std::integral_constant<int, 32>{}, std::integral_constant<int, 2>{},
-                                                      std::integral_constant<int, 2>{});
-    return hipErrorInvalidValue;
+    if (fa != 2 || fb != 2) return hipErrorInvalidValue;
+    if (sf == 32)
+      return launch(std::integral_constant<int, 32>{}, std::integral_constant<int, 2>{}, std::integral_constant<int, 2>{});
+    return launch(std::integral_constant<int, 16>{}, std::integral_constant<int, 2>{}, std::integral_constant<int, 2>{});
   }
 #define MXG_DISPATCH(SF)                                                                                         \
   if (fa == 0 && fb == 0) return launch(std::integral_constant<int, SF>{}, std::integral_constant<int, 0>{},     \

@@ -65,7 +65,6 @@ int check_sizes(int64_t M, int64_t N, int64_t K, int64_t L, int sf, int a_fmt, i
   if (!known(a_fmt) || !known(b_fmt)) return MXG_ERR_FMT;
   const bool fp4 = a_fmt == MXG_FMT_E2M1;
   if (fp4 != (b_fmt == MXG_FMT_E2M1)) return MXG_ERR_FMT;  // packed FP4 on both operands or neither
-  if (fp4 && sf != 32) return MXG_ERR_SFVEC;                // FP4: one E8M0 scale per 32 elements
   // kernel indices are 32-bit per dimension, byte offsets 64-bit
   if (!fits_i32(M) || !fits_i32(N) || !fits_i32(K) || !fits_i32(L)) return MXG_ERR_SHAPE;
   const int64_t lim = INT64_MAX / 8;
@@ -214,6 +213,7 @@ void configure(Prepared* pr, int cus) {
   Config cfg = choose(M, N, K, L, cus);
   if (K > 0 && (pr->flags & MXG_FLAG_TILE_128)) cfg = kT128;
   if (K > 0 && (pr->flags & MXG_FLAG_TILE_256)) cfg = kT256;
+  if (K > 0 && fp4 && pr->sf == 16) cfg = kT128;  // four scale atoms per step fit the 128x128 tile's LDS only
   pr->kind = cfg.kind;
   p.tilesM = (int)cdiv(M, cfg.tile_m);
   p.tilesN = (int)cdiv(N, cfg.tile_n);
@@ -244,6 +244,7 @@ int prepare(Prepared* pr, int64_t M, int64_t N, int64_t K, int64_t L, int sf_vec
   if (c_flags & (c_flags - 1)) return MXG_ERR_FLAGS;        // both 16-bit C types
   if (c_flags && (flags & MXG_FLAG_FP8_MFMA)) return MXG_ERR_FLAGS;  // 16-bit C: bf16 datapath only
   if (a_fmt == MXG_FMT_E2M1 && (flags & MXG_FLAG_FP8_MFMA)) return MXG_ERR_FLAGS;  // FP4: bf16 datapath
+  if (a_fmt == MXG_FMT_E2M1 && sf_vec_size == 16 && (flags & MXG_FLAG_TILE_256)) return MXG_ERR_FLAGS;
   // m-major C: rows of C run along M, so M takes N's place in the 32-bit
   // per-tile store offsets (256 rows * M * 4 bytes)
   if (c_mmajor && M > (1LL << 22) - 4) return MXG_ERR_SHAPE;

@@ -76,8 +76,9 @@ struct Layout {
   // atom bytes per operand per stage: the atoms of both 128-row groups; for
   // a 128-row tile one kilobyte, which takes the one wave's scale DMA (one
   // group's NSF atoms, or with NSF = 1 its atom and the zeros its other half
-  // of the wave reads for a group past the tile)
-  static constexpr int kSF = BT == 256 ? 2 * NSF * 512 : 1024;
+  // of the wave reads for a group past the tile), or with NSF = 4 (FP4 at
+  // sf = 16) two kilobytes, the scale DMAs of two waves
+  static constexpr int kSF = BT == 256 ? 2 * NSF * 512 : (NSF == 4 ? 2048 : 1024);
   static constexpr int kOffB = kBM * kBK;            // A tile: BT rows x 128 bytes
   static constexpr int kOffSFA = kOffB + kBN * kBK;  // B tile: BT rows x 128 bytes
   static constexpr int kOffSFB = kOffSFA + kSF;
@@ -114,18 +115,21 @@ template <int SF, int FA, int FB, int MODE, int CT, int BT>
 __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) {
   // FA = FB = 2: packed FP4 (E2M1), bf16 datapath, sf = 32 (the host enforces it)
   constexpr bool kFp4 = FA == 2;
-  static_assert(!kFp4 || (FB == 2 && SF == 32 && MODE == kModeBf16), "FP4: both operands, sf = 32, bf16 path");
+  static_assert(!kFp4 || (FB == 2 && MODE == kModeBf16), "FP4: both operands, bf16 path");
+  static_assert(!(kFp4 && SF == 16) || (BT == 128 && CT != 4), "FP4 at sf = 16: 128x128 tiles (LDS)");
   static_assert(!kCMajorM<CT> || MODE == kModeBf16, "m-major C: bf16 path");
   static_assert(CT != 4 || (MODE == kModeBf16 && BT == 256), "projection epilogue: bf16 path, 256x256 tiles");
   // LDS ring stages: a 128x128 tile's steps are short, so its bf16 datapath
   // queues the DMA three steps ahead in four stages; a 256x256 tile's ring
   // fills the LDS with two
-  constexpr int kStages = (BT == 128 && MODE == kModeBf16) ? 4 : 2;
+  // (FP4 at sf = 16 carries four scale atoms per step and keeps two stages)
+  constexpr int kStages = (BT == 128 && MODE == kModeBf16 && !(kFp4 && SF == 16)) ? 4 : 2;
   using Y = Layout<SF, kFp4, BT, kStages>;
   constexpr int kBM = Y::kBM, kBN = Y::kBN;
   constexpr int kTM = BT / 64, kTN = BT / 64;  // 32x32 MFMA blocks per wave
   constexpr int kWM = kBM / 2, kWN = kBN / 2;  // wave tile rows and columns
-  static_assert(Y::NSF == 1 || Y::NSF == 2, "one or two scale atoms per 128-row group per step");
+  static_assert(Y::NSF == 1 || Y::NSF == 2 || (Y::NSF == 4 && BT == 128),
+                "one or two scale atoms per 128-row group per step, or four in a 128-row tile");
   constexpr int kEs = kCBytes<CT>;  // bytes per C element
   constexpr int NSF = Y::NSF;
   static_assert(Y::kLds <= 160 * 1024, "LDS");
@@ -168,8 +172,8 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
     g.row_k = (unsigned)(wave * 8 + dma_row) * (unsigned)p.Kbytes;
     g.kchunk = (unsigned)(((ln & 7) ^ dma_row ^ (wave & 1)) << 4);
     g.sf_lane = 16u * (unsigned)(ln & 31);
-    g.sf_rg = NSF == 1 ? (ln >> 5) : (wave >> 1);
-    g.sf_j = NSF == 1 ? 0 : (ln >> 5);
+    g.sf_rg = NSF == 1 ? (ln >> 5) : NSF == 4 ? 0 : (wave >> 1);
+    g.sf_j = NSF == 1 ? 0 : NSF == 4 ? 2 * (wave >> 1) + (ln >> 5) : (ln >> 5);
     return g;
   };
   auto lane_opaque = [&]() {
@@ -187,12 +191,13 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   // resources differ.  SF: sf=32 -> waves 0 and 1 load the A and B atoms of
   // both 128-row groups (lanes 0-31 group 0, 32-63 group 1); sf=16 (or FP4)
   // -> waves 0,1 (A,B) load row group 0's two atoms, waves 2,3 row group
-  // 1's (256-row tiles only).  Groups past the matrix or the tile read as
-  // zero.  Waves that load no atoms issue the same instruction on an empty
+  // 1's (256-row tiles only); four atoms per step (FP4 at sf=16, 128-row
+  // tiles) -> waves 0,1 (A,B) atoms 0 and 1, waves 2,3 atoms 2 and 3.  Groups
+  // past the matrix or the tile read as zero.  Waves that load no atoms issue the same instruction on an empty
   // resource into their own kilobyte of the dummy area (no branch in the
   // step).
   constexpr unsigned kOob = 0x80000000u;
-  const bool sf_wave = (NSF == 2 && BT == 256) || wave < 2;
+  const bool sf_wave = (NSF == 2 && BT == 256) || NSF == 4 || wave < 2;
   const bool sf_is_b = (wave & 1) != 0;
   struct Dma {
     __amdgpu_buffer_rsrc_t ra, rb, rs;
@@ -652,10 +657,13 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   };
   // chunk c's scale: one atom per step (8-bit, sf=32) -> block c (byte c);
   // two atoms (8-bit with sf=16, or FP4 with sf=32, whose 16-byte chunk holds
-  // 32 elements) -> block 2c+h, byte 2(c&1)+h of atom c>>1
-  auto scales = [&](const Geo& g, int c) __attribute__((always_inline)) {
-    const int j = NSF == 1 ? 0 : (c >> 1);
-    const unsigned k = NSF == 1 ? (unsigned)c : (unsigned)(2 * (c & 1) + g.h);
+  // 32 elements) -> block 2c+h, byte 2(c&1)+h of atom c>>1; four atoms (FP4
+  // with sf=16: a lane's 32 elements are two blocks, dwords 0-1 and 2-3) ->
+  // block 4c+2h+u for half u, byte 2h+u of atom c
+  auto scales = [&](const Geo& g, int c, int u) __attribute__((always_inline)) {
+    const int j = NSF == 1 ? 0 : NSF == 4 ? c : (c >> 1);
+    const unsigned k = NSF == 1 ? (unsigned)c
+                                : NSF == 4 ? (unsigned)(2 * g.h + u) : (unsigned)(2 * (c & 1) + g.h);
 #pragma unroll
     for (int i = 0; i < kTM; ++i) fa[i] = e8m0_byte_operand(sa[j][i], k);
 #pragma unroll
@@ -703,7 +711,7 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
     barrier();
     load_sf(g, lds, 0);
     load_raw(g, lds, 0);
-    scales(g, 0);
+    scales(g, 0, 0);
     convert(0);
   };
   // One K step of tile `cur`.  FIRST: the tile's first step (its first MFMA
@@ -748,11 +756,14 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
         }
       }
       if (n < kSlices - 1) {
-        if ((n + 1) % kSpc == 0) scales(g, (n + 1) / kSpc);
+        if ((n + 1) % kSpc == 0) scales(g, (n + 1) / kSpc, 0);
+        if constexpr (NSF == 4) {
+          if ((n + 1) % kSpc == 2) scales(g, (n + 1) / kSpc, 1);
+        }
         convert(n + 1);
       } else {
         // the next step's first slice (its inputs were read after B')
-        scales(g, 0);
+        scales(g, 0, 0);
         convert(0);
       }
 #pragma unroll
@@ -833,7 +844,7 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
     load_sf(g, lds, 0);
     load_raw(g, lds, 0);
     if constexpr (!kFp4) load_raw(g, lds, 1);
-    scales(g, 0);
+    scales(g, 0, 0);
     convert(0);
   };
   // One K step on the ring.  FIRST: the tile's first step (zero C operand on
@@ -875,10 +886,13 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
           if ((n - 1) * kPer1 + q < Y::kDma) dma_ab(d1, (n - 1) * kPer1 + q);
       }
       if (n < kSlices - 1) {
-        if ((n + 1) % kSpc == 0) scales(g, (n + 1) / kSpc);
+        if ((n + 1) % kSpc == 0) scales(g, (n + 1) / kSpc, 0);
+        if constexpr (NSF == 4) {
+          if ((n + 1) % kSpc == 2) scales(g, (n + 1) / kSpc, 1);
+        }
         convert(n + 1);
       } else {
-        scales(g, 0);
+        scales(g, 0, 0);
         convert(0);
       }
 #pragma unroll

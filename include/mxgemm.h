@@ -66,10 +66,15 @@ enum {
   MXG_FMT_E2M1 = 2  /* float4_e2m1fn_x2: packed FP4, two elements per byte,
                        element 2k in the low nibble; bias 1, no inf/NaN, max 6.
                        A is then (L, M, K/2) bytes and B (L, N, K/2).  Both
-                       operands must be E2M1, sf_vec_size 32, K % 32 == 0,
-                       and the default (bf16) datapath; the pages list the
-                       packed container ("Parameters", A dtype) but not
-                       which nibble comes first: low first is the reading. */
+                       operands must be E2M1, K % 32 == 0, and the default
+                       (bf16) datapath; sf_vec_size 32 or 16 (the pages
+                       exclude 16 only for 8-bit A/B, "Support surface and
+                       constraints", dtypes); at 16 the kernel runs 128x128
+                       tiles (the scale atoms of a 256x256 tile's step do
+                       not fit beside it in LDS), and MXG_FLAG_TILE_256 is
+                       MXG_ERR_FLAGS.  The pages list the packed container
+                       ("Parameters", A dtype) but not which nibble comes
+                       first: low first is the reading. */
 };
 
 /* status codes */
@@ -203,7 +208,8 @@ size_t mxgemm_sf_bytes(int64_t MN, int64_t K, int64_t L, int sf_vec_size);
 
 /*
  * mxgemm_launch_config -- the tile shape and grid the GEMM kernel would use
- * for this problem (for reporting and tests).  Writes tile_m, tile_n and
+ * for this problem with 8-bit operands (for reporting and tests; packed FP4
+ * at sf_vec_size 16 always runs 128x128 tiles).  Writes tile_m, tile_n and
  * the number of workgroups; any output pointer may be NULL.  Returns a
  * status like mxgemm_check_support.  Queries the current device's compute
  * unit count (HIP call) only when `grid` is requested.

@@ -58,6 +58,8 @@ def test_check_support(lib):
     assert ok(0, 0, 0, 0, 32, 0, 0) == lib.MXG_OK
     assert ok(-1, 256, 256, 1, 32, 0, 0) == lib.MXG_ERR_SHAPE
     assert ok(256, 256, 256, 1, 8, 0, 0) == lib.MXG_ERR_SFVEC
+    assert ok(256, 256, 256, 1, 16, 2, 2) == lib.MXG_OK      # packed FP4 at sf = 16
+    assert ok(256, 256, 256, 1, 16, 2, 0) == lib.MXG_ERR_FMT
     assert ok(256, 256, 256, 1, 32, 2, 0) == lib.MXG_ERR_FMT
     assert ok(256, 256, 256, 1, 32, 0, 4) == lib.MXG_ERR_FMT
     assert ok(256, 256, 200, 1, 32, 0, 0) == lib.MXG_ERR_ALIGN       # K % 16
@@ -202,6 +204,8 @@ def test_plan_validation_before_device_work(lib):
     assert init(plan, 256, 256, 200, 1, 32, 0, 0, 0) == lib.MXG_ERR_ALIGN
     assert init(plan, 256, 256, 256, 1, 64, 0, 0, 0) == lib.MXG_ERR_SFVEC
     assert init(plan, 256, 256, 256, 1, 32, 0, 0, 96) == lib.MXG_ERR_FLAGS
+    # packed FP4 at sf = 16 runs 128x128 tiles only
+    assert init(plan, 256, 256, 256, 1, 16, 2, 2, lib.MXG_FLAG_TILE_256) == lib.MXG_ERR_FLAGS
     assert init(plan, -1, 256, 256, 1, 32, 0, 0, 0) == lib.MXG_ERR_SHAPE
     assert init(plan, 1 << 22, 16, 16, 1, 32, 0, 0, lib.MXG_FLAG_C_MMAJOR) == lib.MXG_ERR_SHAPE
     # a plan that was never initialised is refused before any device call

@@ -22,37 +22,60 @@ def lib():
 
 
 def run(lib, p, flags=0, c_dtype=torch.float32, guard=2048):
-    M, N, K, L = p["M"], p["N"], p["K"], p["L"]
+    M, N, K, L, sf = p["M"], p["N"], p["K"], p["L"], p["sf"]
     dev = torch.device("cuda:0")
     A, B, SFA, SFB = (torch.from_numpy(np.ascontiguousarray(p[k])).to(dev) for k in ("A", "B", "SFA", "SFB"))
     buf = torch.full((L * M * N + guard,), -5.0, dtype=c_dtype, device=dev)
     am = torch.zeros(1, dtype=torch.float32, device=dev)
-    lib.mxgemm_amax_ex(A, B, SFA, SFB, buf, am, M, N, K, L, 32, E2M1, E2M1, flags)
+    lib.mxgemm_amax_ex(A, B, SFA, SFB, buf, am, M, N, K, L, sf, E2M1, E2M1, flags)
     torch.cuda.synchronize()
     assert torch.all(buf[L * M * N:] == -5.0), "write past C"
     return buf[:L * M * N], am
 
 
-@pytest.mark.parametrize("tile", [0, 4, 8])     # auto, 128x128, 256x256 tiles
+@pytest.mark.parametrize("sf,tile", [(32, 0), (32, 4), (32, 8), (16, 0), (16, 4)])  # tile flag: auto, 128, 256
 @pytest.mark.parametrize("shape", [(256, 256, 256, 1), (300, 520, 544, 2), (64, 100, 32, 1), (520, 260, 1536, 1),
                                    (256, 256, 0, 1)])
-def test_fp4_matches_oracle(lib, shape, tile):
+def test_fp4_matches_oracle(lib, shape, sf, tile):
     M, N, K, L = shape
-    print(f"fp4 {shape} tile flag {tile}", flush=True)
-    p = W.make_problem(M, N, K, L, 32, E2M1, E2M1, seed=M + N + K + 1)
+    print(f"fp4 {shape} sf {sf} tile flag {tile}", flush=True)
+    p = W.make_problem(M, N, K, L, sf, E2M1, E2M1, seed=M + N + K + sf + 1)
     c, am = run(lib, p, tile)
-    cref, sref, aref = oracle.gemm_amax(p["A"], p["B"], p["SFA"], p["SFB"], M, N, K, L, 32, E2M1, E2M1)
+    cref, sref, aref = oracle.gemm_amax(p["A"], p["B"], p["SFA"], p["SFB"], M, N, K, L, sf, E2M1, E2M1)
     got = c.view(L, M, N).double().cpu().numpy()
     assert np.all(np.abs(got - cref) <= 1e-5 * sref + 1e-30)
     assert abs(float(am) - aref) <= 1e-5 * aref
 
 
-def test_fp4_16bit_c_is_rne_of_f32(lib):
-    p = W.make_problem(300, 260, 512, 1, 32, E2M1, E2M1, seed=5)
+@pytest.mark.parametrize("sf", [32, 16])
+def test_fp4_16bit_c_is_rne_of_f32(lib, sf):
+    p = W.make_problem(300, 260, 512, 1, sf, E2M1, E2M1, seed=5)
     c32, a32 = run(lib, p)
     c16, a16 = run(lib, p, lib.MXG_FLAG_C_BF16, torch.bfloat16)
     assert torch.equal(c16.view(torch.int16), c32.to(torch.bfloat16).view(torch.int16))
     assert torch.equal(a16, a32)
+
+
+def test_fp4_sf16_m_major_c_is_the_transpose(lib):
+    # the m-major C of the 128x128 kernel at sf = 16 holds exactly the n-major C transposed
+    M, N, K = 260, 384, 640
+    p = W.make_problem(M, N, K, 1, 16, E2M1, E2M1, seed=21)
+    cn, an = run(lib, p)
+    cm, am = run(lib, p, lib.MXG_FLAG_C_MMAJOR)
+    assert torch.equal(cm.view(N, M).t(), cn.view(M, N))
+    assert torch.equal(am, an)
+
+
+def test_fp4_sf16_ragged_k_and_scale_tail(lib):
+    # K = 32 and 96: the last step holds one or three 16-element blocks of the four an atom covers;
+    # the oracle expands the atoms on its own
+    for M, N, K in ((130, 260, 32), (257, 131 * 4, 96)):
+        p = W.make_problem(M, N, K, 1, 16, E2M1, E2M1, seed=K + 3)
+        c, am = run(lib, p)
+        cref, sref, aref = oracle.gemm_amax(p["A"], p["B"], p["SFA"], p["SFB"], M, N, K, 1, 16, E2M1, E2M1)
+        got = c.view(1, M, N).double().cpu().numpy()
+        assert np.all(np.abs(got - cref) <= 1e-5 * sref + 1e-30), (M, N, K)
+        assert abs(float(am) - aref) <= 1e-5 * aref
 
 
 def test_fp4_large_sampled(lib):
@@ -71,9 +94,13 @@ def test_fp4_large_sampled(lib):
 def test_fp4_rules(lib):
     ok = lib.mxgemm_check_support
     assert ok(256, 256, 256, 1, 32, E2M1, E2M1) == lib.MXG_OK
-    assert ok(256, 256, 256, 1, 16, E2M1, E2M1) == lib.MXG_ERR_SFVEC
+    assert ok(256, 256, 256, 1, 16, E2M1, E2M1) == lib.MXG_OK
+    assert ok(256, 256, 256, 1, 8, E2M1, E2M1) == lib.MXG_ERR_SFVEC
     assert ok(256, 256, 256, 1, 32, E2M1, 0) == lib.MXG_ERR_FMT
     assert ok(256, 256, 240, 1, 32, E2M1, E2M1) == lib.MXG_ERR_ALIGN
     p = W.make_problem(128, 128, 128, 1, 32, E2M1, E2M1, seed=1)
     with pytest.raises(ValueError):
         run(lib, p, lib.MXG_FLAG_FP8_MFMA)
+    p16 = W.make_problem(128, 128, 128, 1, 16, E2M1, E2M1, seed=1)
+    with pytest.raises(ValueError):
+        run(lib, p16, lib.MXG_FLAG_TILE_256)   # sf = 16 runs 128x128 tiles only
