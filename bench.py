@@ -146,7 +146,7 @@ def _is_gemm(name):
 def _is_fused_proj(name):
     # the tile kernel instantiated with the projection epilogue (C type 4, 256x256 tiles), by its
     # demangled or mangled name
-    return "mxgemm_amax_big_kernel" in name and (", 4, 256>" in name or "ELi4ELi256E" in name)
+    return "mxgemm_amax_big_kernel" in name and (", 4, 256>" in name or ", 4, 256, " in name or "ELi4ELi256E" in name)
 
 
 def _is_quantize(name):

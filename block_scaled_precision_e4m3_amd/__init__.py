@@ -34,6 +34,8 @@ MXG_FLAG_TILE_256 = 8
 MXG_FLAG_C_BF16 = 32
 MXG_FLAG_C_F16 = 64
 MXG_FLAG_C_MMAJOR = 128
+MXG_FLAG_A_MMAJOR = 256
+MXG_FLAG_B_NMAJOR = 512
 
 MXG_OK = 0
 MXG_ERR_NULL = -1
@@ -197,12 +199,12 @@ def _fmt_of(t):
     raise MxgemmValueError(MXG_ERR_FMT, f"A/B dtype must be float8_e4m3fn or float8_e5m2, got {t.dtype}")
 
 
-def _as_lrk(t, name, stream=None):
-    """Return (storage tensor contiguous as (L, rows, K), rows, K, L) from a (rows, K, L) view or 2-D.
+def _as_lrk(t, name):
+    """Return (storage tensor, rows, K, L, m_major) from a (rows, K, L) view or 2-D.
 
-    k-major views (strides (K, 1, rows*K)) are used as they are; m-major ones (strides
-    (1, rows, rows*K), the pages' m-major A / n-major B) are rewritten k-major into a new
-    tensor by mxgemm_codes_to_kmajor on `stream`."""
+    k-major views (strides (K, 1, rows*K)) come back as (L, rows, K) storage; m-major ones
+    (strides (1, rows, rows*K), the pages' m-major A / n-major B) as (L, K, rows) storage with
+    m_major True, which the GEMM reads as it is (MXG_FLAG_A_MMAJOR / MXG_FLAG_B_NMAJOR)."""
     import torch
     if t.dim() == 2:
         t = t.unsqueeze(2)
@@ -211,14 +213,10 @@ def _as_lrk(t, name, stream=None):
     rows, k, l = t.shape
     base = t.permute(2, 0, 1)
     if base.is_contiguous():
-        return base, rows, k, l
+        return base, rows, k, l, False
     mmajor = t.permute(2, 1, 0)
     if mmajor.is_contiguous() and t.dtype in (torch.float8_e4m3fn, torch.float8_e5m2):
-        dst = torch.empty((l, rows, k), dtype=t.dtype, device=t.device)
-        codes_to_kmajor(mmajor, dst, rows, k, l, stream)
-        if isinstance(stream, torch.cuda.Stream):
-            dst.record_stream(stream)  # the copy is read on `stream`, not only on the current one
-        return dst, rows, k, l
+        return mmajor, rows, k, l, True
     raise MxgemmValueError(MXG_ERR_ALIGN, f"{name} must be k-major (strides (K, 1, rows*K)) or, for FP8 codes, "
                                           f"m-major (strides (1, rows, rows*K)), batch outermost")
 
@@ -343,8 +341,8 @@ def gemm_amax(a, b, sfa, sfb, c=None, amax=None, sf_vec_size=32, stream=None, ac
     c_major: "n" (C strides (N, 1, M*N), the default) or "m" (strides (1, M, M*N), float32),
     as the pages' wrapper argument of that name."""
     import torch
-    a_base, m, k, l = _as_lrk(a, "A", stream)
-    b_base, n, kb, lb = _as_lrk(b, "B", stream)
+    a_base, m, k, l, a_mm = _as_lrk(a, "A")
+    b_base, n, kb, lb, b_mm = _as_lrk(b, "B")
     if kb != k or lb != l:
         raise MxgemmValueError(MXG_ERR_SHAPE, "A and B disagree on K or L")
     fa, fb = _fmt_of(a), _fmt_of(b)
@@ -369,7 +367,8 @@ def gemm_amax(a, b, sfa, sfb, c=None, amax=None, sf_vec_size=32, stream=None, ac
                                                   "strides (N, 1, M*N)")
     if amax is None:
         amax = torch.zeros((1, 1, 1), dtype=torch.float32, device=a.device)
-    flags = (MXG_FLAG_AMAX_ACCUMULATE if accumulate else 0) | (MXG_FLAG_FP8_MFMA if fp8_mfma else 0) | c_flag
+    flags = (MXG_FLAG_AMAX_ACCUMULATE if accumulate else 0) | (MXG_FLAG_FP8_MFMA if fp8_mfma else 0) | c_flag | \
+        (MXG_FLAG_A_MMAJOR if a_mm else 0) | (MXG_FLAG_B_NMAJOR if b_mm else 0)
     mxgemm_amax_ex(a_base, b_base, sfa_p, sfb_p, c_base, amax, m, n, k, l, sf_vec_size, fa, fb, flags, stream)
     return c, amax
 
@@ -462,7 +461,8 @@ __all__ = [
     "mxgemm_launch_config", "mxgemm_strerror", "gemm_amax", "LIB_PATH", "EXPORTED",
     "mxgemm_mx_quantize", "mx_quantize", "mxgemm_sf_rowwise_to_atoms", "sf_from_rowwise", "Plan",
     "MXG_FMT_E4M3", "MXG_FMT_E5M2", "MXG_FMT_E2M1", "MXG_FLAG_AMAX_ACCUMULATE", "MXG_FLAG_FP8_MFMA", "MXG_FLAG_TILE_128",
-    "MXG_FLAG_TILE_256", "MXG_FLAG_C_BF16", "MXG_FLAG_C_F16", "MXG_FLAG_C_MMAJOR", "codes_to_kmajor",
+    "MXG_FLAG_TILE_256", "MXG_FLAG_C_BF16", "MXG_FLAG_C_F16", "MXG_FLAG_C_MMAJOR", "MXG_FLAG_A_MMAJOR",
+    "MXG_FLAG_B_NMAJOR", "codes_to_kmajor",
     "proj_rope_mxfp8", "gemm_rope_mxfp8", "projection_mxfp8", "projection_mxfp8_noalloc", "MxgemmError",
     "MxgemmValueError",
     "MxgemmRuntimeError",

@@ -16,7 +16,8 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 # carries its own kernels).
 SOURCES = [os.path.join(CSRC, f) for f in ("mxgemm.hip", "launch_t256_bf16_f32.hip", "launch_t256_bf16_c16.hip",
                                            "launch_t128_bf16_f32.hip", "launch_t128_bf16_c16.hip",
-                                           "launch_t256_proj.hip", "launch_fp8.hip", "probes.hip")]
+                                           "launch_t256_proj.hip", "launch_fp8.hip", "launch_t256_mj.hip",
+                                           "launch_t128_mj.hip", "probes.hip")]
 LIB = os.path.join(PKG_DIR, "libmxgemm.so")
 OBJ_DIR = os.path.join(PKG_DIR, "_build")
 

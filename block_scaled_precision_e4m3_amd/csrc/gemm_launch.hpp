@@ -22,6 +22,9 @@ hipError_t launch_bf16_c16_t128(const Params& p, int sf, int fa, int fb, int ct,
 hipError_t launch_proj_t256(const Params& p, int sf, int fa, int fb, int64_t grid, hipStream_t s);
 // scaled-FP8 datapath, float32 C; bt = 256 or 128
 hipError_t launch_fp8(const Params& p, int sf, int fa, int fb, int bt, int64_t grid, hipStream_t s);
+// bf16 datapath, float32 n-major C, m-major A (mj bit 0) and/or n-major B (bit 1); 8-bit formats
+hipError_t launch_bf16_mj_t256(const Params& p, int sf, int fa, int fb, int mj, int64_t grid, hipStream_t s);
+hipError_t launch_bf16_mj_t128(const Params& p, int sf, int fa, int fb, int mj, int64_t grid, hipStream_t s);
 
 // The format dispatch shared by those launchers: K(SF, FA, FB) names the
 // kernel to launch with hipLaunchKernelGGL(kernel, grid, block, 0, s, p).

@@ -196,6 +196,7 @@ struct Prepared {
   int dev;                  // plans: the device the plan was made for
   mxg::Params p;            // sizes and tiling; pointers filled at launch
   int sf, fa, fb, kind, ct;
+  int mj;                   // bit 0: m-major A, bit 1: n-major B
   unsigned flags;
   int64_t grid;
   bool fp8, accumulate, need_c, need_a;
@@ -235,8 +236,17 @@ int prepare(Prepared* pr, int64_t M, int64_t N, int64_t K, int64_t L, int sf_vec
   const unsigned tile_flags = flags & (MXG_FLAG_TILE_128 | MXG_FLAG_TILE_256);
   const unsigned c_flags = flags & (MXG_FLAG_C_BF16 | MXG_FLAG_C_F16);
   if (flags & ~(unsigned)(MXG_FLAG_AMAX_ACCUMULATE | MXG_FLAG_FP8_MFMA | MXG_FLAG_TILE_128 | MXG_FLAG_TILE_256 |
-                          MXG_FLAG_C_BF16 | MXG_FLAG_C_F16 | MXG_FLAG_C_MMAJOR))
+                          MXG_FLAG_C_BF16 | MXG_FLAG_C_F16 | MXG_FLAG_C_MMAJOR | MXG_FLAG_A_MMAJOR |
+                          MXG_FLAG_B_NMAJOR))
     return MXG_ERR_FLAGS;
+  // m-major A / n-major B: 8-bit codes, bf16 datapath, float32 n-major C;
+  // contiguous dimension in whole 16-byte chunks; one batch below 2^31 bytes
+  const int mj = ((flags & MXG_FLAG_A_MMAJOR) ? 1 : 0) | ((flags & MXG_FLAG_B_NMAJOR) ? 2 : 0);
+  if (mj && (a_fmt == MXG_FMT_E2M1 ||
+             (flags & (MXG_FLAG_FP8_MFMA | MXG_FLAG_C_BF16 | MXG_FLAG_C_F16 | MXG_FLAG_C_MMAJOR))))
+    return MXG_ERR_FLAGS;
+  if (((mj & 1) && M * K >= (1LL << 31)) || ((mj & 2) && N * K >= (1LL << 31))) return MXG_ERR_SHAPE;
+  if (((mj & 1) && M % 16 != 0) || ((mj & 2) && N % 16 != 0)) return MXG_ERR_ALIGN;
   const bool c_mmajor = (flags & MXG_FLAG_C_MMAJOR) != 0;
   // m-major C: the bf16 datapath with a float32 C
   if (c_mmajor && (flags & (MXG_FLAG_FP8_MFMA | MXG_FLAG_C_BF16 | MXG_FLAG_C_F16))) return MXG_ERR_FLAGS;
@@ -258,6 +268,7 @@ int prepare(Prepared* pr, int64_t M, int64_t N, int64_t K, int64_t L, int sf_vec
   pr->fp8 = (flags & MXG_FLAG_FP8_MFMA) != 0;
   pr->accumulate = (flags & MXG_FLAG_AMAX_ACCUMULATE) != 0;
   pr->ct = (flags & MXG_FLAG_C_BF16) ? 1 : (flags & MXG_FLAG_C_F16) ? 2 : c_mmajor ? 3 : 0;
+  pr->mj = mj;
   // A, B and the scales are read only when there is a non-empty C and a non-empty K
   pr->need_c = M > 0 && N > 0 && L > 0;
   pr->need_a = pr->need_c && K > 0;
@@ -311,6 +322,9 @@ int launch_prepared(const Prepared& pr, const void* A, const void* B, const uint
     const int64_t words = (int64_t)p.L * p.M * p.N * (pr.ct == 1 || pr.ct == 2 ? 2 : 4) / 8;
     hipLaunchKernelGGL(mxg::c_zero_kernel, dim3((unsigned)grid), dim3(256), 0, s, reinterpret_cast<uint2*>(C), words);
     e = hipGetLastError();
+  } else if (pr.mj) {
+    e = pr.kind == 1 ? mxg::launch_bf16_mj_t256(p, sf, fa, fb, pr.mj, grid, s)
+                     : mxg::launch_bf16_mj_t128(p, sf, fa, fb, pr.mj, grid, s);
   } else if (pr.fp8) {
     e = mxg::launch_fp8(p, sf, fa, fb, pr.kind == 1 ? 256 : 128, grid, s);
   } else if (pr.ct == 1 || pr.ct == 2) {

@@ -111,7 +111,21 @@ __device__ __forceinline__ unsigned sf_tail(unsigned d, int g, int Kb) {
   return (d & keep) | (0x7F7F7F7Fu & ~keep);
 }
 
-template <int SF, int FA, int FB, int MODE, int CT, int BT>
+// 8 bytes of an m-major tile held in LDS as (K row, M column), read with the
+// transposing LDS load: the lanes of each group of 16 give 16 row addresses
+// and lane j receives byte (j & 7) of the rows given by lanes 2b + (j >> 3),
+// b = 0..7 (measured on MI355X for three address patterns).
+__device__ __forceinline__ uint2 lds_tr8(const uint8_t* p) {
+  typedef int v2i_t __attribute__((ext_vector_type(2)));
+  typedef __attribute__((address_space(3))) v2i_t lds_v2i_t;
+  const v2i_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t*)(p));
+  return make_uint2((unsigned)v[0], (unsigned)v[1]);
+}
+
+// MJ: operand majors, bit 0 A m-major ((L, K, M) bytes, M contiguous), bit 1
+// B n-major ((L, K, N)); 8-bit codes on the bf16 datapath with a float32
+// n-major C.
+template <int SF, int FA, int FB, int MODE, int CT, int BT, int MJ = 0>
 __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) {
   // FA = FB = 2: packed FP4 (E2M1), bf16 datapath, sf = 32 (the host enforces it)
   constexpr bool kFp4 = FA == 2;
@@ -119,6 +133,8 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   static_assert(!(kFp4 && SF == 16) || (BT == 128 && CT != 4), "FP4 at sf = 16: 128x128 tiles (LDS)");
   static_assert(!kCMajorM<CT> || MODE == kModeBf16, "m-major C: bf16 path");
   static_assert(CT != 4 || (MODE == kModeBf16 && BT == 256), "projection epilogue: bf16 path, 256x256 tiles");
+  constexpr bool kAMaj = (MJ & 1) != 0, kBMaj = (MJ & 2) != 0;
+  static_assert(MJ == 0 || (MODE == kModeBf16 && !kFp4 && CT == 0), "m-major operands: 8-bit, bf16 path, f32 C");
   // LDS ring stages: a 128x128 tile's steps are short, so its bf16 datapath
   // queues the DMA three steps ahead in four stages; a 256x256 tile's ring
   // fills the LDS with two
@@ -199,18 +215,56 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   constexpr unsigned kOob = 0x80000000u;
   const bool sf_wave = (NSF == 2 && BT == 256) || NSF == 4 || wave < 2;
   const bool sf_is_b = (wave & 1) != 0;
+  // An m-major operand (MJ) is staged as 128 K rows of BT bytes (its tile's
+  // columns), 16-byte chunk u of K row k at slot u ^ sw(k), sw(k) = 2 (k & 7)
+  // for BT = 256 and 2 ((k >> 1) & 3) for BT = 128: the transposing reads of
+  // a pass then cover every bank once.  DMA instruction q of wave w fills K
+  // rows (BT == 256 ? 4 : 8) * (w + 4q) onward, one kilobyte, lane l taking
+  // row (BT == 256 ? l / 16 : l / 8) of those and slot l % (BT / 16); chunks
+  // past the matrix's columns or K rows past K read as zero (the host
+  // requires columns in whole chunks).
+  constexpr int kMjRowsPerQ = BT == 256 ? 16 : 32;  // K rows between a wave's DMA instructions
   struct Dma {
     __amdgpu_buffer_rsrc_t ra, rb, rs;
-    unsigned voff;     // lane's offset in row group 0 of the step (or >= 2^31)
+    unsigned voff_a, voff_b;  // lane's offset for instruction 0 (or >= 2^31)
+    int left_a, left_b;       // m-major: K rows from the lane's first to K (0 if none valid)
     unsigned sf_voff;  // lane's SF offset
     unsigned dst;      // LDS address of the stage
   };
+  // m-major operand X (MN columns) of tile columns mn0..: resource, lane offset, rows left
+  auto mj_setup = [&](const Geo& g, const uint8_t* X, int MN, int mn0, int l, int kt, bool live,
+                      __amdgpu_buffer_rsrc_t& rsrc, unsigned& voff, int& left) {
+    const int ln = g.r + 32 * g.h;
+    const int64_t base = (int64_t)l * MN * p.K + mn0;
+    rsrc = make_rsrc(X + base, live ? (unsigned)((int64_t)MN * p.K - mn0) : 0u);
+    const int row = BT == 256 ? 4 * wave + (ln >> 4) : 8 * wave + (ln >> 3);
+    const int sw = BT == 256 ? 2 * ((4 * (wave & 1) + (ln >> 4)) & 7) : 2 * ((ln >> 4) & 3);
+    const int u = (BT == 256 ? (ln & 15) : (ln & 7)) ^ sw;
+    const int krow = kt * kBK + row;
+    const bool ok = mn0 + 16 * u < MN && krow < p.K;
+    voff = ok ? (unsigned)krow * (unsigned)MN + 16u * (unsigned)u : kOob;
+    left = ok ? p.K - krow : 0;
+  };
   auto dma_setup = [&](const Geo& g, const Tile& T, int kt, bool live, unsigned stage) {
     Dma d;
-    d.ra = make_rsrc(p.A + ((int64_t)T.l * p.M + T.m0) * p.Kbytes, live ? (unsigned)T.mvalid * (unsigned)p.Kbytes : 0u);
-    d.rb = make_rsrc(p.B + ((int64_t)T.l * p.N + T.n0) * p.Kbytes, live ? (unsigned)T.nvalid * (unsigned)p.Kbytes : 0u);
     const unsigned kk = (unsigned)(kt * kBK) + g.kchunk;
-    d.voff = kk < (unsigned)p.Kbytes ? g.row_k + kk : kOob;
+    const unsigned voff = kk < (unsigned)p.Kbytes ? g.row_k + kk : kOob;
+    if constexpr (kAMaj) {
+      mj_setup(g, p.A, p.M, T.m0, T.l, kt, live, d.ra, d.voff_a, d.left_a);
+    } else {
+      d.ra = make_rsrc(p.A + ((int64_t)T.l * p.M + T.m0) * p.Kbytes,
+                       live ? (unsigned)T.mvalid * (unsigned)p.Kbytes : 0u);
+      d.voff_a = voff;
+      d.left_a = 0;
+    }
+    if constexpr (kBMaj) {
+      mj_setup(g, p.B, p.N, T.n0, T.l, kt, live, d.rb, d.voff_b, d.left_b);
+    } else {
+      d.rb = make_rsrc(p.B + ((int64_t)T.l * p.N + T.n0) * p.Kbytes,
+                       live ? (unsigned)T.nvalid * (unsigned)p.Kbytes : 0u);
+      d.voff_b = voff;
+      d.left_b = 0;
+    }
     const int mn0 = sf_is_b ? T.n0 : T.m0;
     const int mnb = sf_is_b ? p.MNbB : p.MNbA;
     const int g0 = mn0 >> 7;
@@ -228,7 +282,16 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   auto dma_ab = [&](const Dma& d, int q) {
     const bool qb = q >= Y::kDmaA;
     const int qq = qb ? q - Y::kDmaA : q;
-    const unsigned voff = d.voff + (unsigned)qq * grp_stride;
+    const bool mj = qb ? kBMaj : kAMaj;
+    unsigned voff;
+    if (mj) {
+      const unsigned mn = (unsigned)(qb ? p.N : p.M);
+      voff = qq * kMjRowsPerQ < (qb ? d.left_b : d.left_a)
+                 ? (qb ? d.voff_b : d.voff_a) + (unsigned)(qq * kMjRowsPerQ) * mn
+                 : kOob;
+    } else {
+      voff = (qb ? d.voff_b : d.voff_a) + (unsigned)qq * grp_stride;
+    }
     const unsigned dst = d.dst + (qb ? (unsigned)Y::kOffB : 0u) + (unsigned)(wave + 4 * qq) * 1024u;
     dma16_at(qb ? d.rb : d.ra, voff, dst);
   };
@@ -648,12 +711,30 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
         sb[j][i] = sf_tail(lds4(st + Y::kOffSFB + (brg * NSF + j) * 512 + 16 * g.r + 4 * (bdw + i)), ga, p.Kb);
     }
   };
-  // chunk c's fragments (32-row steps keep f, so only the chunk is swizzled)
+  // chunk c's fragments (32-row steps keep f, so only the chunk is swizzled).
+  // An m-major operand's lane (r, h) takes the same K elements of its row with
+  // two transposing reads, K 32c + 16h + 8t + (0..7) for t = 0, 1: lane
+  // i = r % 16 of its group of 16 addresses K row 32c + 16h + 8t + i/2 at
+  // column 16 (r / 16) + 8 (i % 2) of the fragment's 32.
+  auto mj_frag = [&](const Geo& g, const uint8_t* tile, int row0, int c) __attribute__((always_inline)) {
+    const int i16 = g.r & 15;
+    const int sw = BT == 256 ? (g.r & 14) : ((g.r >> 1) & 6);
+    const int unit = ((row0 >> 4) ^ sw) | (g.r >> 4);
+    const uint8_t* q = tile + (16 * g.h + (i16 >> 1) + 32 * c) * BT + 8 * (g.r & 1) + 16 * unit;
+    const uint2 lo = lds_tr8(q), hi = lds_tr8(q + 8 * BT);
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
+  };
   auto load_raw = [&](const Geo& g, const uint8_t* st, int c) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < kTM; ++i) ra[c & 1][i] = lds16(st + g.a_off + (((2 * c + g.h) ^ g.xr) << 4) + 4096 * i);
+    for (int i = 0; i < kTM; ++i) {
+      if constexpr (kAMaj) ra[c & 1][i] = mj_frag(g, st, kWM * wm + 32 * i, c);
+      else ra[c & 1][i] = lds16(st + g.a_off + (((2 * c + g.h) ^ g.xr) << 4) + 4096 * i);
+    }
 #pragma unroll
-    for (int i = 0; i < kTN; ++i) rb[c & 1][i] = lds16(st + g.b_off + (((2 * c + g.h) ^ g.xr) << 4) + 4096 * i);
+    for (int i = 0; i < kTN; ++i) {
+      if constexpr (kBMaj) rb[c & 1][i] = mj_frag(g, st + Y::kOffB, kWN * wn + 32 * i, c);
+      else rb[c & 1][i] = lds16(st + g.b_off + (((2 * c + g.h) ^ g.xr) << 4) + 4096 * i);
+    }
   };
   // chunk c's scale: one atom per step (8-bit, sf=32) -> block c (byte c);
   // two atoms (8-bit with sf=16, or FP4 with sf=32, whose 16-byte chunk holds

@@ -129,7 +129,19 @@ enum {
      must be 16-byte aligned, so M % 4 == 0 as well (MXG_ERR_ALIGN otherwise).
      The default datapath with a float32 C only: not with MXG_FLAG_FP8_MFMA
      or MXG_FLAG_C_BF16 / _F16 (MXG_ERR_FLAGS). */
-  MXG_FLAG_C_MMAJOR = 128u
+  MXG_FLAG_C_MMAJOR = 128u,
+  /* m-major A and n-major B ("GEMM + Amax (SM100)", section "Parameters":
+     A of shape (M, K, L) with strides (1, M, M*K), B (N, K, L) with strides
+     (1, N, N*K)): A then holds (L, K, M) codes, M contiguous (A_MMAJOR), B
+     (L, K, N) codes, N contiguous (B_NMAJOR); either or both.  The kernel
+     stages such a tile as K rows in LDS and reads it with gfx950's
+     transposing LDS load, so no copy is made; results are bitwise those of
+     the k-major operands.  8-bit formats, the default datapath and a
+     float32 n-major C only (MXG_ERR_FLAGS otherwise); the contiguous
+     dimension must be a multiple of 16 (MXG_ERR_ALIGN) and one batch of the
+     operand (M*K or N*K bytes) below 2^31 (MXG_ERR_SHAPE). */
+  MXG_FLAG_A_MMAJOR = 256u,
+  MXG_FLAG_B_NMAJOR = 512u
 };
 
 /*

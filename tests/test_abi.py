@@ -100,7 +100,7 @@ def test_errors_before_device_work(lib):
     assert f(*(args[:5] + [None]), *dims, 32, 0, 0, 0, None) == lib.MXG_ERR_NULL
     assert f(*([good + 8] + args[1:]), *dims, 32, 0, 0, 0, None) == lib.MXG_ERR_ALIGN
     assert f(*(args[:4] + [good + 4] + args[5:]), *dims, 32, 0, 0, 0, None) == lib.MXG_ERR_ALIGN
-    assert f(*args, *dims, 32, 0, 0, 256, None) == lib.MXG_ERR_FLAGS    # unknown bit
+    assert f(*args, *dims, 32, 0, 0, 1024, None) == lib.MXG_ERR_FLAGS    # unknown bit
     # m-major C: the bf16 datapath, float32 C, M % 4 == 0 (either tile size)
     mm = lib.MXG_FLAG_C_MMAJOR
     assert f(*args, *dims, 32, 0, 0, mm | lib.MXG_FLAG_FP8_MFMA, None) == lib.MXG_ERR_FLAGS
@@ -206,6 +206,17 @@ def test_plan_validation_before_device_work(lib):
     assert init(plan, 256, 256, 256, 1, 32, 0, 0, 96) == lib.MXG_ERR_FLAGS
     # packed FP4 at sf = 16 runs 128x128 tiles only
     assert init(plan, 256, 256, 256, 1, 16, 2, 2, lib.MXG_FLAG_TILE_256) == lib.MXG_ERR_FLAGS
+    # m-major A / n-major B: 8-bit codes, bf16 datapath, float32 n-major C, whole 16-byte chunks
+    am, bn = lib.MXG_FLAG_A_MMAJOR, lib.MXG_FLAG_B_NMAJOR
+    assert init(plan, 256, 256, 256, 1, 32, 2, 2, am) == lib.MXG_ERR_FLAGS
+    assert init(plan, 256, 256, 256, 1, 32, 0, 0, bn | lib.MXG_FLAG_FP8_MFMA) == lib.MXG_ERR_FLAGS
+    assert init(plan, 256, 256, 256, 1, 32, 0, 0, am | lib.MXG_FLAG_C_BF16) == lib.MXG_ERR_FLAGS
+    assert init(plan, 256, 256, 256, 1, 32, 0, 0, am | lib.MXG_FLAG_C_MMAJOR) == lib.MXG_ERR_FLAGS
+    assert init(plan, 264, 256, 256, 1, 32, 0, 0, am) == lib.MXG_ERR_ALIGN
+    assert init(plan, 256, 264, 256, 1, 32, 0, 0, bn) == lib.MXG_ERR_ALIGN
+    assert init(plan, 264, 256, 256, 1, 32, 0, 0, bn) != lib.MXG_ERR_ALIGN     # M is free with B n-major
+    assert init(plan, 1 << 16, 256, 1 << 15, 1, 32, 0, 0, am) == lib.MXG_ERR_SHAPE  # one batch >= 2^31 B
+    assert init(plan, 1 << 16, 256, 1 << 15, 1, 32, 0, 0, bn) != lib.MXG_ERR_SHAPE
     assert init(plan, -1, 256, 256, 1, 32, 0, 0, 0) == lib.MXG_ERR_SHAPE
     assert init(plan, 1 << 22, 16, 16, 1, 32, 0, 0, lib.MXG_FLAG_C_MMAJOR) == lib.MXG_ERR_SHAPE
     # a plan that was never initialised is refused before any device call
