@@ -532,37 +532,44 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
           *reinterpret_cast<unsigned*>(p.col_scales + (tok0 >> 5) * N + c0 + 4 * r) = sb;
         }
       }
-      // 4. both directions' codes: lane takes rows (ln / 8) + 8k and column
-      // groups (ln % 8) + 8b; a row block (32 columns) is 8 consecutive
-      // lanes, whose maximum three DPP steps find (quad swaps, then the
-      // mirror of the half-row)
-      v4u ecol[4];
+      // 4. both directions' codes: lane takes the 16 columns 16q .. 16q+15
+      // (q = ln % 8) of rows (ln / 8) + 8k, so that each direction's codes of
+      // a row leave as one 16-byte store and 8 lanes write a whole 128-byte
+      // line; a row block (32 columns) is a lane pair, whose maximum one DPP
+      // swap finds, and the row's 4 block scales gather in its lane q = 0
+      const int q = ln & 7;
+      v4u ecol[4];  // column exponents of columns 16q + 4j .. 16q + 4j + 3
 #pragma unroll
-      for (int bb = 0; bb < 4; ++bb) ecol[bb] = *reinterpret_cast<const v4u*>(z + ((ln & 7) + 8 * bb) * P + 128);
+      for (int j = 0; j < 4; ++j) ecol[j] = *reinterpret_cast<const v4u*>(z + (4 * q + j) * P + 128);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int rr = (ln >> 3) + 8 * k;
         const int64_t tok = tok0 + rr;
-        unsigned rs = 0u;
+        v4f v[4];
 #pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
-          const int g = (ln & 7) + 8 * bb;
-          const v4f v = *reinterpret_cast<const v4f*>(z + rr * P + 4 * g);
-          const v4u ec = ecol[bb];
-          float bm = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-          bm = fmaxf(bm, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(bm), 0xB1, 0xF, 0xF, false)));
-          bm = fmaxf(bm, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(bm), 0x4E, 0xF, 0xF, false)));
-          bm = fmaxf(bm, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(bm), 0x141, 0xF, 0xF, false)));
-          const int er = quant::block_exponent<0>(bm);
-          const int64_t o = tok * N + c0 + 4 * g;
-          *reinterpret_cast<unsigned*>(p.row_codes + o) =
-              quant::codes4<0>(ldexpf(v[0], -er), ldexpf(v[1], -er), ldexpf(v[2], -er), ldexpf(v[3], -er));
-          *reinterpret_cast<unsigned*>(p.col_codes + o) =
-              quant::codes4<0>(ldexpf(v[0], -(int)ec[0]), ldexpf(v[1], -(int)ec[1]), ldexpf(v[2], -(int)ec[2]),
-                               ldexpf(v[3], -(int)ec[3]));
-          rs |= ((unsigned)(er + 127) & 0xFFu) << (8 * bb);
+        for (int j = 0; j < 4; ++j) v[j] = *reinterpret_cast<const v4f*>(z + rr * P + 16 * q + 4 * j);
+        float bm = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          bm = fmaxf(bm, fmaxf(fmaxf(fabsf(v[j][0]), fabsf(v[j][1])), fmaxf(fabsf(v[j][2]), fabsf(v[j][3]))));
+        bm = fmaxf(bm, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(bm), 0xB1, 0xF, 0xF, false)));
+        const int er = quant::block_exponent<0>(bm);
+        v4u rc, cc;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          rc[j] = quant::codes4<0>(ldexpf(v[j][0], -er), ldexpf(v[j][1], -er), ldexpf(v[j][2], -er),
+                                   ldexpf(v[j][3], -er));
+          cc[j] = quant::codes4<0>(ldexpf(v[j][0], -(int)ecol[j][0]), ldexpf(v[j][1], -(int)ecol[j][1]),
+                                   ldexpf(v[j][2], -(int)ecol[j][2]), ldexpf(v[j][3], -(int)ecol[j][3]));
         }
-        if ((ln & 7) == 0) *reinterpret_cast<unsigned*>(p.row_scales + tok * (N >> 5) + (c0 >> 5)) = rs;
+        const int64_t o = tok * N + c0 + 16 * q;
+        *reinterpret_cast<v4u*>(p.row_codes + o) = rc;
+        *reinterpret_cast<v4u*>(p.col_codes + o) = cc;
+        const unsigned sbyte = (unsigned)(er + 127) & 0xFFu;
+        const int base = ln & ~7;
+        const unsigned rs = sbyte | ((unsigned)__shfl((int)sbyte, base + 2) << 8) |
+                            ((unsigned)__shfl((int)sbyte, base + 4) << 16) | ((unsigned)__shfl((int)sbyte, base + 6) << 24);
+        if (q == 0) *reinterpret_cast<unsigned*>(p.row_scales + tok * (N >> 5) + (c0 >> 5)) = rs;
       }
     }
   };
