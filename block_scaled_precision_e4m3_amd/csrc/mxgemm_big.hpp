@@ -557,8 +557,7 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
         v4u rc, cc;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          rc[j] = quant::codes4<0>(ldexpf(v[j][0], -er), ldexpf(v[j][1], -er), ldexpf(v[j][2], -er),
-                                   ldexpf(v[j][3], -er));
+          rc[j] = quant::codes4_e4m3_exp(v[j][0], v[j][1], v[j][2], v[j][3], er);
           cc[j] = quant::codes4<0>(ldexpf(v[j][0], -(int)ecol[j][0]), ldexpf(v[j][1], -(int)ecol[j][1]),
                                    ldexpf(v[j][2], -(int)ecol[j][2]), ldexpf(v[j][3], -(int)ecol[j][3]));
         }
