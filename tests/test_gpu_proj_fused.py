@@ -107,6 +107,36 @@ def test_fused_equals_rope_quantise_of_the_gemm(lib, tokens, heads, d, qr, K, sf
     compare(out, ref)
 
 
+def test_fused_wide_exponent_range(lib):
+    # token rows scaled by 2^U(-10, 10) before MX quantisation: Y's row blocks span about
+    # twenty exponents (row codes at many block scales), and each 32-token column block
+    # mixes rows far apart in size (column codes down to subnormal and zero); bit-exact
+    # against the oracle's RoPE + quantisation of the plain GEMM's Y
+    tokens, heads, d, qr, K = 256, 4, 192, 64, 768
+    n = heads * d
+    print(f"fused projection, wide exponents: {tokens} tokens, {heads}x{d}, K={K}", flush=True)
+    rng = np.random.default_rng(99)
+    x = rng.standard_normal((1, tokens, K)) * np.exp2(rng.uniform(-10, 10, size=(1, tokens, 1)))
+    w = rng.standard_normal((1, n, K)) / np.sqrt(K)
+    xq, xs = W.mx_quantize(x.astype(np.float32), 32, E4)
+    wq, ws = W.mx_quantize(w.astype(np.float32), 32, E4)
+    p = dict(A=xq, B=wq, SFA=W.pack_sf(xs, tokens, K, 1, 32), SFB=W.pack_sf(ws, n, K, 1, 32),
+             M=tokens, N=n, K=K, L=1, sf=32, a_fmt=E4, b_fmt=E4)
+    dev = torch.device("cuda:0")
+    d_ = {k: torch.from_numpy(np.ascontiguousarray(p[k])).to(dev) for k in ("A", "B", "SFA", "SFB")}
+    cs, sn = rope_tables(tokens, qr, seed=5)
+    bufs, sizes, out = guarded_outputs(tokens, heads, d)
+    lib.gemm_rope_mxfp8(d_["A"], d_["B"], d_["SFA"], d_["SFB"], cs.to(dev), sn.to(dev), tokens, heads, d, qr, K,
+                        out=out)
+    torch.cuda.synchronize()
+    check_guards(bufs, sizes)
+    y = plain_y(lib, p, d_)
+    rs = out[1].cpu().numpy().astype(int)
+    assert rs.max() - rs.min() >= 16, "row scales should span a wide range"
+    ref = oracle.proj_rope_mxfp8(y, cs.float().numpy(), sn.float().numpy(), heads, d, qr)
+    compare(out, ref)
+
+
 def rowwise_problem(tokens, n, k, seed):
     rng = np.random.default_rng(seed)
     x = rng.standard_normal((1, tokens, k)).astype(np.float32)
