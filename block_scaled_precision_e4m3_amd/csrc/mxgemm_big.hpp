@@ -18,16 +18,21 @@
 //   2^-13 of the largest in its 8-element K group, so terms much smaller
 //   than their neighbours are truncated.
 //
-// Work shape: one workgroup per CU, 4 waves in 2 x 2, on square C tiles of
-// BT x BT (BT = 256: waves of 128 x 128 in 4 x 4 MFMA blocks, all 256
-// matrix-core registers; BT = 128: waves of 64 x 64).  Tiles are taken
+// Work shape: one workgroup per CU, 4 computing waves in 2 x 2, on square C
+// tiles of BT x BT (BT = 256: waves of 128 x 128 in 4 x 4 MFMA blocks, all
+// 256 matrix-core registers; BT = 128: waves of 64 x 64).  Tiles are taken
 // persistently: workgroup w runs tiles w, w+G, ....
 //
 // * The K loop moves 128 bytes of every operand row per step through an LDS
 //   ring (2 stages for BT = 256, 4 for the bf16 datapath at BT = 128) by
 //   direct global->LDS DMA, the step's E8M0 atoms beside the tile.  Per
 //   128-K step a 256x256 tile moves 64 KB for 8.4 M multiply-adds, a
-//   128x128 tile 32 KB for 2.1 M.
+//   128x128 tile 32 KB for 2.1 M.  The 4-stage ring's DMA comes from 4 more
+//   waves that do nothing else: a wave whose DMA finds the vector-memory
+//   queue full stops issuing until it drains, which, on the computing waves,
+//   would stall their MFMAs for the operand stream (a 128x128 tile moves
+//   twice the bytes per flop of a 256x256 one).  The 256x256 waves hold all
+//   512 registers of their SIMD, leaving no room for a second wave.
 // * bf16 step: 8 MFMA slices of 16 K; each slice's conversions run under the
 //   previous slice's MFMAs (scheduling-group barriers pin the interleave), so
 //   one wave per SIMD keeps the matrix core fed; one barrier per step.
@@ -124,9 +129,12 @@ __device__ __forceinline__ uint2 lds_tr8(const uint8_t* p) {
 
 // MJ: operand majors, bit 0 A m-major ((L, K, M) bytes, M contiguous), bit 1
 // B n-major ((L, K, N)); 8-bit codes on the bf16 datapath with a float32
-// n-major C.
-template <int SF, int FA, int FB, int MODE, int CT, int BT, int MJ = 0>
-__global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) {
+// n-major C.  NW: waves per workgroup, 4, or 8 on the 128x128 ring (every
+// format but FP4 at sf = 16), where waves 4..7 only stream the operands into
+// the ring (each what wave w - 4 would queue) and waves 0..3 only compute and
+// store, so the compute waves never stall on a full vector-memory queue.
+template <int SF, int FA, int FB, int MODE, int CT, int BT, int MJ = 0, int NW = 4>
+__global__ __launch_bounds__(64 * NW, 1) void mxgemm_amax_big_kernel(Params p) {
   // FA = FB = 2: packed FP4 (E2M1), bf16 datapath, sf = 32 (the host enforces it)
   constexpr bool kFp4 = FA == 2;
   static_assert(!kFp4 || (FB == 2 && MODE == kModeBf16), "FP4: both operands, bf16 path");
@@ -135,6 +143,8 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   static_assert(CT != 4 || (MODE == kModeBf16 && BT == 256), "projection epilogue: bf16 path, 256x256 tiles");
   constexpr bool kAMaj = (MJ & 1) != 0, kBMaj = (MJ & 2) != 0;
   static_assert(MJ == 0 || (MODE == kModeBf16 && !kFp4 && CT == 0), "m-major operands: 8-bit, bf16 path, f32 C");
+  static_assert(NW == 4 || (NW == 8 && BT == 128 && MODE == kModeBf16 && !(kFp4 && SF == 16) && CT != 4),
+                "8 waves: the 128x128 ring of the bf16 path");
   // LDS ring stages: a 128x128 tile's steps are short, so its bf16 datapath
   // queues the DMA three steps ahead in four stages; a 256x256 tile's ring
   // fills the LDS with two
@@ -153,7 +163,9 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int dw = NW == 8 ? wave & 3 : wave;  // the wave's share of the DMA
+  const bool producer = NW == 8 && wave >= 4;  // 8 waves: this wave only queues DMA
+  const int wm = NW == 8 ? (wave >> 1) & 1 : wave >> 1, wn = wave & 1;
 
   const int G = (int)gridDim.x;
   const int t0 = first_tile(p);
@@ -185,11 +197,11 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
     g.a_off = (kWM * wm + g.r) * kBK;
     g.b_off = Y::kOffB + (kWN * wn + g.r) * kBK;
     const int dma_row = ln >> 3;
-    g.row_k = (unsigned)(wave * 8 + dma_row) * (unsigned)p.Kbytes;
-    g.kchunk = (unsigned)(((ln & 7) ^ dma_row ^ (wave & 1)) << 4);
+    g.row_k = (unsigned)(dw * 8 + dma_row) * (unsigned)p.Kbytes;
+    g.kchunk = (unsigned)(((ln & 7) ^ dma_row ^ (dw & 1)) << 4);
     g.sf_lane = 16u * (unsigned)(ln & 31);
-    g.sf_rg = NSF == 1 ? (ln >> 5) : NSF == 4 ? 0 : (wave >> 1);
-    g.sf_j = NSF == 1 ? 0 : NSF == 4 ? 2 * (wave >> 1) + (ln >> 5) : (ln >> 5);
+    g.sf_rg = NSF == 1 ? (ln >> 5) : NSF == 4 ? 0 : (dw >> 1);
+    g.sf_j = NSF == 1 ? 0 : NSF == 4 ? 2 * (dw >> 1) + (ln >> 5) : (ln >> 5);
     return g;
   };
   auto lane_opaque = [&]() {
@@ -213,8 +225,8 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   // resource into their own kilobyte of the dummy area (no branch in the
   // step).
   constexpr unsigned kOob = 0x80000000u;
-  const bool sf_wave = (NSF == 2 && BT == 256) || NSF == 4 || wave < 2;
-  const bool sf_is_b = (wave & 1) != 0;
+  const bool sf_wave = (NSF == 2 && BT == 256) || NSF == 4 || dw < 2;
+  const bool sf_is_b = (dw & 1) != 0;
   // An m-major operand (MJ) is staged as 128 K rows of BT bytes (its tile's
   // columns), 16-byte chunk u of K row k at slot u ^ sw(k), sw(k) = 2 (k & 7)
   // for BT = 256 and 2 ((k >> 1) & 3) for BT = 128: the transposing reads of
@@ -237,8 +249,8 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
     const int ln = g.r + 32 * g.h;
     const int64_t base = (int64_t)l * MN * p.K + mn0;
     rsrc = make_rsrc(X + base, live ? (unsigned)((int64_t)MN * p.K - mn0) : 0u);
-    const int row = BT == 256 ? 4 * wave + (ln >> 4) : 8 * wave + (ln >> 3);
-    const int sw = BT == 256 ? 2 * ((4 * (wave & 1) + (ln >> 4)) & 7) : 2 * ((ln >> 4) & 3);
+    const int row = BT == 256 ? 4 * dw + (ln >> 4) : 8 * dw + (ln >> 3);
+    const int sw = BT == 256 ? 2 * ((4 * (dw & 1) + (ln >> 4)) & 7) : 2 * ((ln >> 4) & 3);
     const int u = (BT == 256 ? (ln & 15) : (ln & 7)) ^ sw;
     const int krow = kt * kBK + row;
     const bool ok = mn0 + 16 * u < MN && krow < p.K;
@@ -292,14 +304,14 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
     } else {
       voff = (qb ? d.voff_b : d.voff_a) + (unsigned)qq * grp_stride;
     }
-    const unsigned dst = d.dst + (qb ? (unsigned)Y::kOffB : 0u) + (unsigned)(wave + 4 * qq) * 1024u;
+    const unsigned dst = d.dst + (qb ? (unsigned)Y::kOffB : 0u) + (unsigned)(dw + 4 * qq) * 1024u;
     dma16_at(qb ? d.rb : d.ra, voff, dst);
   };
   // waves 2 and 3 (the only ones that use it) each own a kilobyte
-  const unsigned sf_dummy = lds0 + (unsigned)Y::kOffDummy + (unsigned)(wave & 1) * 1024u;
+  const unsigned sf_dummy = lds0 + (unsigned)Y::kOffDummy + (unsigned)(dw & 1) * 1024u;
   auto dma_sf = [&](const Dma& d) {
     const unsigned dst = d.dst + (sf_is_b ? (unsigned)Y::kOffSFB : (unsigned)Y::kOffSFA) +
-                         (NSF == 1 ? 0u : (unsigned)(wave >> 1) * 1024u);
+                         (NSF == 1 ? 0u : (unsigned)(dw >> 1) * 1024u);
     dma16_at(d.rs, d.sf_voff, sf_wave ? dst : sf_dummy);
   };
 
@@ -578,10 +590,12 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   int s = 0;                     // global step index: selects the ring stage
   if (my_tiles > 0) {
     cur = make_tile<kBM, kBN>(p, t0);
-    const Dma d0 = dma_setup(geo(lane), cur, 0, true, lds0);
-    dma_sf(d0);
+    if (NW == 4 || producer) {
+      const Dma d0 = dma_setup(geo(lane), cur, 0, true, lds0);
+      dma_sf(d0);
 #pragma unroll
-    for (int q = 0; q < Y::kDma; ++q) dma_ab(d0, q);
+      for (int q = 0; q < Y::kDma; ++q) dma_ab(d0, q);
+    }
   }
 
   // FP8 datapath: one K step of tile `cur`; queues the DMA of the next step
@@ -900,7 +914,10 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   // first kStages - 2 steps ("hold") the previous tile's C stores may stay in
   // flight as well, since the DMA waited for went out before that tile's
   // epilogue.  Past the end of the work the DMAs go through empty resources,
-  // so every step queues the same instructions and the counts hold.
+  // so every step queues the same instructions and the counts hold.  With 8
+  // waves the same DMA, stage for stage, comes from the DMA waves (produce,
+  // below), which do the waiting, and the computing waves only meet them at
+  // the barriers.
   constexpr int kDmaPerStep = Y::kDma + 1;
   int di = 0, dkt = 0;  // the step whose DMA goes out next: the workgroup's tile di, K step dkt
   Tile dtile = cur;
@@ -917,16 +934,18 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
   // steps 1 .. kStages - 2 join step 0 (queued above) before anything is read
   auto prime_ring = [&]() __attribute__((always_inline)) {
     const Geo g = geo(lane_opaque());
-    (void)next_target();  // step 0
+    if constexpr (NW == 4) {
+      (void)next_target();  // step 0
 #pragma unroll
-    for (int j = 1; j + 1 < kStages; ++j) {
-      const Tgt tg = next_target();
-      const Dma d = dma_setup(g, tg.t, tg.kt, tg.live, lds0 + stage_at(j));
-      dma_sf(d);
+      for (int j = 1; j + 1 < kStages; ++j) {
+        const Tgt tg = next_target();
+        const Dma d = dma_setup(g, tg.t, tg.kt, tg.live, lds0 + stage_at(j));
+        dma_sf(d);
 #pragma unroll
-      for (int q = 0; q < Y::kDma; ++q) dma_ab(d, q);
+        for (int q = 0; q < Y::kDma; ++q) dma_ab(d, q);
+      }
+      wait_vm<0>();
     }
-    wait_vm<0>();
     barrier();
     load_sf(g, lds, 0);
     load_raw(g, lds, 0);
@@ -963,14 +982,16 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
       } else {
         if (n == 1 || n == 3) load_raw(g, st, (n + 3) / 2);
       }
-      if (n == 1) {
-        d1 = dma_setup(g, tg.t, tg.kt, tg.live, lds0 + stage_at(s + kStages - 1));
-        dma_sf(d1);
-      }
-      if (n >= 1 && n <= 3) {
+      if constexpr (NW == 4) {
+        if (n == 1) {
+          d1 = dma_setup(g, tg.t, tg.kt, tg.live, lds0 + stage_at(s + kStages - 1));
+          dma_sf(d1);
+        }
+        if (n >= 1 && n <= 3) {
 #pragma unroll
-        for (int q = 0; q < kPer1; ++q)
-          if ((n - 1) * kPer1 + q < Y::kDma) dma_ab(d1, (n - 1) * kPer1 + q);
+          for (int q = 0; q < kPer1; ++q)
+            if ((n - 1) * kPer1 + q < Y::kDma) dma_ab(d1, (n - 1) * kPer1 + q);
+        }
       }
       if (n < kSlices - 1) {
         if ((n + 1) % kSpc == 0) scales(g, (n + 1) / kSpc, 0);
@@ -999,7 +1020,8 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
       }
       __builtin_amdgcn_sched_barrier(0);
       if (n == kSlices - 3) {
-        wait_vm<kWait>();
+        // (8 waves: the DMA waves have waited for step s+1's DMA before it)
+        if constexpr (NW == 4) wait_vm<kWait>();
         barrier();  // B'
         load_sf(g, stn, nkt);
         load_raw(g, stn, 0);
@@ -1011,26 +1033,72 @@ __global__ __launch_bounds__(kThreads, 1) void mxgemm_amax_big_kernel(Params p) 
     ++s;
   };
 
+  // 8 waves: the DMA waves' whole life.  Steps 0 .. kStages - 2 go out
+  // before the prime's barrier; then, between B' of step s - 1 and B' of step
+  // s, the DMA of step s + kStages - 1 into the stage every compute wave
+  // finished reading before B' of step s - 1, and a wait for their own DMA of
+  // step s + 1 (the later two steps' stay in flight) ahead of B' of step s.
+  // That is the compute waves' barrier sequence: the prime's, then one B' per
+  // step.  Past the work the DMA goes through empty resources.
+  auto produce = [&]() __attribute__((always_inline)) {
+    if (my_tiles == 0) return;
+    {
+      const Geo g = geo(lane_opaque());
+      (void)next_target();  // step 0 (queued above)
+#pragma unroll
+      for (int j = 1; j + 1 < kStages; ++j) {
+        const Tgt tg = next_target();
+        const Dma d = dma_setup(g, tg.t, tg.kt, tg.live, lds0 + stage_at(j));
+        dma_sf(d);
+#pragma unroll
+        for (int q = 0; q < Y::kDma; ++q) dma_ab(d, q);
+      }
+    }
+    wait_vm<0>();
+    barrier();
+    const int64_t steps = (int64_t)my_tiles * p.ksteps;
+    for (int64_t t = 0; t < steps; ++t) {
+      const Geo g = geo(lane_opaque());
+      const Tgt tg = next_target();
+      const Dma d = dma_setup(g, tg.t, tg.kt, tg.live, lds0 + stage_at((int)(t & (kStages - 1)) + kStages - 1));
+      dma_sf(d);
+#pragma unroll
+      for (int q = 0; q < Y::kDma; ++q) dma_ab(d, q);
+      wait_vm<(kStages - 2) * kDmaPerStep>();
+      barrier();
+    }
+  };
+  // the compute waves' DMA target of a step (8 waves: none, the DMA waves
+  // queue it)
+  auto ring_target = [&]() {
+    if constexpr (NW == 4) return next_target();
+    else return Tgt{cur, 0, false};
+  };
+
   const std::true_type yes;
   const std::false_type no;
   if constexpr (MODE == kModeBf16 && kStages > 2) {
-    if (my_tiles > 0) prime_ring();
-    for (int i = 0; i < my_tiles; ++i) {
-      const bool more = i + 1 < my_tiles;
-      const Tile nxt = more ? make_tile<kBM, kBN>(p, t0 + (i + 1) * G) : cur;
-      const int ks = p.ksteps;
-      auto nk = [&](int kt) { return kt + 1 < ks ? kt + 1 : 0; };
-      step_ring(yes, yes, nk(0), next_target());
-      int kt = 1;
+    if (producer) {
+      produce();
+    } else {
+      if (my_tiles > 0) prime_ring();
+      for (int i = 0; i < my_tiles; ++i) {
+        const bool more = i + 1 < my_tiles;
+        const Tile nxt = more ? make_tile<kBM, kBN>(p, t0 + (i + 1) * G) : cur;
+        const int ks = p.ksteps;
+        auto nk = [&](int kt) { return kt + 1 < ks ? kt + 1 : 0; };
+        step_ring(yes, yes, nk(0), ring_target());
+        int kt = 1;
 #pragma unroll
-      for (int h = 1; h + 2 < kStages; ++h)
-        if (kt < ks) {
-          step_ring(no, yes, nk(kt), next_target());
-          ++kt;
-        }
-      for (; kt < ks; ++kt) step_ring(no, no, nk(kt), next_target());
-      store_all(store_ctx(cur));
-      cur = nxt;
+        for (int h = 1; h + 2 < kStages; ++h)
+          if (kt < ks) {
+            step_ring(no, yes, nk(kt), ring_target());
+            ++kt;
+          }
+        for (; kt < ks; ++kt) step_ring(no, no, nk(kt), ring_target());
+        store_all(store_ctx(cur));
+        cur = nxt;
+      }
     }
   } else {
   if constexpr (MODE == kModeBf16) {

@@ -108,9 +108,11 @@ enum {
   MXG_FLAG_FP8_MFMA = 2u,
   /* Force the tile size instead of the automatic choice (for tests and
      tuning).  TILE_128: 128x128 tiles; TILE_256: 256x256 tiles; one
-     workgroup of 4 waves per CU either way.  Both sizes compute every
-     output the same way, so results agree bit for bit.  Ignored when K == 0.
-     Setting both is an error. */
+     workgroup per CU either way, of 4 computing waves (128x128 tiles on the
+     default path, FP4 at sf = 16 aside: and 4 more that only stream the
+     operands into LDS).  Both sizes compute every output the same way, so
+     results agree bit for bit.  Ignored when K == 0.  Setting both is an
+     error. */
   MXG_FLAG_TILE_128 = 4u,
   MXG_FLAG_TILE_256 = 8u,
   /* A 16-bit C ("GEMM + Amax (SM100)", section "Parameters": the C tensor
