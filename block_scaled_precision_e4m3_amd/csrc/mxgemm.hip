@@ -133,19 +133,21 @@ bool on_device(const void* p, int dev) {
   return attr.device == dev;
 }
 
-// Tile shapes, one workgroup of 4 waves per CU either way (mxgemm_big.hpp):
-// 256x256 (waves of 128x128) or 128x128 (waves of 64x64).  A 256x256 tile
-// moves half the L2->LDS bytes per flop and converts half the operand bytes
-// per MFMA, so it runs a tile's worth of flops faster; 128x128 tiles spread a
-// small problem over more CUs.  The choice compares the time of the rounds of
-// tiles the CUs run, a 128x128 tile costing kSmallCost of a 256x256 tile's
-// (which has four times its flops).  kind 3 is the zero fill of K == 0.
+// Tile shapes, one workgroup per CU either way (mxgemm_big.hpp): 256x256 (4
+// waves of 128x128) or 128x128 (4 computing waves of 64x64 and 4 DMA waves).
+// A 256x256 tile moves half the L2->LDS bytes per flop and converts half the
+// operand bytes per MFMA, so it runs a tile's worth of flops faster; 128x128
+// tiles spread a small problem over more CUs.  The choice compares the time
+// of the rounds of tiles the CUs run, a 128x128 tile costing kSmallCost of a
+// 256x256 tile's (which has four times its flops; measured on MI355X: 0.30
+// on the 4000x7168x2048 and 8192x24576x1536 problems, each run both ways).
+// kind 3 is the zero fill of K == 0.
 struct Config {
   int kind;  // 0: 128x128 tiles, 1: 256x256 tiles, 3: K == 0
   int tile_m, tile_n, per_cu;
 };
 constexpr Config kT128 = {0, 128, 128, 1}, kT256 = {1, 256, 256, 1}, kZero = {3, 128, 128, 1};
-constexpr double kSmallCost = 0.35;
+constexpr double kSmallCost = 0.30;
 
 Config choose(int64_t M, int64_t N, int64_t K, int64_t L, int cus) {
   if (K == 0) return kZero;
