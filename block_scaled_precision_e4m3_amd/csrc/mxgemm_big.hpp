@@ -28,9 +28,8 @@
 //   direct global->LDS DMA, the step's E8M0 atoms beside the tile.  Per
 //   128-K step a 256x256 tile moves 64 KB for 8.4 M multiply-adds, a
 //   128x128 tile 32 KB for 2.1 M.  The 4-stage ring's DMA comes from 4 more
-//   waves that do nothing else: a wave whose DMA finds the vector-memory
-//   queue full stops issuing until it drains, which, on the computing waves,
-//   would stall their MFMAs for the operand stream (a 128x128 tile moves
+//   waves that do nothing else, so that a DMA instruction waiting for room in
+//   the vector-memory queue holds up no MFMA issue (a 128x128 tile moves
 //   twice the bytes per flop of a 256x256 one).  The 256x256 waves hold all
 //   512 registers of their SIMD, leaving no room for a second wave.
 // * bf16 step: 8 MFMA slices of 16 K; each slice's conversions run under the
