@@ -303,7 +303,14 @@ def test_back_to_back_calls_bitwise_equal(lib, M, N, K, sf):
     check_c(outs[0][0][0, rows], c_ref, s_ref, "back-to-back rows")
 
 
-@pytest.mark.parametrize("M,N,K,L,sf,fa,fb", [(300, 520, 592, 2, 32, E4, E4), (1000, 772, 1040, 1, 16, E5, E4)])
+@pytest.mark.parametrize("M,N,K,L,sf,fa,fb", [
+    (300, 520, 592, 2, 32, E4, E4),
+    (1000, 772, 1040, 1, 16, E5, E4),
+    # more 128x128 tiles (544) than workgroups: the operand stream runs on
+    # across tiles, with one K step per tile and with a ragged eighth
+    (2100, 4000, 112, 1, 32, E4, E4),
+    (2100, 4000, 1008, 1, 16, E5, E4),
+])
 def test_tile_sizes_agree_bitwise(lib, M, N, K, L, sf, fa, fb):
     # Both tile sizes run the same per-output computation (the same K order
     # through the same MFMA slices), so their C and Amax agree bit for bit.
