@@ -235,16 +235,17 @@ template <int CT>
 constexpr bool kCMajorM = CT == 3;
 
 // Four consecutive outputs of one C row, given in float32, stored as C's
-// element type at byte offset voff + soff of resource rc.
-template <int CT>
+// element type at byte offset voff + soff of resource rc, with cache policy
+// bits CP (2: non-temporal).
+template <int CT, int CP = 0>
 __device__ __forceinline__ void store_c4(const v4f& v, __amdgpu_buffer_rsrc_t rc, int voff, int soff) {
   if constexpr (CT == 0 || CT == 3)
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), rc, voff, soff, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), rc, voff, soff, CP);
   else if constexpr (CT == 1)
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, __builtin_convertvector(v, v4bf)), rc, voff, soff,
-                                          0);
+                                          CP);
   else
-    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, __builtin_convertvector(v, v4h)), rc, voff, soff, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, __builtin_convertvector(v, v4h)), rc, voff, soff, CP);
 }
 
 // Eight packed E2M1 elements (one dword, element 2i in the low nibble of byte
