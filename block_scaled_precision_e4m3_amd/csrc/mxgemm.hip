@@ -650,8 +650,13 @@ int mxgemm_proj_rope_mxfp8(const float* Y, const uint16_t* cos_bf16, const uint1
       break;
     }
   const int64_t grid = cdiv(p.num_tiles, p.per_wg);
-  hipLaunchKernelGGL(mxg::rope::proj_rope_mxfp8_kernel, dim3((unsigned)grid), dim3(mxg::rope::kThreads),
-                     (unsigned)mxg::rope::lds_bytes(p.D, p.QR, p.per_wg), (hipStream_t)stream, p);
+  const unsigned lds = (unsigned)mxg::rope::lds_bytes(p.D, p.QR, p.per_wg);
+  if (p.D == 192 && p.QR == 64)  // the projection page's head: constant index arithmetic
+    hipLaunchKernelGGL((mxg::rope::proj_rope_mxfp8_kernel<192, 64>), dim3((unsigned)grid), dim3(mxg::rope::kThreads),
+                       lds, (hipStream_t)stream, p);
+  else
+    hipLaunchKernelGGL((mxg::rope::proj_rope_mxfp8_kernel<0, 0>), dim3((unsigned)grid), dim3(mxg::rope::kThreads),
+                       lds, (hipStream_t)stream, p);
   return hipGetLastError() == hipSuccess ? MXG_OK : MXG_ERR_LAUNCH;
 }
 

@@ -62,19 +62,24 @@ inline size_t lds_bytes(int D, int QR, int per_wg) {
 
 __device__ __forceinline__ float bf16_bits_to_float(uint16_t b) { return __uint_as_float((unsigned)b << 16); }
 
+// DC, QC: the head size and rotary width as compile-time constants (the
+// projection page's 192 and 64), so that the index arithmetic divides by
+// constants; 0, 0 takes both from p.
+template <int DC, int QC>
 __global__ __launch_bounds__(kThreads) void proj_rope_mxfp8_kernel(RParams p) {
   // dynamic LDS, lds_bytes(D, QR): the tile (32 x (D + 4) floats), the column
   // exponents (D ints), the cos and sin rows (32 x QR bf16 each); every part
   // starts 16-byte aligned (D % 32 == 0, QR even)
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
   float* z = reinterpret_cast<float*>(dyn);
-  int* ecol = reinterpret_cast<int*>(z + 32 * (p.D + 4));
-  uint16_t* csl = reinterpret_cast<uint16_t*>(ecol + p.D);
-  uint16_t* snl = csl + 32 * p.QR;
-  uint8_t* rsl = reinterpret_cast<uint8_t*>(snl + 32 * p.QR);  // the run's row scale bytes, (32, per_wg * nb)
+  const int D = DC ? DC : p.D, QR = DC ? QC : p.QR;
+  int* ecol = reinterpret_cast<int*>(z + 32 * (D + 4));
+  uint16_t* csl = reinterpret_cast<uint16_t*>(ecol + D);
+  uint16_t* snl = csl + 32 * QR;
+  uint8_t* rsl = reinterpret_cast<uint8_t*>(snl + 32 * QR);  // the run's row scale bytes, (32, per_wg * nb)
   const int t = threadIdx.x;
-  const int D = p.D, P = p.D + 4, HD = p.H * p.D;
-  const int nope = p.D - p.QR, R = p.QR / 2, nb = p.D / 32;
+  const int P = D + 4, HD = p.H * D;
+  const int nope = D - QR, R = QR / 2, nb = D / 32;
   const int q4 = D / 4;  // float4 groups per token (a multiple of 8: D % 32 == 0)
   // a contiguous run of tiles per workgroup: consecutive heads of one token
   // block, so that a workgroup writes whole 128-byte lines of the code rows
@@ -88,34 +93,74 @@ __global__ __launch_bounds__(kThreads) void proj_rope_mxfp8_kernel(RParams p) {
   const int w = (G & 7) == 0 ? (b & 7) * (G >> 3) + (b >> 3) : b;
   const int a0 = w * p.per_wg, a1 = min(a0 + p.per_wg, p.num_tiles);
   const int run_bytes = (a1 - a0) * nb;  // a token's row scale bytes over the run (per_wg divides H)
+  // thread t takes the tile's 16-byte groups f = t + kThreads k (token
+  // f / q4, features 4 (f % q4) ..), the same in every tile, so their
+  // offsets are worked out once: in Y and in the code arrays (both (tokens,
+  // H * D) elements) relative to the tile's first element, and in LDS.  It
+  // loads them one tile ahead: tile a + 1's loads go out right after tile a
+  // reaches LDS and land while tile a is processed.  The phases meet at
+  // barriers that wait for LDS operations only, so neither those loads nor
+  // the code stores hold them.
+  constexpr int kMaxF4 = 32 * (kMaxD / 4) / kThreads;
+  constexpr int kMaxPairs = 32 * (kMaxQR / 2) / kThreads;
+  int fr[kMaxF4], fc[kMaxF4], zo[kMaxF4];
+  int64_t go[kMaxF4];
+#pragma unroll
+  for (int k = 0; k < kMaxF4; ++k) {
+    const int f = t + kThreads * k;
+    fr[k] = f / q4;
+    fc[k] = f - fr[k] * q4;
+    zo[k] = fr[k] * P + 4 * fc[k];
+    go[k] = (int64_t)fr[k] * HD + 4 * fc[k];
+  }
+  const int ngroups = 32 * q4;
+  float4 nx[kMaxF4];
+  auto fetch = [&](int a) {
+    const float* y = p.Y + (int64_t)(a / p.H) * 32 * HD + (int64_t)(a % p.H) * D;
+#pragma unroll
+    for (int k = 0; k < kMaxF4; ++k)
+      if (t + kThreads * k < ngroups) nx[k] = *reinterpret_cast<const float4*>(y + go[k]);
+  };
+  if (a0 < a1) fetch(a0);
+  int cs_tb = -1;  // the token block whose cos / sin rows are in LDS
   for (int a = a0; a < a1; ++a) {
     const int h = a % p.H, tb = a / p.H;
     const int64_t row0 = (int64_t)tb * 32;
-    __syncthreads();  // the previous tile's LDS reads are done
+    const int64_t base = row0 * HD + (int64_t)h * D;  // the tile's first element in Y and the code arrays
+    barrier();  // the previous tile's LDS reads are done
     // the tile into LDS, rotary features de-interleaved on the way: feature
     // nope + 2i (a_i) to position nope + i, nope + 2i + 1 (b_i) to nope + R + i
-    for (int f = t; f < 32 * q4; f += kThreads) {
-      const int r = f / q4, c = f - r * q4;
-      const float4 v = *reinterpret_cast<const float4*>(p.Y + (row0 + r) * HD + (int64_t)h * D + 4 * c);
+#pragma unroll
+    for (int k = 0; k < kMaxF4; ++k) {
+      if (t + kThreads * k >= ngroups) continue;
+      const int c = fc[k];
+      const float4 v = nx[k];
       if (4 * c + 3 < nope) {
-        *reinterpret_cast<float4*>(z + r * P + 4 * c) = v;
+        *reinterpret_cast<float4*>(z + zo[k]) = v;
       } else {
         const float e4[4] = {v.x, v.y, v.z, v.w};
+        float* zr = z + fr[k] * P;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int d = 4 * c + j, k = d - nope;
-          z[r * P + (k < 0 ? d : nope + (k & 1) * R + (k >> 1))] = e4[j];
+          const int d = 4 * c + j, kk = d - nope;
+          zr[kk < 0 ? d : nope + (kk & 1) * R + (kk >> 1)] = e4[j];
         }
       }
     }
-    // the 32 tokens' cos / sin rows: 32 * QR * 2 contiguous bytes per table
-    for (int f = t; f < 4 * p.QR; f += kThreads) {
-      reinterpret_cast<uint4*>(csl)[f] = reinterpret_cast<const uint4*>(p.cs + row0 * p.QR)[f];
-      reinterpret_cast<uint4*>(snl)[f] = reinterpret_cast<const uint4*>(p.sn + row0 * p.QR)[f];
+    if (a + 1 < a1) fetch(a + 1);
+    // the 32 tokens' cos / sin rows (32 * QR * 2 contiguous bytes per table),
+    // once per token block
+    if (tb != cs_tb) {
+      for (int f = t; f < 4 * QR; f += kThreads) {
+        reinterpret_cast<uint4*>(csl)[f] = reinterpret_cast<const uint4*>(p.cs + row0 * QR)[f];
+        reinterpret_cast<uint4*>(snl)[f] = reinterpret_cast<const uint4*>(p.sn + row0 * QR)[f];
+      }
+      cs_tb = tb;
     }
-    __syncthreads();
+    barrier();
     // RoPE: each thread rotates its own pairs (i, R + i) in place
-    for (int f = t; f < 32 * R; f += kThreads) {
+#pragma unroll
+    for (int k = 0; k < kMaxPairs; ++k) {
       // each product and the sum rounded on its own: a fused multiply-add
       // (which the compiler forms by default, also from __fmul_rn /
       // __fsub_rn, whose own operations carry the contraction flag) rounds
@@ -123,16 +168,18 @@ __global__ __launch_bounds__(kThreads) void proj_rope_mxfp8_kernel(RParams p) {
       // flip a code.  Plain operators here, in a scope where contraction is
       // off.
 #pragma clang fp contract(off)
+      const int f = t + kThreads * k;
+      if (f >= 32 * R) continue;
       const int r = f / R, i = f - r * R;
       float* zr = z + r * P + nope;
       const float av = zr[i], bv = zr[R + i];
-      const float c1 = bf16_bits_to_float(csl[r * p.QR + i]), s1 = bf16_bits_to_float(snl[r * p.QR + i]);
-      const float c2 = bf16_bits_to_float(csl[r * p.QR + R + i]), s2 = bf16_bits_to_float(snl[r * p.QR + R + i]);
+      const float c1 = bf16_bits_to_float(csl[r * QR + i]), s1 = bf16_bits_to_float(snl[r * QR + i]);
+      const float c2 = bf16_bits_to_float(csl[r * QR + R + i]), s2 = bf16_bits_to_float(snl[r * QR + R + i]);
       const float ac = av * c1, bs = bv * s1, bc = bv * c2, as = av * s2;
       zr[i] = ac - bs;
       zr[R + i] = bc + as;
     }
-    __syncthreads();
+    barrier();
     // column blocks: the exponent of feature d over the 32 tokens
     for (int d = t; d < D; d += kThreads) {
       float bm = 0.f;
@@ -142,21 +189,24 @@ __global__ __launch_bounds__(kThreads) void proj_rope_mxfp8_kernel(RParams p) {
       ecol[d] = e;
       p.col_scales[((int64_t)tb * p.H + h) * D + d] = (uint8_t)(e + 127);
     }
-    __syncthreads();
+    barrier();
     // both directions' codes: thread (r, c) holds features 4c..4c+3 of token
     // r; the 8 threads of a row block are consecutive lanes (q4 and the
     // thread count are multiples of 8, so the 8 lanes of a group take part in
-    // a pass together or not at all)
-    for (int f = t; f < 32 * q4; f += kThreads) {
-      const int r = f / q4, c = f - r * q4;
-      const float4 v = *reinterpret_cast<const float4*>(z + r * P + 4 * c);
+    // a pass together or not at all).  The row block's 4 values share one
+    // exponent and convert with it as the scale operand (bitwise ldexp then
+    // convert).
+#pragma unroll
+    for (int k = 0; k < kMaxF4; ++k) {
+      if (t + kThreads * k >= ngroups) continue;
+      const int r = fr[k], c = fc[k];
+      const float4 v = *reinterpret_cast<const float4*>(z + zo[k]);
       float bm = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
 #pragma unroll
       for (int sh = 1; sh < 8; sh <<= 1) bm = fmaxf(bm, __shfl_xor(bm, sh));
       const int e = quant::block_exponent<0>(bm);
-      const int64_t o = ((row0 + r) * p.H + h) * (int64_t)D + 4 * c;
-      *reinterpret_cast<unsigned*>(p.row_codes + o) =
-          quant::codes4<0>(ldexpf(v.x, -e), ldexpf(v.y, -e), ldexpf(v.z, -e), ldexpf(v.w, -e));
+      const int64_t o = base + go[k];
+      *reinterpret_cast<unsigned*>(p.row_codes + o) = quant::codes4_e4m3_exp(v.x, v.y, v.z, v.w, e);
       if ((c & 7) == 0) rsl[r * run_bytes + (a - a0) * nb + (c >> 3)] = (uint8_t)(e + 127);
       *reinterpret_cast<unsigned*>(p.col_codes + o) =
           quant::codes4<0>(ldexpf(v.x, -ecol[4 * c]), ldexpf(v.y, -ecol[4 * c + 1]), ldexpf(v.z, -ecol[4 * c + 2]),
@@ -166,7 +216,7 @@ __global__ __launch_bounds__(kThreads) void proj_rope_mxfp8_kernel(RParams p) {
   // the run's row scales: per token, run_bytes contiguous bytes (heads h0 ..)
   // in one coalesced pass instead of a scattered byte per row block
   if (a0 < a1) {
-    __syncthreads();
+    barrier();
     const int h0 = a0 % p.H;
     const int64_t row0 = (int64_t)(a0 / p.H) * 32;
     for (int f = t; f < 32 * run_bytes; f += kThreads) {
