@@ -102,7 +102,6 @@ __global__ __launch_bounds__(kThreads) void proj_rope_mxfp8_kernel(RParams p) {
   // barriers that wait for LDS operations only, so neither those loads nor
   // the code stores hold them.
   constexpr int kMaxF4 = 32 * (kMaxD / 4) / kThreads;
-  constexpr int kMaxPairs = 32 * (kMaxQR / 2) / kThreads;
   int fr[kMaxF4], fc[kMaxF4], zo[kMaxF4];
   int64_t go[kMaxF4];
 #pragma unroll
@@ -128,26 +127,6 @@ __global__ __launch_bounds__(kThreads) void proj_rope_mxfp8_kernel(RParams p) {
     const int64_t row0 = (int64_t)tb * 32;
     const int64_t base = row0 * HD + (int64_t)h * D;  // the tile's first element in Y and the code arrays
     barrier();  // the previous tile's LDS reads are done
-    // the tile into LDS, rotary features de-interleaved on the way: feature
-    // nope + 2i (a_i) to position nope + i, nope + 2i + 1 (b_i) to nope + R + i
-#pragma unroll
-    for (int k = 0; k < kMaxF4; ++k) {
-      if (t + kThreads * k >= ngroups) continue;
-      const int c = fc[k];
-      const float4 v = nx[k];
-      if (4 * c + 3 < nope) {
-        *reinterpret_cast<float4*>(z + zo[k]) = v;
-      } else {
-        const float e4[4] = {v.x, v.y, v.z, v.w};
-        float* zr = z + fr[k] * P;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int d = 4 * c + j, kk = d - nope;
-          zr[kk < 0 ? d : nope + (kk & 1) * R + (kk >> 1)] = e4[j];
-        }
-      }
-    }
-    if (a + 1 < a1) fetch(a + 1);
     // the 32 tokens' cos / sin rows (32 * QR * 2 contiguous bytes per table),
     // once per token block
     if (tb != cs_tb) {
@@ -156,29 +135,49 @@ __global__ __launch_bounds__(kThreads) void proj_rope_mxfp8_kernel(RParams p) {
         reinterpret_cast<uint4*>(snl)[f] = reinterpret_cast<const uint4*>(p.sn + row0 * QR)[f];
       }
       cs_tb = tb;
+      barrier();
     }
-    barrier();
-    // RoPE: each thread rotates its own pairs (i, R + i) in place
+    // the tile into LDS, RoPE applied on the way: a group of 4 features holds
+    // whole pairs (a_i, b_i) = (feature nope + 2i, nope + 2i + 1), since nope
+    // is even, and its thread writes the rotated a to position nope + i and b
+    // to nope + R + i of the rotary part
 #pragma unroll
-    for (int k = 0; k < kMaxPairs; ++k) {
-      // each product and the sum rounded on its own: a fused multiply-add
-      // (which the compiler forms by default, also from __fmul_rn /
-      // __fsub_rn, whose own operations carry the contraction flag) rounds
-      // a*c - b*s once, and under cancellation that moves the value and can
-      // flip a code.  Plain operators here, in a scope where contraction is
-      // off.
+    for (int k = 0; k < kMaxF4; ++k) {
+      if (t + kThreads * k >= ngroups) continue;
+      const int r = fr[k], c = fc[k];
+      const float4 v = nx[k];
+      if (4 * c + 3 < nope) {
+        *reinterpret_cast<float4*>(z + zo[k]) = v;
+      } else {
+        // each product and the sum rounded on its own: a fused multiply-add
+        // (which the compiler forms by default, also from __fmul_rn /
+        // __fsub_rn, whose own operations carry the contraction flag) rounds
+        // a*c - b*s once, and under cancellation that moves the value and
+        // can flip a code.  Plain operators here, in a scope where
+        // contraction is off.
 #pragma clang fp contract(off)
-      const int f = t + kThreads * k;
-      if (f >= 32 * R) continue;
-      const int r = f / R, i = f - r * R;
-      float* zr = z + r * P + nope;
-      const float av = zr[i], bv = zr[R + i];
-      const float c1 = bf16_bits_to_float(csl[r * QR + i]), s1 = bf16_bits_to_float(snl[r * QR + i]);
-      const float c2 = bf16_bits_to_float(csl[r * QR + R + i]), s2 = bf16_bits_to_float(snl[r * QR + R + i]);
-      const float ac = av * c1, bs = bv * s1, bc = bv * c2, as = av * s2;
-      zr[i] = ac - bs;
-      zr[R + i] = bc + as;
+        const float e4[4] = {v.x, v.y, v.z, v.w};
+        float* zr = z + r * P;
+        const uint16_t* cr = csl + r * QR;
+        const uint16_t* sr = snl + r * QR;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int d = 4 * c + j, kk = d - nope;
+          if (kk < 0) {
+            zr[d] = e4[j];
+          } else if ((kk & 1) == 0 && j < 3) {
+            const int i = kk >> 1;
+            const float av = e4[j], bv = e4[j + 1];
+            const float c1 = bf16_bits_to_float(cr[i]), s1 = bf16_bits_to_float(sr[i]);
+            const float c2 = bf16_bits_to_float(cr[R + i]), s2 = bf16_bits_to_float(sr[R + i]);
+            const float ac = av * c1, bs = bv * s1, bc = bv * c2, as = av * s2;
+            zr[nope + i] = ac - bs;
+            zr[nope + R + i] = bc + as;
+          }
+        }
+      }
     }
+    if (a + 1 < a1) fetch(a + 1);
     barrier();
     // column blocks: the exponent of feature d over the 32 tokens
     for (int d = t; d < D; d += kThreads) {
