@@ -189,27 +189,41 @@ __global__ __launch_bounds__(kThreads) void proj_rope_mxfp8_kernel(RParams p) {
       p.col_scales[((int64_t)tb * p.H + h) * D + d] = (uint8_t)(e + 127);
     }
     barrier();
-    // both directions' codes: thread (r, c) holds features 4c..4c+3 of token
-    // r; the 8 threads of a row block are consecutive lanes (q4 and the
-    // thread count are multiples of 8, so the 8 lanes of a group take part in
-    // a pass together or not at all).  The row block's 4 values share one
-    // exponent and convert with it as the scale operand (bitwise ldexp then
-    // convert).
+    // both directions' codes: thread (r, q) takes features 16q .. 16q + 15
+    // of token r (D / 16 threads per token, an even count, so a 32-feature
+    // row block is the lane pair q, q ^ 1 and one xor shuffle finds its
+    // maximum), and each direction's 16 codes leave as one 16-byte store.
+    // The row block's values share one exponent and convert with it as the
+    // scale operand (bitwise ldexp then convert).
+    {
+      const int nq = D / 16;
+      const int r = t / nq, q = t - r * nq;
+      if (r < 32) {
+        const float* zr = z + r * P + 16 * q;
+        float4 v[4];
 #pragma unroll
-    for (int k = 0; k < kMaxF4; ++k) {
-      if (t + kThreads * k >= ngroups) continue;
-      const int r = fr[k], c = fc[k];
-      const float4 v = *reinterpret_cast<const float4*>(z + zo[k]);
-      float bm = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+        for (int j = 0; j < 4; ++j) v[j] = *reinterpret_cast<const float4*>(zr + 4 * j);
+        float bm = 0.f;
 #pragma unroll
-      for (int sh = 1; sh < 8; sh <<= 1) bm = fmaxf(bm, __shfl_xor(bm, sh));
-      const int e = quant::block_exponent<0>(bm);
-      const int64_t o = base + go[k];
-      *reinterpret_cast<unsigned*>(p.row_codes + o) = quant::codes4_e4m3_exp(v.x, v.y, v.z, v.w, e);
-      if ((c & 7) == 0) rsl[r * run_bytes + (a - a0) * nb + (c >> 3)] = (uint8_t)(e + 127);
-      *reinterpret_cast<unsigned*>(p.col_codes + o) =
-          quant::codes4<0>(ldexpf(v.x, -ecol[4 * c]), ldexpf(v.y, -ecol[4 * c + 1]), ldexpf(v.z, -ecol[4 * c + 2]),
-                           ldexpf(v.w, -ecol[4 * c + 3]));
+        for (int j = 0; j < 4; ++j)
+          bm = fmaxf(bm, fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)), fmaxf(fabsf(v[j].z), fabsf(v[j].w))));
+        bm = fmaxf(bm, __shfl_xor(bm, 1));
+        const int e = quant::block_exponent<0>(bm);
+        uint4 rc, cc;
+        const int* ec = ecol + 16 * q;
+        unsigned* rcu = reinterpret_cast<unsigned*>(&rc);
+        unsigned* ccu = reinterpret_cast<unsigned*>(&cc);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          rcu[j] = quant::codes4_e4m3_exp(v[j].x, v[j].y, v[j].z, v[j].w, e);
+          ccu[j] = quant::codes4<0>(ldexpf(v[j].x, -ec[4 * j]), ldexpf(v[j].y, -ec[4 * j + 1]),
+                                    ldexpf(v[j].z, -ec[4 * j + 2]), ldexpf(v[j].w, -ec[4 * j + 3]));
+        }
+        const int64_t o = base + (int64_t)r * HD + 16 * q;
+        *reinterpret_cast<uint4*>(p.row_codes + o) = rc;
+        *reinterpret_cast<uint4*>(p.col_codes + o) = cc;
+        if ((q & 1) == 0) rsl[r * run_bytes + (a - a0) * nb + (q >> 1)] = (uint8_t)(e + 127);
+      }
     }
   }
   // the run's row scales: per token, run_bytes contiguous bytes (heads h0 ..)
