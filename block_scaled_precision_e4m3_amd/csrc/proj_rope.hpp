@@ -17,19 +17,20 @@
 //
 // One workgroup of 512 threads per (32-token block, head), in runs of
 // consecutive heads.  The 32 x D tile is read with 16-byte loads (each
-// token's D floats are contiguous) and parked in LDS at a pitch of D + 4
-// floats (rows stay 16-byte aligned, and a column read by 64 lanes hits 64
-// banks); the rotary features are de-interleaved on the way in (a_i to
-// position i of the rotary part, b_i to R + i), so that each thread then
-// rotates its own pairs in place.  The tokens' cos / sin rows come in with
-// 16-byte loads too.  Then one thread per feature finds its column block's
-// exponent, and finally thread (token r, features 4c..4c+3) makes both codes of its 4
-// values: the row block's maximum comes from the 8 threads of the block
-// (consecutive lanes, xor shuffles), the column exponents from LDS; each
-// direction's 4 codes leave as one dword store, consecutive threads writing
-// consecutive dwords of a token's row.  Row scale bytes collect in LDS over
-// the workgroup's run of heads and leave at its end, a token's bytes for the
-// whole run contiguous (scattered single bytes cost about 15% of the time).
+// token's D floats are contiguous), one tile ahead into registers, and parked
+// in LDS at a pitch of D + 4 floats (rows stay 16-byte aligned, and a column
+// read by 64 lanes hits 64 banks).  The tokens' cos / sin rows come in with
+// 16-byte loads, once per token block.  A 4-feature group holds whole rotary
+// pairs, so the thread that loaded it rotates them on the way into LDS (a_i
+// to position i of the rotary part, b_i to R + i).  Then one thread per
+// feature finds its column block's exponent, and finally thread (token r,
+// features 16q .. 16q + 15) makes both directions' codes: the row block's
+// maximum from one xor shuffle with the neighbouring lane, the column
+// exponents from LDS; each direction's 16 codes leave as one 16-byte store.
+// Row scale bytes collect in LDS over the workgroup's run of heads and leave
+// at its end, a token's bytes for the whole run contiguous (scattered single
+// bytes cost about 15% of the time).  The phases meet at barriers that wait
+// for LDS operations only.
 #pragma once
 
 #include "mx_quantize.hpp"
