@@ -131,7 +131,8 @@ __device__ __forceinline__ uint2 lds_tr8(const uint8_t* p) {
 // n-major C.  NW: waves per workgroup, 4, or 8 on the 128x128 ring (every
 // format but FP4 at sf = 16), where waves 4..7 only stream the operands into
 // the ring (each what wave w - 4 would queue) and waves 0..3 only compute and
-// store, so the compute waves never stall on a full vector-memory queue.
+// store, so no DMA instruction waiting for room in the vector-memory queue
+// holds up the computing waves.
 template <int SF, int FA, int FB, int MODE, int CT, int BT, int MJ = 0, int NW = 4>
 __global__ __launch_bounds__(64 * NW, 1) void mxgemm_amax_big_kernel(Params p) {
   // FA = FB = 2: packed FP4 (E2M1), bf16 datapath, sf = 32 (the host enforces it)
@@ -1038,11 +1039,12 @@ __global__ __launch_bounds__(64 * NW, 1) void mxgemm_amax_big_kernel(Params p) {
 
   // 8 waves: the DMA waves' whole life.  Steps 0 .. kStages - 2 go out
   // before the prime's barrier; then, between B' of step s - 1 and B' of step
-  // s, the DMA of step s + kStages - 1 into the stage every compute wave
+  // s, the DMA of step s + kStages - 1 into the stage every computing wave
   // finished reading before B' of step s - 1, and a wait for their own DMA of
-  // step s + 1 (the later two steps' stay in flight) ahead of B' of step s.
-  // That is the compute waves' barrier sequence: the prime's, then one B' per
-  // step.  Past the work the DMA goes through empty resources.
+  // step s + 1 (the DMA of the two later steps stays in flight) ahead of B'
+  // of step s.  That is the computing waves' barrier sequence: the prime's,
+  // then one B' per step.  Past the work the DMA goes through empty
+  // resources.
   auto produce = [&]() __attribute__((always_inline)) {
     if (my_tiles == 0) return;
     {
@@ -1071,7 +1073,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mxgemm_amax_big_kernel(Params p) {
       barrier();
     }
   };
-  // the compute waves' DMA target of a step (8 waves: none, the DMA waves
+  // the computing waves' DMA target of a step (8 waves: none, the DMA waves
   // queue it)
   auto ring_target = [&]() {
     if constexpr (NW == 4) return next_target();
