@@ -9,7 +9,9 @@ preset value above or below the result, or a bfloat16 / float16 C ("GEMM +
 Amax (SM100)", sections "Equations" and "Parameters").  Each case checks
 every C element and Amax against the oracle at the stated tolerance (a
 16-bit C: bit for bit the round-to-nearest-even of the library's float32 C,
-which meets the tolerance), and that nothing past C was written.
+which meets the tolerance), and that nothing past C was written.  Thirty
+more draw packed FP4 (E2M1) operands, with the modes FP4 takes (K a multiple
+of 32; no 256x256 tiles at sf = 16; k-major operands).
 """
 
 import numpy as np
@@ -49,6 +51,27 @@ def _cases(n=90, seed=2024):
 
 
 CASES = _cases()
+FP4_MODES = ["plain", "c_mmajor", "accumulate_down", "c_bf16", "accumulate_up"]
+
+
+def _fp4_cases(n=30, seed=4048):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        mode = FP4_MODES[i % len(FP4_MODES)]
+        M = int(rng.integers(1, 521))
+        if mode == "c_mmajor":
+            M = 4 * max(1, M // 4)
+        N = 4 * int(rng.integers(1, 131))
+        K = 32 * int(rng.integers(1, 40))
+        L = int(rng.choice([1, 1, 2]))
+        sf = int(rng.choice([16, 32]))
+        tile = int(rng.choice([0, 4] if sf == 16 else [0, 4, 8]))
+        out.append((100 + i, mode, M, N, K, L, sf, W.FMT_E2M1, W.FMT_E2M1, tile))
+    return out
+
+
+FP4_CASES = _fp4_cases()
 
 
 @pytest.fixture(scope="module")
@@ -58,7 +81,7 @@ def lib():
     return lib
 
 
-@pytest.mark.parametrize("i,mode,M,N,K,L,sf,fa,fb,tile", CASES)
+@pytest.mark.parametrize("i,mode,M,N,K,L,sf,fa,fb,tile", CASES + FP4_CASES)
 def test_sweep_against_oracle(lib, i, mode, M, N, K, L, sf, fa, fb, tile):
     print(f"sweep case {i}: {mode} {M}x{N}x{K}x{L} sf={sf} fmts {fa},{fb} tile flag {tile}", flush=True)
     p = W.make_problem(M, N, K, L, sf, fa, fb, seed=1000 + i, dist="student_t3" if i % 2 else "normal")
