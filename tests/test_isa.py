@@ -11,7 +11,10 @@ here rather than trusted:
   5 wait states the DMA macro carries, which hold whatever came before);
 * no buffer or global memory instruction, compiler-made ones included, reads
   an SGPR that a VALU instruction wrote fewer than 5 wait states before it
-  in straight-line code.
+  in straight-line code;
+* the RoPE kernels and the GEMM with the projection epilogue hold no fused
+  multiply-add: the rotation rounds each product and the sum on its own, and
+  the compiler forms an FMA from such code unless contraction is off.
 
 The disassembly is of device code built in this repository from its sources.
 """
@@ -34,7 +37,7 @@ def _tool(name):
 
 
 @pytest.fixture(scope="module")
-def disasm(tmp_path_factory):
+def disasm_text(tmp_path_factory):
     if not os.path.exists(LIB):
         pytest.skip("libmxgemm.so is not built")
     objcopy, bundler, objdump = _tool("llvm-objcopy"), _tool("clang-offload-bundler"), _tool("llvm-objdump")
@@ -59,6 +62,12 @@ def disasm(tmp_path_factory):
                        check=True, capture_output=True)
         out += subprocess.run([objdump, "-d", "--mcpu=gfx950", "--no-show-raw-insn", code],
                               check=True, capture_output=True, text=True).stdout
+    return out
+
+
+@pytest.fixture(scope="module")
+def disasm(disasm_text):
+    out = disasm_text
     insts = []
     for line in out.split("\n"):
         text = line.split("//")[0].strip()
@@ -155,3 +164,31 @@ def test_no_valu_sgpr_to_vmem_hazard(disasm):
     bad, checked = _find_hazards(disasm)
     assert checked > 1000
     assert not bad, f"{len(bad)} VALU-SGPR -> VMEM hazards, e.g. {bad[:3]}"
+
+
+def test_rotation_kernels_hold_no_fused_multiply_add(disasm_text):
+    # functions by their "<symbol>:" labels; the RoPE kernels and the GEMM
+    # instantiations with the projection epilogue (C type 4, 256x256 tiles)
+    funcs = re.split(r"\n(?=[0-9a-f]+ <[^>]+>:)", disasm_text)
+    checked = 0
+    for f in funcs:
+        m = re.match(r"[0-9a-f]+ <([^>]+)>:", f)
+        if not m:
+            continue
+        name = m.group(1)
+        if "proj_rope_mxfp8_kernel" in name or "ELi4ELi256ELi0E" in name:
+            checked += 1
+            fused = _FUSED.findall(f)
+            assert not fused, f"{name}: {fused[:3]}"
+    assert checked >= 3, "expected the RoPE kernels and the projection-epilogue GEMMs"
+
+
+_FUSED = re.compile(r"\bv_(?:fma|fmac|mad|mac|pk_fma)\w*?_f32")
+
+
+def test_fused_multiply_add_pattern():
+    for inst in ("v_fma_f32 v1, v2, v3, v4", "v_fmac_f32_e32 v1, v2, v3", "v_pk_fma_f32 v[0:1], v[2:3], v[4:5], v[6:7]",
+                 "v_mad_f32 v1, v2, v3, v4", "v_fma_mix_f32 v1, v2, v3, v4"):
+        assert _FUSED.search(inst), inst
+    for inst in ("v_mad_u64_u32 v[0:1], s[0:1], v2, v3, 0", "v_mul_f32_e32 v1, v2, v3", "v_sub_f32_e32 v1, v2, v3"):
+        assert not _FUSED.search(inst), inst
