@@ -204,7 +204,7 @@ constexpr uint32_t kPlanMagic = 0x4D584731u;  // "MXG1"
 struct Prepared {
   uint32_t magic;
   int dev;                  // plans: the device the plan was made for
-  mxg::Params p;            // sizes and tiling; pointers filled at launch
+  mxg::Params p{};          // sizes and tiling; pointers filled at launch
   int sf, fa, fb, kind, ct;
   int mj;                   // bit 0: m-major A, bit 1: n-major B
   unsigned flags;
@@ -381,7 +381,7 @@ bool aligned16_all(std::initializer_list<const void*> ps) {
 int launch_projection(const void* A, const void* B, const uint8_t* SFA, const uint8_t* SFB, const uint16_t* cs,
                       const uint16_t* sn, uint8_t* rc, uint8_t* rsc, uint8_t* cc, uint8_t* csc, int64_t tokens,
                       int64_t H, int64_t D, int64_t QR, int64_t K, int sf, int fa, int fb, int cus, hipStream_t s) {
-  mxg::Params p;
+  mxg::Params p{};  // every pointer the launch does not set stays null
   memset(&p, 0, sizeof(p));
   p.A = static_cast<const uint8_t*>(A);
   p.B = static_cast<const uint8_t*>(B);
