@@ -13,6 +13,10 @@
 * Same-sign data with long K, where the float32 accumulation error is
   largest: the error must stay within the bound the header states as a
   function of K, and within the contract bound up to K = 2048.
+* Amax across workgroups: every workgroup issues at most one atomic and skips
+  it when Amax already holds its maximum.  With every output equal, and with
+  one outlier row in the first, a middle or the last tile (one-round and
+  multi-round grids), Amax must be the closed-form maximum.
 """
 
 import numpy as np
@@ -185,3 +189,30 @@ def test_same_sign_long_k(lib, K, tile):
     if K <= 2048:
         check_c(c, c_ref, s_ref, f"same sign K={K}")
         check_amax(amax, amax_ref)
+
+
+@pytest.mark.parametrize("tile", list(TILES))
+@pytest.mark.parametrize("M,N", [(1024, 1024), (4096, 2304)])
+@pytest.mark.parametrize("where", ["none", "first", "middle", "last"])
+def test_amax_across_workgroups(lib, M, N, where, tile):
+    # Codes 1.0 (0x38) everywhere and scale bytes 127: every output is exactly K.
+    # An outlier row gets scale bytes 131 on A, so that row is exactly 16 K.
+    # 1024 x 1024 is one round of tiles; 4096 x 2304 at 128 x 128 tiles is 576
+    # tiles in three rounds (at 256 x 256, 144 tiles in one).
+    K, L, sf, fmt = 128, 1, 32, E4
+    kb = K // sf
+    a = np.full((L, M, K), 0x38, dtype=np.uint8)
+    b = np.full((L, N, K), 0x38, dtype=np.uint8)
+    sa = np.full((L, M, kb), 127, dtype=np.uint8)
+    sb = np.full((L, N, kb), 127, dtype=np.uint8)
+    row = {"none": None, "first": 0, "middle": M // 2 + 37, "last": M - 1}[where]
+    if row is not None:
+        sa[:, row, :] = 131
+    p = problem(a, b, sa, sb, sf, fmt, fmt)
+    c, amax = run_fetch(lib, p, tile)
+    expect = np.full((L, M, N), float(K), dtype=np.float32)
+    if row is not None:
+        expect[:, row, :] = 16.0 * K
+    assert np.array_equal(c, expect), f"C differs from the closed form ({where} outlier)"
+    assert float_bits(amax) == float_bits(16.0 * K if row is not None else float(K)), \
+        f"Amax {amax} ({where} outlier, {M}x{N}, {tile})"

@@ -323,3 +323,28 @@ def test_tile_sizes_agree_bitwise(lib, M, N, K, L, sf, fa, fb):
     c256, a256 = fetch(p, d)
     assert np.array_equal(c128.view(np.uint32), c256.view(np.uint32))
     assert float_bits(a128) == float_bits(a256)
+
+
+@pytest.mark.parametrize("M,N,K,L", [
+    (4000, 7168, 2048, 1),      # 448 tiles of 256x256: two rounds of 224
+    (8192, 24576, 1536, 1),     # 3072 tiles: twelve whole rounds
+    (2048, 2048, 2048, 1),      # 256 tiles of 128x128: one round
+    (1024, 1024, 128, 1),       # 64 tiles: fewer than the CUs
+    (2100, 4000, 112, 1),       # 544 tiles of 128x128: three rounds
+    (4096, 4096, 4096, 8),      # batched: 8 x 256 tiles of 256x256
+])
+def test_persistent_grid_is_balanced(lib, M, N, K, L):
+    # The persistent grid: the tile count when it fits the CUs; above that, the
+    # same number of rounds as a full grid, with the workgroups of a round
+    # rounded up to a multiple of 8 (so each XCD gets a contiguous run), so that
+    # every workgroup runs the same number of tiles give or take one.
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    tm, tn, grid = lib.mxgemm_launch_config(M, N, K, L, 32)
+    tiles = L * -(-M // tm) * -(-N // tn)
+    if tiles <= cus:
+        assert grid == tiles
+    else:
+        assert grid <= cus and grid % 8 == 0
+        assert -(-tiles // grid) == -(-tiles // cus), "as many rounds as a full grid"
+        per = [len(range(w, tiles, grid)) for w in range(grid)]
+        assert max(per) - min(per) <= 1
