@@ -213,6 +213,11 @@ __global__ __launch_bounds__(64 * NW, 1) void mxgemm_amax_big_kernel(Params p) {
     asm volatile("" : "+v"(ln));
     return ln;
   };
+  // The 128x128 ring's waves have registers to spare, so its steps (and its DMA
+  // waves) take the lane geometry computed once (20 VALU instructions fewer
+  // per step, 2-3% on 2048^3); the 256x256 steps recompute it from the opaque
+  // lane index, which keeps it out of their full register file.
+  const Geo g_ring = geo(lane);
 
   // --- DMA of one stage ------------------------------------------------------
   // A/B: wave w fills the 8-row groups w, w+4, ... of each tile, one
@@ -941,7 +946,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mxgemm_amax_big_kernel(Params p) {
   auto stage_at = [&](int step) { return (unsigned)(step & (kStages - 1)) * (unsigned)Y::kStage; };
   // steps 1 .. kStages - 2 join step 0 (queued above) before anything is read
   auto prime_ring = [&]() __attribute__((always_inline)) {
-    const Geo g = geo(lane_opaque());
+    const Geo g = g_ring;
     if constexpr (NW == 4) {
       (void)next_target();  // step 0
 #pragma unroll
@@ -972,7 +977,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mxgemm_amax_big_kernel(Params p) {
     constexpr int kWaitSteady = (kStages - 2) * kDmaPerStep;
     constexpr int kWait = kHold ? kWaitSteady + kNStores : kWaitSteady;
     static_assert(kWait <= 63, "vmcnt counts to 63");
-    const Geo g = geo(lane_opaque());
+    const Geo g = g_ring;
     const uint8_t* st = lds + stage_at(s);
     const uint8_t* stn = lds + stage_at(s + 1);
     constexpr int kSlices = kFp4 ? 16 : 8;
@@ -1052,7 +1057,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mxgemm_amax_big_kernel(Params p) {
   auto produce = [&]() __attribute__((always_inline)) {
     if (my_tiles == 0) return;
     {
-      const Geo g = geo(lane_opaque());
+      const Geo g = g_ring;
       (void)next_target();  // step 0 (queued above)
 #pragma unroll
       for (int j = 1; j + 1 < kStages; ++j) {
@@ -1067,7 +1072,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mxgemm_amax_big_kernel(Params p) {
     barrier();
     const int64_t steps = (int64_t)my_tiles * p.ksteps;
     for (int64_t t = 0; t < steps; ++t) {
-      const Geo g = geo(lane_opaque());
+      const Geo g = g_ring;
       const Tgt tg = next_target();
       const Dma d = dma_setup(g, tg.t, tg.kt, tg.live, lds0 + stage_at((int)(t & (kStages - 1)) + kStages - 1));
       dma_sf(d);
