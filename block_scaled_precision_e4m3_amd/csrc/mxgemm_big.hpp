@@ -213,11 +213,15 @@ __global__ __launch_bounds__(64 * NW, 1) void mxgemm_amax_big_kernel(Params p) {
     asm volatile("" : "+v"(ln));
     return ln;
   };
-  // The 128x128 ring's waves have registers to spare, so its steps (and its DMA
-  // waves) take the lane geometry computed once (20 VALU instructions fewer
-  // per step, 2-3% on 2048^3); the 256x256 steps recompute it from the opaque
-  // lane index, which keeps it out of their full register file.
-  const Geo g_ring = geo(lane);
+  // The lane geometry, computed once: the 128x128 ring's steps and DMA waves,
+  // and the 256x256 bf16 steps of k-major 8-bit operands with sf = 32 and a
+  // stored C, take it from here rather than rebuilding it every step from the
+  // opaque lane index (20-28 VALU instructions fewer per step: 2048^3 24.5 ->
+  // 23.6 us, 8192x24576x1536 525 -> 520 us).  The other 256x256 instances
+  // (sf = 16, FP4, m-major operands, the projection epilogue) would spill
+  // registers with it held, so they keep rebuilding it.
+  const Geo g_lane = geo(lane);
+  constexpr bool kHoistGeo = BT == 128 || (SF == 32 && !kFp4 && MJ == 0 && CT != 4);
 
   // --- DMA of one stage ------------------------------------------------------
   // A/B: wave w fills the 8-row groups w, w+4, ... of each tile, one
@@ -814,7 +818,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mxgemm_amax_big_kernel(Params p) {
   // after both have landed everywhere
   // (the projection epilogue queues step 1 from step 0 instead)
   auto prime = [&](const Tgt& n1) __attribute__((always_inline)) {
-    const Geo g = geo(lane_opaque());
+    const Geo g = kHoistGeo ? g_lane : geo(lane_opaque());
     if constexpr (CT != 4) {
       const Dma d1 = dma_setup(g, n1.t, n1.kt, n1.live, lds0 + (unsigned)Y::kStage);
       dma_sf(d1);
@@ -838,7 +842,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mxgemm_amax_big_kernel(Params p) {
     constexpr bool kFirst = decltype(first)::value;
     constexpr bool kLate = decltype(late)::value;
     constexpr bool kEarly = decltype(early)::value;
-    const Geo g = geo(lane_opaque());
+    const Geo g = kHoistGeo ? g_lane : geo(lane_opaque());
     const uint8_t* stn = lds + ((s & 1) ^ 1) * Y::kStage;
     const uint8_t* st = lds + (s & 1) * Y::kStage;
     // slices of 16 K per step: 8 (8-bit) or 16 (FP4); kSpc per 32-byte chunk
@@ -946,7 +950,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mxgemm_amax_big_kernel(Params p) {
   auto stage_at = [&](int step) { return (unsigned)(step & (kStages - 1)) * (unsigned)Y::kStage; };
   // steps 1 .. kStages - 2 join step 0 (queued above) before anything is read
   auto prime_ring = [&]() __attribute__((always_inline)) {
-    const Geo g = g_ring;
+    const Geo g = g_lane;
     if constexpr (NW == 4) {
       (void)next_target();  // step 0
 #pragma unroll
@@ -977,7 +981,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mxgemm_amax_big_kernel(Params p) {
     constexpr int kWaitSteady = (kStages - 2) * kDmaPerStep;
     constexpr int kWait = kHold ? kWaitSteady + kNStores : kWaitSteady;
     static_assert(kWait <= 63, "vmcnt counts to 63");
-    const Geo g = g_ring;
+    const Geo g = g_lane;
     const uint8_t* st = lds + stage_at(s);
     const uint8_t* stn = lds + stage_at(s + 1);
     constexpr int kSlices = kFp4 ? 16 : 8;
@@ -1057,7 +1061,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mxgemm_amax_big_kernel(Params p) {
   auto produce = [&]() __attribute__((always_inline)) {
     if (my_tiles == 0) return;
     {
-      const Geo g = g_ring;
+      const Geo g = g_lane;
       (void)next_target();  // step 0 (queued above)
 #pragma unroll
       for (int j = 1; j + 1 < kStages; ++j) {
@@ -1072,7 +1076,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mxgemm_amax_big_kernel(Params p) {
     barrier();
     const int64_t steps = (int64_t)my_tiles * p.ksteps;
     for (int64_t t = 0; t < steps; ++t) {
-      const Geo g = g_ring;
+      const Geo g = g_lane;
       const Tgt tg = next_target();
       const Dma d = dma_setup(g, tg.t, tg.kt, tg.live, lds0 + stage_at((int)(t & (kStages - 1)) + kStages - 1));
       dma_sf(d);
