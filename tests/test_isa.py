@@ -14,7 +14,10 @@ here rather than trusted:
   in straight-line code;
 * the RoPE kernels and the GEMM with the projection epilogue hold no fused
   multiply-add: the rotation rounds each product and the sum on its own, and
-  the compiler forms an FMA from such code unless contraction is off.
+  the compiler forms an FMA from such code unless contraction is off;
+* no GEMM kernel instance with 8-bit operands spills vector registers to
+  scratch memory (their registers are budgeted to the last one: the lane
+  geometry is held across a tile only where it fits).
 
 The disassembly is of device code built in this repository from its sources.
 """
@@ -37,7 +40,8 @@ def _tool(name):
 
 
 @pytest.fixture(scope="module")
-def disasm_text(tmp_path_factory):
+def code_objects(tmp_path_factory):
+    """The library's gfx950 code objects, one per translation unit."""
     if not os.path.exists(LIB):
         pytest.skip("libmxgemm.so is not built")
     objcopy, bundler, objdump = _tool("llvm-objcopy"), _tool("clang-offload-bundler"), _tool("llvm-objdump")
@@ -52,7 +56,7 @@ def disasm_text(tmp_path_factory):
     magic = b"__CLANG_OFFLOAD_BUNDLE__"
     starts = [i for i in range(0, len(data), 8) if data.startswith(magic, i)]
     assert starts, "no offload bundle in the library"
-    out = ""
+    codes = []
     for n, (a, b) in enumerate(zip(starts, starts[1:] + [len(data)])):
         part, code = str(d / f"bundle{n}.bin"), str(d / f"gfx950_{n}.hsaco")
         with open(part, "wb") as f:
@@ -60,9 +64,33 @@ def disasm_text(tmp_path_factory):
         subprocess.run([bundler, "--unbundle", "--type=o", f"--input={part}",
                         "--targets=hipv4-amdgcn-amd-amdhsa--gfx950", f"--output={code}"],
                        check=True, capture_output=True)
-        out += subprocess.run([objdump, "-d", "--mcpu=gfx950", "--no-show-raw-insn", code],
-                              check=True, capture_output=True, text=True).stdout
-    return out
+        codes.append(code)
+    return codes
+
+
+@pytest.fixture(scope="module")
+def disasm_text(code_objects):
+    objdump = _tool("llvm-objdump")
+    return "".join(subprocess.run([objdump, "-d", "--mcpu=gfx950", "--no-show-raw-insn", code],
+                                  check=True, capture_output=True, text=True).stdout for code in code_objects)
+
+
+@pytest.fixture(scope="module")
+def kernel_spills(code_objects):
+    """Kernel name -> vector registers spilled, from the code objects' metadata notes."""
+    readelf = _tool("llvm-readelf")
+    if not readelf:
+        pytest.skip("llvm-readelf not found")
+    spills = {}
+    for code in code_objects:
+        notes = subprocess.run([readelf, "--notes", code], check=True, capture_output=True, text=True).stdout
+        for kernel in notes.split("  - .")[1:]:
+            name = re.search(r"\.name:\s+(\S+)", kernel)
+            count = re.search(r"\.vgpr_spill_count:\s+(\d+)", kernel)
+            if name and count:
+                spills[name.group(1)] = int(count.group(1))
+    assert spills, "no kernel metadata found"
+    return spills
 
 
 @pytest.fixture(scope="module")
@@ -192,3 +220,19 @@ def test_fused_multiply_add_pattern():
         assert _FUSED.search(inst), inst
     for inst in ("v_mad_u64_u32 v[0:1], s[0:1], v2, v3, 0", "v_mul_f32_e32 v1, v2, v3", "v_sub_f32_e32 v1, v2, v3"):
         assert not _FUSED.search(inst), inst
+
+
+def test_gemm_kernels_with_8bit_operands_do_not_spill(kernel_spills):
+    # mxgemm_amax_big_kernel<SF, FA, FB, MODE, CT, BT, MJ, NW>: FA == 2 is packed
+    # FP4, whose 256x256 instances spill outside their K loop and are left out.
+    gemm = {k: v for k, v in kernel_spills.items() if "mxgemm_amax_big_kernel" in k}
+    assert len(gemm) > 50, "fewer GEMM kernel instances than expected"
+    checked = 0
+    for name, count in gemm.items():
+        args = re.search(r"kernelILi(\d+)ELi(\d+)ELi(\d+)E", name)
+        assert args, name
+        if args.group(2) == "2":
+            continue
+        checked += 1
+        assert count == 0, f"{name} spills {count} vector registers"
+    assert checked > 40
