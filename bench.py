@@ -203,7 +203,8 @@ def _per_dispatch(rows, kernel_substr, counter, kernel_name_exact=False):
 
 
 def rocprof_summary(d, workload, fp8_mfma, commands, op="gemm"):
-    """Text summary of a rocprofv3 kernel trace (d/kt) and two counter passes (d/fetch, d/write)."""
+    """Text summary of a rocprofv3 kernel trace (d/kt), two counter passes (d/fetch, d/write) and,
+    when present, a matrix-core counter pass (d/mfma)."""
     import workloads as W
     cfg = W.WORKLOADS[workload]
     M, N, K, L, sf = cfg["M"], cfg["N"], cfg["K"], cfg["L"], cfg["sf"]
@@ -298,6 +299,23 @@ def rocprof_summary(d, workload, fp8_mfma, commands, op="gemm"):
                 out += [f"rope_traffic_bytes_per_launch: {rfb + rwb:.0f}",
                         f"rope_algorithmic_bytes_per_launch: {rab}",
                         f"rope_traffic_over_algorithmic: {(rfb + rwb) / rab:.3f}"]
+    mfma = _csv_rows(os.path.join(d, "mfma", "**", "*counter_collection.csv"))
+    if mfma and gemm_name:
+        # SQ_VALU_MFMA_BUSY_CYCLES sums the matrix-core busy cycles of every SIMD;
+        # SQ_BUSY_CYCLES sums the busy cycles of every shader engine (32 engines of
+        # 8 CUs, so 32 SIMDs to an engine): their ratio over 32 is the fraction of
+        # the kernel's cycles the matrix cores were busy, at whatever clock it held
+        insts = _per_dispatch(mfma, gemm_name, "SQ_INSTS_MFMA", kernel_name_exact=True)
+        busy = _per_dispatch(mfma, gemm_name, "SQ_VALU_MFMA_BUSY_CYCLES", kernel_name_exact=True)
+        sq = _per_dispatch(mfma, gemm_name, "SQ_BUSY_CYCLES", kernel_name_exact=True)
+        if insts and busy and sq:
+            mi, mb, sb = sum(insts) / len(insts), sum(busy) / len(busy), sum(sq) / len(sq)
+            out += ["",
+                    "matrix cores (--pmc SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES; per dispatch, "
+                    f"mean of {len(busy)}):",
+                    f"  SQ_INSTS_MFMA {mi:.0f}  SQ_VALU_MFMA_BUSY_CYCLES {mb:.4g}  SQ_BUSY_CYCLES {sb:.4g}",
+                    f"mfma_instructions_per_launch: {mi:.0f}",
+                    f"mfma_busy_fraction: {mb / (32.0 * sb):.3f}"]
     out += ["", f"kernel_source_sha256: {kernel_source_hash()}"]
     bench_line = os.path.join(d, "bench.json")
     if os.path.exists(bench_line):
