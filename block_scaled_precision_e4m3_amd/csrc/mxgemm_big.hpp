@@ -214,14 +214,15 @@ __global__ __launch_bounds__(64 * NW, 1) void mxgemm_amax_big_kernel(Params p) {
     return ln;
   };
   // The lane geometry, computed once: the 128x128 ring's steps and DMA waves,
-  // and the 256x256 bf16 steps of k-major 8-bit operands with sf = 32 and a
-  // stored C, take it from here rather than rebuilding it every step from the
-  // opaque lane index (20-28 VALU instructions fewer per step: 2048^3 24.5 ->
-  // 23.6 us, 8192x24576x1536 525 -> 520 us).  The other 256x256 instances
-  // (sf = 16, FP4, m-major operands, the projection epilogue) would spill
-  // registers with it held, so they keep rebuilding it.
+  // and the 256x256 bf16 steps of k-major 8-bit operands with a stored C, take
+  // it from here rather than rebuilding it every step from the opaque lane
+  // index (20-28 VALU instructions fewer per step: 2048^3 24.5 -> 23.6 us,
+  // 8192x24576x1536 520.6 -> 513.9 us, 4000x7168x2048 at sf = 16 110.7 ->
+  // 108.7 us; at sf = 16 one register then spills, outside the K loop).  The
+  // other 256x256 instances (FP4, m-major operands, the projection epilogue)
+  // would spill dozens of registers with it held, so they keep rebuilding it.
   const Geo g_lane = geo(lane);
-  constexpr bool kHoistGeo = BT == 128 || (SF == 32 && !kFp4 && MJ == 0 && CT != 4);
+  constexpr bool kHoistGeo = BT == 128 || (!kFp4 && MJ == 0 && CT != 4);
 
   // --- DMA of one stage ------------------------------------------------------
   // A/B: wave w fills the 8-row groups w, w+4, ... of each tile, one
