@@ -224,7 +224,11 @@ size_t mxgemm_sf_bytes(int64_t MN, int64_t K, int64_t L, int sf_vec_size);
  * mxgemm_launch_config -- the tile shape and grid the GEMM kernel would use
  * for this problem with 8-bit operands (for reporting and tests; packed FP4
  * at sf_vec_size 16 always runs 128x128 tiles).  Writes tile_m, tile_n and
- * the number of workgroups; any output pointer may be NULL.  Returns a
+ * the number of workgroups (the tile count when the tiles fit the compute
+ * units; otherwise the tiles of one of the rounds a full grid would need,
+ * rounded up to a multiple of 8 and capped at the compute units, so every
+ * workgroup runs the same number of tiles give or take one); any output
+ * pointer may be NULL.  Returns a
  * status like mxgemm_check_support.  Queries the current device's compute
  * unit count (HIP call) only when `grid` is requested.
  */
