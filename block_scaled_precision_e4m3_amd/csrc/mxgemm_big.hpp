@@ -214,11 +214,12 @@ __global__ __launch_bounds__(64 * NW, 1) void mxgemm_amax_big_kernel(Params p) {
     return ln;
   };
   // The lane geometry, computed once: the 128x128 ring's steps and DMA waves,
-  // and the 256x256 bf16 steps of k-major 8-bit operands with a stored C, take
-  // it from here rather than rebuilding it every step from the opaque lane
-  // index (20-28 VALU instructions fewer per step: 2048^3 24.5 -> 23.6 us,
-  // 8192x24576x1536 520.6 -> 513.9 us, 4000x7168x2048 at sf = 16 110.7 ->
-  // 108.7 us; at sf = 16 one register then spills, outside the K loop).  The
+  // and the 256x256 steps (both datapaths) of k-major 8-bit operands with a
+  // stored C, take it from here rather than rebuilding it every step from the
+  // opaque lane index (20-28 VALU instructions fewer per step: 2048^3 24.5 ->
+  // 23.6 us, 8192x24576x1536 520.6 -> 513.9 us, 4000x7168x2048 at sf = 16
+  // 110.7 -> 108.7 us, the FP8 datapath 1.5-4%; at sf = 16 one register then
+  // spills, outside the K loop).  The
   // other 256x256 instances (FP4, m-major operands, the projection epilogue)
   // would spill dozens of registers with it held, so they keep rebuilding it.
   const Geo g_lane = geo(lane);
@@ -630,7 +631,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mxgemm_amax_big_kernel(Params p) {
     else wait_vm<kNStores - 1>();
     after_dma = 0;
     barrier();
-    const Geo g = geo(lane_opaque());
+    const Geo g = kHoistGeo ? g_lane : geo(lane_opaque());
     const uint8_t* st = lds + (s & 1) * Y::kStage;
     // fragment row i (32-row steps keep f, so only the chunk is swizzled)
     auto a_frag = [&](int i, int c) { return lds16(st + g.a_off + ((c ^ g.xr) << 4) + 4096 * i); };
